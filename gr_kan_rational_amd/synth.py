@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the GR-KAN activation: the one module that both
+the HIP path's tests/benchmark and the fp64 oracle draw their inputs from.
+
+It holds no part of the activation's arithmetic: it only draws normal
+variates, scales them and (for bf16 I/O) rounds them to bf16.
+
+Workloads.  The pages measure KAT models (ViT-style transformers with 197
+tokens per image, batch 1024) whose MLPs are GR-KAN layers; the activation
+tensors such a model feeds the GR-KAN kernels are [B, N, d].  These
+generators stand in for them with i.i.d. normal data of the same shapes:
+
+    tiny            [2, 8, 32]        fp32  dY ~ N(0, 1)     seed 1
+    kat-t           [128, 197, 192]   fp32  dY ~ N(0, 1e-2)  seed 2
+    kat-s-hid       [1024, 197, 1536] fp32  dY ~ N(0, 1e-2)  seed 3, group 0 numerator = identity
+    kat-b           [1024, 197, 768]  fp32  dY ~ N(0, 1e-2)  seed 4
+    kat-b-hid-bf16  [1024, 197, 3072] bf16  dY ~ N(0, 1e-2)  seed 5
+
+with n_g = 8 groups, coefficients A [8, 6] and B [8, 4] ~ N(0, 0.5) and
+X ~ N(0, 1) everywhere; N(0, s) means standard deviation s.
+
+Recipe (reproducible, independent of the number of threads):
+  * A then B from ``numpy.random.default_rng(seed)`` as float32 standard
+    normals, multiplied by the std in float32;
+  * X and dY in fixed chunks of 2**22 elements of the row-major tensor;
+    chunk k of tensor t (t = 1 for X, 2 for dY) comes from
+    ``PCG64(SeedSequence(seed, spawn_key=(t, k)))`` as float32 standard
+    normals times the std in float32;
+  * bf16 tensors are those float32 draws rounded to nearest-even bf16 and
+    stored as uint16 bit patterns.
+A run with fewer rows draws an exact prefix of the full tensors.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+CHUNK = 1 << 22
+N_NUM, N_DEN = 6, 4
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    seq: int
+    d: int
+    n_groups: int
+    io: str            # "f32" or "bf16" (I/O dtype of X, Y, dY, dX)
+    coef_std: float
+    x_std: float
+    dy_std: float
+    seed: int
+    identity_group0: bool = False
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.seq
+
+    @property
+    def elements(self) -> int:
+        return self.rows * self.d
+
+    @property
+    def d_g(self) -> int:
+        return self.d // self.n_groups
+
+    @property
+    def io_bytes(self) -> int:
+        return 2 if self.io == "bf16" else 4
+
+    def with_rows(self, rows: int) -> "Workload":
+        """Same recipe with `rows` rows in total (batch = rows, seq = 1)."""
+        return replace(self, batch=rows, seq=1)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in (
+        Workload("tiny", 2, 8, 32, 8, "f32", 0.5, 1.0, 1.0, 1),
+        Workload("kat-t", 128, 197, 192, 8, "f32", 0.5, 1.0, 1e-2, 2),
+        Workload("kat-s-hid", 1024, 197, 1536, 8, "f32", 0.5, 1.0, 1e-2, 3, True),
+        Workload("kat-b", 1024, 197, 768, 8, "f32", 0.5, 1.0, 1e-2, 4),
+        Workload("kat-b-hid-bf16", 1024, 197, 3072, 8, "bf16", 0.5, 1.0, 1e-2, 5),
+    )
+}
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def bf16_bits(f: np.ndarray) -> np.ndarray:
+    """Round float32 values to nearest-even bf16; returns the uint16 bit patterns."""
+    u = np.ascontiguousarray(f, dtype=np.float32).view(np.uint32)
+    lsb = (u >> 16) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> 16).astype(np.uint16)
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    """Exact float32 value of bf16 bit patterns (uint16)."""
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+def coefficients(w: Workload) -> tuple[np.ndarray, np.ndarray]:
+    rng = np.random.default_rng(w.seed)
+    std = np.float32(w.coef_std)
+    A = rng.standard_normal((w.n_groups, N_NUM), dtype=np.float32) * std
+    B = rng.standard_normal((w.n_groups, N_DEN), dtype=np.float32) * std
+    if w.identity_group0:
+        A[0] = np.array([0, 1, 0, 0, 0, 0], dtype=np.float32)
+    return A.astype(np.float32), B.astype(np.float32)
+
+
+def _tensor(w: Workload, which: int, std: float, out: np.ndarray) -> None:
+    """Fill the flat `out` (float32, or uint16 for bf16) with tensor `which`."""
+    n = out.size
+    nchunk = (n + CHUNK - 1) // CHUNK
+    s = np.float32(std)
+
+    def fill(k):
+        lo, hi = k * CHUNK, min(n, (k + 1) * CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(w.seed, spawn_key=(which, k))))
+        if w.io == "bf16":
+            tmp = g.standard_normal(hi - lo, dtype=np.float32)
+            if std != 1.0:
+                np.multiply(tmp, s, out=tmp)
+            out[lo:hi] = bf16_bits(tmp)
+        else:
+            dst = out[lo:hi]
+            g.standard_normal(out=dst, dtype=np.float32)
+            if std != 1.0:
+                np.multiply(dst, s, out=dst)
+
+    if nchunk <= 1:
+        for k in range(nchunk):
+            fill(k)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(fill, range(nchunk)))
+
+
+def make_inputs(w: Workload | str, rows: int | None = None, need_dy: bool = True) -> dict:
+    """Inputs of workload `w` (optionally only its first `rows` rows).
+
+    Returns ``{"A", "B", "x", "dy", "workload"}`` with x/dy shaped [rows, d]
+    (float32, or uint16 bf16 bit patterns when ``w.io == "bf16"``).
+    """
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if rows is not None:
+        if rows > w.rows:
+            raise ValueError("rows beyond the workload's size")
+        w = w.with_rows(rows)
+    A, B = coefficients(w)
+    dt = np.uint16 if w.io == "bf16" else np.float32
+    x = np.empty(w.elements, dtype=dt)
+    _tensor(w, 1, w.x_std, x)
+    dy = None
+    if need_dy:
+        dy = np.empty(w.elements, dtype=dt)
+        _tensor(w, 2, w.dy_std, dy)
+        dy = dy.reshape(w.rows, w.d)
+    return {"A": A, "B": B, "x": x.reshape(w.rows, w.d), "dy": dy, "workload": w}

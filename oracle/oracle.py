@@ -1,0 +1,235 @@
+"""fp64 CPU oracle for the GR-KAN safe Pade activation (forward and backward).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this module.  The HIP
+library never loads it, and it shares no code with the HIP path.
+
+The arithmetic lives in ``grkan_oracle.c`` (plain C, fp64; see its header for
+the definition being computed and the passages of the pages it follows).
+This wrapper only:
+
+* converts fp32 / bf16 inputs to their exact fp64 values,
+* cuts the rows into fixed chunks and runs the C routine on them from a
+  thread pool (each chunk sums its rows in index order; the chunk sums are
+  combined exactly with ``math.fsum``),
+* gathers sampled elements for the one-by-one checks at full size.
+
+Every function here is pinned by the ``not gpu`` tests in
+``tests/test_oracle_pins.py`` (closed forms, library routines, symbolic
+differentiation, finite differences, brute-force sums).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "grkan_oracle.c")
+_LIB = os.path.join(_HERE, "libgrkan_oracle.so")
+
+NA, NB = 6, 4           # numerator a_0..a_5, denominator b_1..b_4
+NK = NA + NB
+# record layout of grkan_oracle_point (kept in step with the C enum)
+F, DX, TA, TB, FMAG, DXMAG, SIGN, DEN, NOUT = 0, 1, 2, 8, 12, 13, 14, 15, 16
+
+_CHUNK_ELEMS = 1 << 16
+
+
+def build(force: bool = True) -> str:
+    """Compile ``grkan_oracle.c`` with gcc into ``libgrkan_oracle.so``."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-std=gnu11", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+           "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib_handle = None
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lp = ctypes.POINTER(ctypes.c_long)
+        lib.grkan_oracle_point.argtypes = [ctypes.c_double, ctypes.c_double, dp, dp, dp]
+        lib.grkan_oracle_point.restype = None
+        lib.grkan_oracle_rows.argtypes = [dp, dp, ctypes.c_long, ctypes.c_long, ctypes.c_int,
+                                          dp, dp, dp, dp, dp, dp, dp, dp]
+        lib.grkan_oracle_rows.restype = ctypes.c_int
+        lib.grkan_oracle_points.argtypes = [dp, dp, lp, ctypes.c_long, ctypes.c_long,
+                                            ctypes.c_int, dp, dp, dp]
+        lib.grkan_oracle_points.restype = ctypes.c_int
+        lib.grkan_oracle_nout.restype = ctypes.c_int
+        if lib.grkan_oracle_nout() != NOUT:
+            raise RuntimeError("oracle library record layout does not match oracle.py")
+        _lib_handle = lib
+    return _lib_handle
+
+
+def threads() -> int:
+    """Host threads the oracle uses: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def to_f64(a: np.ndarray, io: str = "f32") -> np.ndarray:
+    """Exact fp64 value of an fp32 array, or of a bf16 array stored as uint16 bits."""
+    if io == "bf16":
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 data must be given as its uint16 bit patterns")
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if io == "f32":
+        if a.dtype != np.float32:
+            raise TypeError("f32 data must be float32")
+        return a.astype(np.float64)
+    raise ValueError(f"unknown io dtype {io!r}")
+
+
+def _load_f64(dst: np.ndarray, src: np.ndarray, io: str, local) -> np.ndarray:
+    """to_f64 into a preallocated buffer (no temporaries)."""
+    if io == "bf16":
+        if src.dtype != np.uint16:
+            raise TypeError("bf16 data must be given as its uint16 bit patterns")
+        u = getattr(local, "u32", None)
+        if u is None or u.size < src.size:
+            u = np.empty(src.size, dtype=np.uint32)
+            local.u32 = u
+        u = u[:src.size]
+        np.copyto(u, src)
+        np.left_shift(u, 16, out=u)
+        np.copyto(dst, u.view(np.float32))
+    elif io == "f32":
+        if src.dtype != np.float32:
+            raise TypeError("f32 data must be float32")
+        np.copyto(dst, src)
+    else:
+        raise ValueError(f"unknown io dtype {io!r}")
+    return dst
+
+
+def _coef(A, B, n_groups):
+    A = np.ascontiguousarray(np.asarray(A, dtype=np.float64).reshape(n_groups, NA))
+    B = np.ascontiguousarray(np.asarray(B, dtype=np.float64).reshape(n_groups, NB))
+    return A, B
+
+
+def point(x: float, dy: float, a, b) -> np.ndarray:
+    """One element: the NOUT-record of grkan_oracle_point (a: 6 values, b: 4)."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64).reshape(NA))
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.float64).reshape(NB))
+    out = np.zeros(NOUT, dtype=np.float64)
+    _lib().grkan_oracle_point(float(x), float(dy), _ptr(a), _ptr(b), _ptr(out))
+    return out
+
+
+def run(x, A, B, n_groups: int, dy=None, io: str = "f32", elements: bool = True,
+        nthreads: int | None = None) -> dict:
+    """Forward (and backward when ``dy`` is given) over a whole [..., d] tensor.
+
+    Returns a dict with fp64 arrays shaped like ``x`` for ``y``, ``ymag`` and,
+    with ``dy``, ``dx``, ``dxmag`` (only when ``elements``), and always, with
+    ``dy``, ``dA`` [n_g, 6], ``dB`` [n_g, 4] and the L2 norms of their terms
+    ``nA``, ``nB`` (same shapes).
+    """
+    shape = x.shape
+    d = shape[-1]
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    x2 = x.reshape(rows, d)
+    dy2 = None if dy is None else dy.reshape(rows, d)
+    A64, B64 = _coef(A, B, n_groups)
+    lib = _lib()
+    res = {}
+    if elements:
+        res["y"] = np.empty((rows, d), dtype=np.float64)
+        res["ymag"] = np.empty((rows, d), dtype=np.float64)
+        if dy is not None:
+            res["dx"] = np.empty((rows, d), dtype=np.float64)
+            res["dxmag"] = np.empty((rows, d), dtype=np.float64)
+    step = max(1, _CHUNK_ELEMS // d)
+    starts = list(range(0, rows, step))
+    nchunk = len(starts)
+    sums = np.zeros((nchunk, n_groups * NK), dtype=np.float64)
+    sumsq = np.zeros((nchunk, n_groups * NK), dtype=np.float64)
+
+    local = threading.local()
+
+    def scratch(name, n):
+        buf = getattr(local, name, None)
+        if buf is None or buf.size < n:
+            buf = np.empty(n, dtype=np.float64)
+            setattr(local, name, buf)
+        return buf[:n]
+
+    def work(ci):
+        r0 = starts[ci]
+        r1 = min(rows, r0 + step)
+        n = (r1 - r0) * d
+        xc = _load_f64(scratch("x", n), x2[r0:r1].reshape(-1), io, local)
+        dyc = None
+        if dy2 is not None:
+            dyc = _load_f64(scratch("dy", n), dy2[r0:r1].reshape(-1), io, local)
+        outs = {k: res[k][r0:r1] for k in res}  # row slices of C-contiguous arrays
+        sp = _ptr(sums[ci]) if dy is not None else None
+        sq = _ptr(sumsq[ci]) if dy is not None else None
+        rc = lib.grkan_oracle_rows(_ptr(xc), _ptr(dyc), r1 - r0, d, n_groups,
+                                   _ptr(A64), _ptr(B64), _ptr(outs.get("y")),
+                                   _ptr(outs.get("ymag")), _ptr(outs.get("dx")),
+                                   _ptr(outs.get("dxmag")), sp, sq)
+        if rc != 0:
+            raise ValueError("oracle rejected the shape")
+
+    nt = nthreads or threads()
+    if nt == 1 or nchunk == 1:
+        for ci in range(nchunk):
+            work(ci)
+    else:
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(work, range(nchunk)))
+
+    for k in list(res):
+        res[k] = res[k].reshape(shape)
+    if dy is not None:
+        tot = np.array([math.fsum(sums[:, k]) for k in range(n_groups * NK)]).reshape(n_groups, NK)
+        tot2 = np.array([math.fsum(sumsq[:, k]) for k in range(n_groups * NK)]).reshape(n_groups, NK)
+        nrm = np.sqrt(tot2)
+        res["dA"], res["dB"] = tot[:, :NA].copy(), tot[:, NA:].copy()
+        res["nA"], res["nB"] = nrm[:, :NA].copy(), nrm[:, NA:].copy()
+    return res
+
+
+def points(x, A, B, n_groups: int, flat_idx, dy=None, io: str = "f32") -> np.ndarray:
+    """Records [n, NOUT] for the elements at flat indices ``flat_idx`` of ``x``."""
+    d = x.shape[-1]
+    flat_idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
+    xv = np.ascontiguousarray(to_f64(x.reshape(-1)[flat_idx], io))
+    dyv = None if dy is None else np.ascontiguousarray(to_f64(dy.reshape(-1)[flat_idx], io))
+    A64, B64 = _coef(A, B, n_groups)
+    out = np.empty((flat_idx.size, NOUT), dtype=np.float64)
+    rc = _lib().grkan_oracle_points(_ptr(xv), _ptr(dyv),
+                                    flat_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
+                                    flat_idx.size, d, n_groups, _ptr(A64), _ptr(B64), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the shape")
+    return out

@@ -1,0 +1,370 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself.
+
+Each test names the part of the oracle it pins and the outside fact it uses:
+closed forms, numpy/torch library routines, symbolic differentiation
+(sympy), exact finite differences, brute-force sums, exact special cases.
+Pages cited: [FlashKAT notes] = "FlashKAT: Understanding and Addressing
+Performance Bottlenecks in the Kolmogorov-Arnold Transformer" (Paper-Notes
+page, AAAI 2026).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from gr_kan_rational_amd import synth
+
+rng = np.random.default_rng(1234)
+
+
+def f32(v):
+    return np.float32(v)
+
+
+def rand_coef(n_g=1, scale=0.5):
+    A = (rng.standard_normal((n_g, 6)) * scale).astype(np.float32)
+    B = (rng.standard_normal((n_g, 4)) * scale).astype(np.float32)
+    return A, B
+
+
+XS = np.array([-3.5, -1.25, -0.3, -1e-3, 0.0, 2e-3, 0.5, 0.875, 1.0, 2.75, 4.0], dtype=np.float32)
+
+
+def fwd(xs, a, b, dy=1.0):
+    return np.array([orc.point(float(x), dy, a, b) for x in xs])
+
+
+# ---------------------------------------------------------------- forward F
+
+def test_identity_numerator_no_denominator_is_identity():
+    """a = (0,1,0,0,0,0), b = 0  =>  F(x) = x exactly, dF/dx = 1, no b-gradient."""
+    r = fwd(XS, [0, 1, 0, 0, 0, 0], [0, 0, 0, 0], dy=0.75)
+    assert np.array_equal(r[:, orc.F], XS.astype(np.float64))
+    assert np.all(r[:, orc.DX] == 0.75)
+    assert np.all(r[:, orc.TB:orc.TB + 4] == 0.0)
+
+
+def test_polynomial_when_denominator_vanishes():
+    """b = 0  =>  F = P (numpy polyval) and dF/dx = P' (numpy polyder)."""
+    a = (rng.standard_normal(6) * 0.7).astype(np.float32).astype(np.float64)
+    r = fwd(XS, a, [0, 0, 0, 0], dy=1.0)
+    P = np.polynomial.polynomial.polyval(XS.astype(np.float64), a)
+    Pd = np.polynomial.polynomial.polyval(XS.astype(np.float64), np.polynomial.polynomial.polyder(a))
+    np.testing.assert_allclose(r[:, orc.F], P, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(r[:, orc.DX], Pd, rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("b1", [1.0, -1.0])
+def test_softsign(b1):
+    """a = x, b_1 = +-1  =>  F = x / (1 + |x|) = torch softsign; F' = 1/(1+|x|)^2 (torch autograd)."""
+    import torch
+
+    t = torch.tensor(XS.astype(np.float64), requires_grad=True)
+    y = torch.nn.functional.softsign(t)
+    (g,) = torch.autograd.grad(y.sum(), t)
+    r = fwd(XS, [0, 1, 0, 0, 0, 0], [b1, 0, 0, 0])
+    np.testing.assert_allclose(r[:, orc.F], y.detach().numpy(), rtol=1e-15, atol=1e-300)
+    nz = XS != 0  # softsign's autograd is smooth at 0; the rational's kink convention is tested apart
+    np.testing.assert_allclose(r[nz, orc.DX], g.numpy()[nz], rtol=1e-14)
+
+
+def test_lorentzian_b2():
+    """a_0 = 1, b_2 = 1  =>  F = 1/(1+x^2), F' = -2x/(1+x^2)^2."""
+    x = XS.astype(np.float64)
+    r = fwd(XS, [1, 0, 0, 0, 0, 0], [0, 1, 0, 0])
+    np.testing.assert_allclose(r[:, orc.F], 1 / (1 + x * x), rtol=1e-15)
+    np.testing.assert_allclose(r[:, orc.DX], -2 * x / (1 + x * x) ** 2, rtol=1e-14, atol=1e-300)
+
+
+def test_cubic_b3_is_softsign_of_cube():
+    """a_3 = 1, b_3 = 1  =>  F = softsign(x^3) (torch)."""
+    import torch
+
+    x = XS.astype(np.float64)
+    r = fwd(XS, [0, 0, 0, 1, 0, 0], [0, 0, 1, 0])
+    ref = torch.nn.functional.softsign(torch.tensor(x ** 3)).numpy()
+    np.testing.assert_allclose(r[:, orc.F], ref, rtol=1e-15, atol=1e-300)
+
+
+def test_quartic_b4():
+    """a_4 = 1, b_4 = 1  =>  F = x^4/(1+x^4) = 1 - 1/(1+x^4)."""
+    x = XS.astype(np.float64)
+    r = fwd(XS, [0, 0, 0, 0, 1, 0], [0, 0, 0, 1])
+    np.testing.assert_allclose(r[:, orc.F], 1 - 1 / (1 + x ** 4), rtol=1e-14, atol=1e-15)
+
+
+def test_a5_term_and_zero_input():
+    """x = 0  =>  F = a_0 and dX = dY * a_1 (sign(0) = 0 kills the Q' term); a_5 x^5 enters F."""
+    a, b = rand_coef()
+    r = orc.point(0.0, 2.0, a[0], b[0])
+    assert r[orc.F] == np.float64(a[0, 0])
+    assert r[orc.DX] == 2.0 * np.float64(a[0, 1])
+    assert r[orc.SIGN] == 0 and np.all(r[orc.TB:orc.TB + 4] == 0)
+    r2 = orc.point(2.0, 1.0, [0, 0, 0, 0, 0, 1], [0, 0, 0, 0])
+    assert r2[orc.F] == 32.0 and r2[orc.DX] == 80.0
+
+
+def test_linear_in_numerator():
+    """F is linear in a: F(2a + a') = 2F(a) + F(a')."""
+    a, b = rand_coef()
+    a2, _ = rand_coef()
+    lhs = fwd(XS, 2 * a[0].astype(np.float64) + a2[0], b[0])[:, orc.F]
+    rhs = 2 * fwd(XS, a[0], b[0])[:, orc.F] + fwd(XS, a2[0], b[0])[:, orc.F]
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-13, atol=1e-13)
+
+
+def test_odd_symmetry():
+    """P odd and Q odd (b_2 = b_4 = 0)  =>  |Q(-x)| = |Q(x)|  =>  F(-x) = -F(x)."""
+    a = np.array([0, 0.3, 0, -0.7, 0, 0.2])
+    b = np.array([0.4, 0, -1.1, 0])
+    assert np.array_equal(fwd(-XS, a, b)[:, orc.F], -fwd(XS, a, b)[:, orc.F])
+
+
+def test_group_map_is_contiguous():
+    """Channel c uses group floor(c / d_g) ([FlashKAT notes], section on Algorithm 2: a block owns
+    all d_g channels of one group).  Group g gets a_0 = g + 1, b = 0, so F == g + 1 on its channels,
+    and dA[g][0] is the sum of dY over exactly those channels."""
+    n_g, d, rows = 4, 12, 5
+    A = np.zeros((n_g, 6), np.float32)
+    A[:, 0] = np.arange(1, n_g + 1)
+    B = np.zeros((n_g, 4), np.float32)
+    x = rng.standard_normal((rows, d)).astype(np.float32)
+    dy = rng.standard_normal((rows, d)).astype(np.float32)
+    r = orc.run(x, A, B, n_g, dy=dy)
+    expect = np.repeat(np.arange(1, n_g + 1), d // n_g)[None, :].repeat(rows, 0)
+    assert np.array_equal(r["y"], expect.astype(np.float64))
+    for g in range(n_g):
+        cols = slice(g * 3, g * 3 + 3)
+        assert r["dA"][g, 0] == pytest.approx(math.fsum(dy[:, cols].astype(np.float64).ravel()), rel=1e-15)
+
+
+# ------------------------------------------------------ derivatives (sympy)
+
+def test_derivatives_match_sympy():
+    """dF/dx, dF/da_i, dF/db_j against sympy's symbolic derivatives of P/(1+|Q|), evaluated exactly
+    at fp32 points (the forward itself is pinned by the closed forms above)."""
+    import sympy as sp
+
+    X = sp.Symbol("x", real=True)
+    asym = sp.symbols("a0:6", real=True)
+    bsym = sp.symbols("b1:5", real=True)
+    P = sum(asym[i] * X ** i for i in range(6))
+    Q = sum(bsym[j - 1] * X ** j for j in range(1, 5))
+    Fs = P / (1 + sp.Abs(Q))
+    dFx = sp.diff(Fs, X)
+    dFa = [sp.diff(Fs, asym[i]) for i in range(6)]
+    dFb = [sp.diff(Fs, bsym[j]) for j in range(4)]
+    for trial in range(6):
+        a, b = rand_coef()
+        subs = {asym[i]: sp.Rational(float(a[0, i])) for i in range(6)}
+        subs.update({bsym[j]: sp.Rational(float(b[0, j])) for j in range(4)})
+        for xv in (f32(-1.7), f32(-0.4), f32(0.9), f32(2.3)):
+            s2 = dict(subs)
+            s2[X] = sp.Rational(float(xv))
+            r = orc.point(float(xv), 1.0, a[0], b[0])
+            ex = float(sp.N(Fs.subs(s2), 40))
+            assert r[orc.F] == pytest.approx(ex, rel=1e-14, abs=1e-300)
+            assert r[orc.DX] == pytest.approx(float(sp.N(dFx.subs(s2), 40)), rel=1e-12, abs=1e-14)
+            for i in range(6):
+                assert r[orc.TA + i] == pytest.approx(float(sp.N(dFa[i].subs(s2), 40)), rel=1e-13, abs=1e-300)
+            for j in range(4):
+                assert r[orc.TB + j] == pytest.approx(float(sp.N(dFb[j].subs(s2), 40)), rel=1e-12, abs=1e-14)
+
+
+# ------------------------------------------- finite differences on `tiny`
+
+@pytest.fixture(scope="module")
+def tiny():
+    return synth.make_inputs("tiny")
+
+
+def _loss(x, dy, A, B, n_g):
+    """L = sum of dY * F over every element, summed exactly."""
+    y = orc.run(x, A, B, n_g)["y"]
+    return math.fsum((dy.astype(np.float64) * y).ravel())
+
+
+def test_dx_central_differences(tiny):
+    """dX = dY * dF/dx against central differences of the oracle's F, all 512 elements of `tiny`
+    except those within a step of a kink of |Q| (where the derivative jumps)."""
+    x, dy, A, B = tiny["x"], tiny["dy"], tiny["A"], tiny["B"]
+    n_g = 8
+    d = x.shape[1]
+    r = orc.run(x, A, B, n_g, dy=dy)
+    checked = 0
+    for idx in range(x.size):
+        g = (idx % d) // (d // n_g)
+        xv = float(x.ravel()[idx])
+        h = 2.0 ** -20 * max(1.0, abs(xv))
+        lo = orc.point(xv - h, 0.0, A[g], B[g])
+        hi = orc.point(xv + h, 0.0, A[g], B[g])
+        if lo[orc.SIGN] != hi[orc.SIGN]:
+            continue
+        fd = (hi[orc.F] - lo[orc.F]) / (2 * h) * float(dy.ravel()[idx])
+        assert r["dx"].ravel()[idx] == pytest.approx(fd, rel=1e-6, abs=1e-9)
+        checked += 1
+    assert checked >= 500
+
+
+def test_dA_exact_differences(tiny):
+    """F is linear in a, so L(a + e_gi) - L(a) = dA[g][i] up to fp64 rounding of L."""
+    x, dy, A, B = tiny["x"], tiny["dy"], tiny["A"], tiny["B"]
+    r = orc.run(x, A, B, 8, dy=dy)
+    L0 = _loss(x, dy, A, B, 8)
+    for g in (0, 3, 7):
+        for i in range(6):
+            A2 = A.astype(np.float64).copy()
+            A2[g, i] += 1.0
+            diff = _loss(x, dy, A2, B, 8) - L0
+            assert diff == pytest.approx(r["dA"][g, i], rel=1e-9, abs=1e-9 * max(1.0, abs(L0)))
+
+
+def test_dB_central_differences(tiny):
+    """dB[g][j] against central differences of L in b_j (no element changes the sign of Q)."""
+    x, dy, A, B = tiny["x"], tiny["dy"], tiny["A"], tiny["B"]
+    r = orc.run(x, A, B, 8, dy=dy)
+    h = 1e-6
+    for g in (1, 4, 6):
+        for j in range(4):
+            Bp = B.astype(np.float64).copy()
+            Bm = Bp.copy()
+            Bp[g, j] += h
+            Bm[g, j] -= h
+            idx = np.arange(x.size)
+            idx = idx[(idx % x.shape[1]) // (x.shape[1] // 8) == g]
+            sp_ = orc.points(x, A, Bp, 8, idx, dy=dy)[:, orc.SIGN]
+            sm_ = orc.points(x, A, Bm, 8, idx, dy=dy)[:, orc.SIGN]
+            assert np.array_equal(sp_, sm_), "a sign flip of Q inside the step would break the difference"
+            fd = (_loss(x, dy, A, Bp, 8) - _loss(x, dy, A, Bm, 8)) / (2 * h)
+            scale = r["nB"][g, j] * math.sqrt(x.size)
+            assert fd == pytest.approx(r["dB"][g, j], rel=1e-6, abs=1e-6 * scale)
+
+
+def test_identity_case_sums_closed_form(tiny):
+    """Identity numerator with b = 0: dA[g][i] = sum dY x^i, dB = 0, dX = dY."""
+    x, dy = tiny["x"], tiny["dy"]
+    A = np.tile(np.array([0, 1, 0, 0, 0, 0], np.float32), (8, 1))
+    B = np.zeros((8, 4), np.float32)
+    r = orc.run(x, A, B, 8, dy=dy)
+    assert np.array_equal(r["dx"], dy.astype(np.float64))
+    assert np.array_equal(r["y"], x.astype(np.float64))
+    assert np.all(r["dB"] == 0)
+    d_g = x.shape[1] // 8
+    for g in range(8):
+        xs = x[:, g * d_g:(g + 1) * d_g].astype(np.float64).ravel()
+        ds = dy[:, g * d_g:(g + 1) * d_g].astype(np.float64).ravel()
+        for i in range(6):
+            assert r["dA"][g, i] == pytest.approx(math.fsum(ds * xs ** i), rel=1e-14, abs=1e-14)
+
+
+def test_softsign_dB_closed_form():
+    """a = x, b = (b1,0,0,0): dF/db_1 = -sign(b1 x) x^2 / (1+|b1 x|)^2."""
+    b1 = 0.625
+    x = XS.astype(np.float64)
+    r = fwd(XS, [0, 1, 0, 0, 0, 0], [b1, 0, 0, 0])
+    ref = -np.sign(b1 * x) * x * x / (1 + np.abs(b1 * x)) ** 2
+    np.testing.assert_allclose(r[:, orc.TB], ref, rtol=1e-14, atol=1e-300)
+
+
+# ----------------------------------------------------- sums: brute force
+
+def test_group_sums_brute_force(tiny):
+    """The chunked, threaded group sums equal a brute-force fsum over per-element records
+    taken one by one, and do not depend on the chunking, thread count or row order."""
+    x, dy, A, B = tiny["x"], tiny["dy"], tiny["A"], tiny["B"]
+    d = x.shape[1]
+    rec = orc.points(x, A, B, 8, np.arange(x.size), dy=dy)
+    groups = (np.arange(x.size) % d) // (d // 8)
+    r = orc.run(x, A, B, 8, dy=dy)
+    for g in range(8):
+        for k in range(10):
+            ref = math.fsum(rec[groups == g, orc.TA + k])
+            got = r["dA"][g, k] if k < 6 else r["dB"][g, k - 6]
+            assert got == pytest.approx(ref, rel=1e-13, abs=1e-15)
+    perm = np.random.default_rng(0).permutation(x.shape[0])
+    rp = orc.run(x[perm], A, B, 8, dy=dy[perm], nthreads=3)
+    np.testing.assert_allclose(rp["dA"], r["dA"], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(rp["dB"], r["dB"], rtol=1e-13, atol=1e-15)
+    r2 = orc.run(x, A, B, 8, dy=(2 * dy.astype(np.float32)))
+    assert np.array_equal(r2["dA"], 2 * r["dA"]) and np.array_equal(r2["dB"], 2 * r["dB"])
+
+
+def test_chunked_run_matches_single_chunk():
+    """More rows than one chunk (2^16 elements): threaded chunks give the same elements and sums."""
+    w = synth.WORKLOADS["kat-t"]
+    inp = synth.make_inputs(w, rows=700)
+    r1 = orc.run(inp["x"], inp["A"], inp["B"], 8, dy=inp["dy"], nthreads=1)
+    r8 = orc.run(inp["x"], inp["A"], inp["B"], 8, dy=inp["dy"], nthreads=8)
+    assert np.array_equal(r1["dx"], r8["dx"]) and np.array_equal(r1["y"], r8["y"])
+    np.testing.assert_allclose(r8["dA"], r1["dA"], rtol=1e-14, atol=1e-18)
+    np.testing.assert_allclose(r8["dB"], r1["dB"], rtol=1e-14, atol=1e-18)
+
+
+# ------------------------------------------------- sign of Q near roots
+
+def test_sign_at_fp32_neighbours_of_irrational_root():
+    """Q = x (x^2 - 2): at fp32 neighbours of sqrt(2) the sign of Q is the sign of x^2 - 2,
+    which is exact in fp64 for fp32 x."""
+    b = [-2, 0, 1, 0]
+    r2 = np.float32(math.sqrt(2))
+    for xv in (np.nextafter(r2, np.float32(0)), r2, np.nextafter(r2, np.float32(2))):
+        xd = float(xv)
+        exact = np.sign(xd * xd - 2.0)
+        assert orc.point(xd, 1.0, [0, 1, 0, 0, 0, 0], b)[orc.SIGN] == exact
+
+
+def test_sign_beyond_fp64_resolution():
+    """Q = x (x - 1)^3 = x^4 - 3x^3 + 3x^2 - x (b = (-1, 3, -3, 1)); at x = 1 +- one fp32 step
+    the value is ~1e-21 while its terms are ~1, below fp64 resolution.  The oracle must still return
+    the exact sign: + above 1, - below, 0 at 1."""
+    b = [-1, 3, -3, 1]
+    one = np.float32(1)
+    assert orc.point(float(np.nextafter(one, np.float32(2))), 1.0, [0] * 6, b)[orc.SIGN] == 1
+    assert orc.point(float(np.nextafter(one, np.float32(0))), 1.0, [0] * 6, b)[orc.SIGN] == -1
+    assert orc.point(1.0, 1.0, [0] * 6, b)[orc.SIGN] == 0
+
+
+def test_sign_exact_root_is_zero():
+    """Q = x (x - 0.75): at x = 0.75 exactly Q = 0, s = 0, so dX = dY P'/D and the b-terms vanish."""
+    a = [0.1, 0.2, 0.3, 0.4, 0.5, 0.6]
+    r = orc.point(0.75, 1.5, a, [-0.75, 1, 0, 0])
+    assert r[orc.SIGN] == 0 and r[orc.DEN] == 1.0
+    Pd = np.polynomial.polynomial.polyval(0.75, np.polynomial.polynomial.polyder(np.array(a)))
+    assert r[orc.DX] == pytest.approx(1.5 * Pd, rel=1e-15)
+    assert np.all(r[orc.TB:orc.TB + 4] == 0)
+
+
+# --------------------------------------------- comparator scale (mag fields)
+
+def test_magnitude_bounds_fp32_evaluation():
+    """FMAG/DXMAG are the scales an fp32 evaluation's error is bounded by: they dominate |F| and
+    |dX|, equal them when every term is non-negative, and a plain numpy float32 evaluation stays
+    within 16 * 2^-24 of them."""
+    a = np.array([0.5, 0.25, 0.125, 0.0625, 0.03125, 0.015625])
+    r = orc.point(1.5, 1.0, a, [0, 0, 0, 0])
+    assert r[orc.FMAG] == pytest.approx(r[orc.F], rel=1e-15)
+    u = 2.0 ** -24
+    for _ in range(200):
+        A, B = rand_coef(scale=1.0)
+        xv = np.float32(rng.standard_normal() * 2)
+        dyv = np.float32(rng.standard_normal())
+        r = orc.point(float(xv), float(dyv), A[0], B[0])
+        assert r[orc.FMAG] >= abs(r[orc.F]) and r[orc.DXMAG] >= abs(r[orc.DX])
+        a32, b32 = A[0], B[0]
+        P = np.float32(0)
+        for i in range(5, -1, -1):
+            P = P * xv + a32[i]
+        q = np.float32(0)
+        for j in range(3, -1, -1):
+            q = q * xv + b32[j]
+        Q = q * xv
+        D = np.float32(1) + np.abs(Q)
+        assert abs(float(P / D) - r[orc.F]) <= 16 * u * r[orc.FMAG]
+
+
+def test_bf16_decode_is_exact():
+    """bf16 bit patterns decode to their exact values: 0x3F80 = 1, 0xC000 = -2, 0x3EAB = 0.333984375."""
+    bits = np.array([0x3F80, 0xC000, 0x3EAB, 0x0000, 0x8000], dtype=np.uint16)
+    v = orc.to_f64(bits, "bf16")
+    assert list(v[:3]) == [1.0, -2.0, 0.333984375] and v[3] == 0.0 and math.copysign(1, v[4]) == -1
