@@ -1,0 +1,257 @@
+"""Benchmark: GR-KAN activation forward + backward throughput on one MI355X.
+
+A step is one forward (grkan_forward) and one backward (grkan_backward,
+deterministic two-stage reduction) of the group-rational activation over a
+whole batch of synthetic activations, all resident in HBM before timing.
+Default workload: KAT-B shape, fp32 [1024, 197, 768], 8 groups.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload kat-b]
+                    [--mode deterministic|atomic] [--no-cpu-baseline] [--no-naive]
+
+Prints one JSON line.  `value` is elements per second of the whole step
+(E / step time); `roofline` rates the dominant kernel -- the backward call --
+by its algorithmic bytes (read x and dy, write dx: 12 B per fp32 element)
+over its average duration, timed with HIP events on the stream it runs on.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload.  `detail` adds the forward's figures, the atomic-mode and naive
+per-element-atomic backward times, and the rounding error of each backward
+reduction against the oracle's fp64 group sums (tests/golden).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("grkan_kernels.hip", "grkan_device.h", "grkan_api.hip"):
+        with open(os.path.join(ROOT, "gr_kan_rational_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, io_bytes_per_launch: float):
+    """HBM bytes per backward launch from the committed rocprofv3 PMC summary, or None when
+    absent or taken on a different kernel source."""
+    path = os.path.join(PROFILES, f"grkan_bwd_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def error_stats(got: np.ndarray, ref: np.ndarray) -> dict:
+    e = got.astype(np.float64) - ref
+    rel = np.abs(e) / np.maximum(np.abs(ref), 1e-300)
+    return {"mae": float(np.mean(np.abs(e))), "var": float(np.var(e)), "max_rel": float(np.max(rel))}
+
+
+def cpu_baseline(w, target_s: float = 10.0) -> dict:
+    """fp64 oracle (forward + backward of every element) on the first rows of the workload."""
+    from gr_kan_rational_amd import synth
+    from oracle import oracle
+
+    calib_rows = 256
+    inp = synth.make_inputs(w, rows=calib_rows)
+    t0 = time.perf_counter()
+    oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io)
+    dt = time.perf_counter() - t0
+    rows = int(min(w.rows, max(calib_rows, calib_rows * target_s / max(dt, 1e-3))))
+    inp = synth.make_inputs(w, rows=rows)
+    t0 = time.perf_counter()
+    oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io)
+    dt = time.perf_counter() - t0
+    n = rows * w.d
+    return {"value": n / dt, "unit": "elements/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"first {rows} of {w.rows} rows ({n} elements) of {w.name}, forward + backward "
+                      f"(Y, dX, dA, dB) in fp64, {dt:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="kat-b")
+    ap.add_argument("--mode", choices=["deterministic", "atomic"], default="deterministic")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-naive", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the activation shards by rows with no "
+              "communication but the dA/dB all-reduce, which is not part of this build); "
+              "use --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gr_kan_rational_amd.binding as gk
+    from gr_kan_rational_amd import synth
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gk.load_library()
+    w = synth.WORKLOADS[args.workload]
+    io = gk.GRKAN_BF16 if w.io == "bf16" else gk.GRKAN_F32
+    log(f"workload {w.name} [{w.batch},{w.seq},{w.d}] {w.io}: generating inputs")
+    inp = synth.make_inputs(w)
+
+    def to_dev(a):
+        if w.io == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    x, dy = to_dev(inp["x"]), to_dev(inp["dy"])
+    A = torch.from_numpy(inp["A"]).to(dev)
+    B = torch.from_numpy(inp["B"]).to(dev)
+    del inp
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    dA = torch.empty((w.n_groups, 6), dtype=torch.float32, device=dev)
+    dB = torch.empty((w.n_groups, 4), dtype=torch.float32, device=dev)
+    det = args.mode == "deterministic"
+    flags = gk.GRKAN_DETERMINISTIC if det else 0
+    ws_bytes = gk.grkan_backward_workspace_size(w.rows, w.d, w.n_groups, io, flags)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        gk.grkan_forward(x, A, B, w.n_groups, out=y, stream=stream)
+
+    def bwd(deterministic=det, naive=False):
+        gk.grkan_backward(x, dy, A, B, w.n_groups, deterministic=deterministic, naive=naive,
+                          dx=dx, dA=dA, dB=dB, workspace=ws, stream=stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        fwd()
+        ev[k][1].record(stream)
+        bwd()
+        ev[k][2].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms_per_step = total_ms / args.steps
+    E = w.elements
+    es = w.io_bytes
+    value = E / (ms_per_step * 1e-3)
+    bwd_bytes = 3 * es * E
+    fwd_bytes = 2 * es * E
+    bwd_gbps = bwd_bytes / (bwd_ms * 1e-3) / 1e9
+    fwd_gbps = fwd_bytes / (fwd_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step:.4f} ms (fwd {fwd_ms:.4f}, bwd {bwd_ms:.4f}); wall {wall:.3f} s")
+
+    detail = {
+        "elements": E,
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "fwd_GBps": fwd_gbps, "fwd_frac_hbm_peak": fwd_gbps / HBM_PEAK_GBPS,
+        "bwd_GBps": bwd_gbps, "bwd_frac_hbm_peak": bwd_gbps / HBM_PEAK_GBPS,
+        "fwdbwd_GBps": (fwd_bytes + bwd_bytes) / (ms_per_step * 1e-3) / 1e9,
+        "launch_fwd": gk.grkan_query_launch(w.rows, w.d, w.n_groups, io, 0),
+        "launch_bwd": gk.grkan_query_launch(w.rows, w.d, w.n_groups, io, 1),
+        "device": torch.cuda.get_device_name(dev),
+    }
+
+    # other backward modes, outside the timed region
+    def time_one(fn, reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        s.record(stream)
+        for _ in range(reps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    golden = os.path.join(GOLDEN, f"{w.name}.sums.json")
+    ref = None
+    if os.path.exists(golden):
+        with open(golden) as f:
+            g = json.load(f)
+        ref = (np.array(g["dA"]), np.array(g["dB"]))
+    errors = {}
+    other = "atomic" if det else "deterministic"
+    detail[f"bwd_{other}_ms"] = time_one(lambda: bwd(deterministic=not det), 10)
+    for mode in ("deterministic", "atomic"):
+        bwd(deterministic=(mode == "deterministic"))
+        torch.cuda.synchronize()
+        if ref is not None:
+            errors[mode] = {"dA": error_stats(dA.cpu().numpy(), ref[0]), "dB": error_stats(dB.cpu().numpy(), ref[1])}
+    if not args.no_naive:
+        log("naive per-element-atomic backward (one run)")
+        detail["bwd_naive_ms"] = time_one(lambda: bwd(naive=True), 1)
+        if ref is not None:
+            errors["naive_per_element_atomic"] = {"dA": error_stats(dA.cpu().numpy(), ref[0]),
+                                                  "dB": error_stats(dB.cpu().numpy(), ref[1])}
+    if errors:
+        detail["grad_error_vs_fp64_oracle"] = errors
+
+    traffic = traffic_from_profiles(w.name, bwd_bytes)
+    out = {
+        "metric": "GR-KAN fwd+bwd elements/s and achieved HBM GB/s (% peak) at KAT-B shape",
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.io == "f32" else "f32 (bf16 I/O)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "shape": [w.batch, w.seq, w.d], "n_groups": w.n_groups,
+                   "io": w.io, "backward_mode": args.mode},
+        "roofline": {"bound": "hbm", "achieved": bwd_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": bwd_gbps / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "grkan_backward (main kernel + fixed-order merge)",
+                     "algorithmic_bytes_per_launch": bwd_bytes},
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -12,6 +12,8 @@ __all__ = [
     "grkan_status_string",
     "GRKANFunction",
     "GRKANError",
+    "grkan_query_launch",
+    "load_library",
 ]
 
 

@@ -1,0 +1,69 @@
+"""Build libgrkan.so (gfx950) in-tree with hipcc.
+
+Every translation unit is compiled for gfx950 only, with packed-FP32
+instruction selection disabled, then linked into ``libgrkan.so`` next to this
+file.  The baseline kernel's translation unit is compiled with the compiler's
+atomic optimizer off so that each lane's atomic stays a hardware atomic.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OBJ = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libgrkan.so")
+ARCH = "gfx950"
+
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
+]
+UNITS = {
+    "grkan_api.hip": [],
+    "grkan_kernels.hip": [],
+    "grkan_naive.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+}
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    cc = hipcc()
+
+    def compile_unit(item):
+        name, extra = item
+        out = os.path.join(OBJ, name.replace(".hip", ".o"))
+        cmd = [cc, *COMMON, *extra, "-c", os.path.join(CSRC, name), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {name}:\n{r.stderr}")
+        if verbose and r.stderr.strip():
+            print(r.stderr)
+        return out
+
+    with ThreadPoolExecutor(len(UNITS)) as ex:
+        objs = list(ex.map(compile_unit, UNITS.items()))
+    tmp = LIB + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,180 @@
+"""Thin Python binding of libgrkan.so (C ABI in include/grkan.h).
+
+Argument marshalling only: tensors become device pointers, shapes and a
+stream handle; every step of the computation runs in the library's HIP
+kernels.  The library is loaded on first use; if it is missing or cannot be
+loaded, every call raises -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgrkan.so")
+
+GRKAN_OK, GRKAN_ERR_INVALID_ARG, GRKAN_ERR_UNSUPPORTED, GRKAN_ERR_HIP = 0, 1, 2, 3
+GRKAN_F32, GRKAN_BF16 = 0, 1
+GRKAN_DETERMINISTIC = 1 << 0
+GRKAN_NAIVE_ATOMIC = 1 << 1
+
+
+class GRKANError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {grkan_status_string(status)}")
+
+
+class grkan_launch_t(ctypes.Structure):
+    _fields_ = [
+        ("block", ctypes.c_int32),
+        ("rows_per_iter", ctypes.c_int32),
+        ("unroll", ctypes.c_int32),
+        ("slices", ctypes.c_int32),
+        ("grid", ctypes.c_int64),
+        ("cus", ctypes.c_int32),
+        ("blocks_per_cu", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgrkan.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"GR-KAN HIP library not built ({path}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, u32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    lib.grkan_forward.argtypes = [vp, vp, vp, vp, i64, i64, i32, ctypes.c_int, vp]
+    lib.grkan_forward.restype = ctypes.c_int
+    lib.grkan_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, ctypes.c_int, u32, vp, sz, vp]
+    lib.grkan_backward.restype = ctypes.c_int
+    lib.grkan_backward_workspace_size.argtypes = [i64, i64, i32, ctypes.c_int, u32]
+    lib.grkan_backward_workspace_size.restype = sz
+    lib.grkan_status_string.argtypes = [ctypes.c_int]
+    lib.grkan_status_string.restype = ctypes.c_char_p
+    lib.grkan_query_launch.argtypes = [i64, i64, i32, ctypes.c_int, i32, ctypes.POINTER(grkan_launch_t)]
+    lib.grkan_query_launch.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def grkan_status_string(status: int) -> str:
+    return load_library().grkan_status_string(int(status)).decode()
+
+
+def _io(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GRKAN_F32
+    if t.dtype == torch.bfloat16:
+        return GRKAN_BF16
+    raise TypeError(f"GR-KAN I/O dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_coefs(A: torch.Tensor, B: torch.Tensor, n_groups: int, dev) -> None:
+    for name, t, k in (("A", A, 6), ("B", B, 4)):
+        if t.dtype != torch.float32 or t.device != dev or not t.is_contiguous() or t.numel() != n_groups * k:
+            raise ValueError(f"{name} must be a contiguous float32 [{n_groups}, {k}] tensor on {dev}")
+
+
+def _rows_d(x: torch.Tensor):
+    if x.dim() < 1 or not x.is_contiguous():
+        raise ValueError("activations must be contiguous with channels last")
+    d = x.shape[-1]
+    return (x.numel() // d if d else 0), d
+
+
+def grkan_forward(x: torch.Tensor, A: torch.Tensor, B: torch.Tensor, n_groups: int = 8,
+                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = F(x), the group-rational activation, computed by ``grkan_forward``."""
+    lib = load_library()
+    io = _io(x)
+    _check_coefs(A, B, n_groups, x.device)
+    rows, d = _rows_d(x)
+    y = torch.empty_like(x) if out is None else out
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+        raise ValueError("out must match x")
+    st = lib.grkan_forward(_ptr(x), _ptr(y), _ptr(A), _ptr(B), rows, d, n_groups, io, ctypes.c_void_p(_stream(stream)))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_forward")
+    return y
+
+
+def grkan_backward_workspace_size(rows: int, d: int, n_groups: int, io: int = GRKAN_F32,
+                                  flags: int = GRKAN_DETERMINISTIC) -> int:
+    return int(load_library().grkan_backward_workspace_size(rows, d, n_groups, io, flags))
+
+
+def grkan_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                   n_groups: int = 8, deterministic: bool = True, naive: bool = False,
+                   dx: torch.Tensor | None = None, dA: torch.Tensor | None = None,
+                   dB: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   stream=None):
+    """(dx, dA, dB) of the group-rational activation, computed by ``grkan_backward``.
+
+    ``deterministic`` selects the two-stage fixed-order reduction (the
+    default); otherwise one fp32 atomic per coefficient per workgroup.
+    ``naive`` selects the per-element-atomic baseline (measurement only).
+    """
+    lib = load_library()
+    io = _io(x)
+    if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device or not dy.is_contiguous():
+        raise ValueError("dy must match x")
+    _check_coefs(A, B, n_groups, x.device)
+    rows, d = _rows_d(x)
+    flags = GRKAN_NAIVE_ATOMIC if naive else (GRKAN_DETERMINISTIC if deterministic else 0)
+    dx = torch.empty_like(x) if dx is None else dx
+    dA = torch.empty((n_groups, 6), dtype=torch.float32, device=x.device) if dA is None else dA
+    dB = torch.empty((n_groups, 4), dtype=torch.float32, device=x.device) if dB is None else dB
+    ws_bytes = lib.grkan_backward_workspace_size(rows, d, n_groups, io, flags)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    wsp = _ptr(workspace) if workspace is not None else None
+    wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.grkan_backward(_ptr(x), _ptr(dy), _ptr(A), _ptr(B), _ptr(dx), _ptr(dA), _ptr(dB),
+                            rows, d, n_groups, io, flags, wsp, wsn, ctypes.c_void_p(_stream(stream)))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_backward")
+    return dx, dA, dB
+
+
+def grkan_query_launch(rows: int, d: int, n_groups: int, io: int, pass_: int) -> dict:
+    """Launch geometry on the current device (pass_ 0 = forward, 1 = backward)."""
+    out = grkan_launch_t()
+    st = load_library().grkan_query_launch(rows, d, n_groups, io, pass_, ctypes.byref(out))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_query_launch")
+    return {f: getattr(out, f) for f, _ in grkan_launch_t._fields_}
+
+
+class GRKANFunction(torch.autograd.Function):
+    """Autograd wrapper: forward by grkan_forward, backward by grkan_backward."""
+
+    @staticmethod
+    def forward(ctx, x, A, B, n_groups=8):
+        ctx.save_for_backward(x, A, B)
+        ctx.n_groups = n_groups
+        return grkan_forward(x.contiguous(), A.contiguous(), B.contiguous(), n_groups)
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, A, B = ctx.saved_tensors
+        dx, dA, dB = grkan_backward(x.contiguous(), dy.contiguous(), A.contiguous(), B.contiguous(),
+                                    ctx.n_groups)
+        return dx, dA.view_as(A), dB.view_as(B), None

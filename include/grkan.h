@@ -1,0 +1,145 @@
+/*
+ * grkan.h -- C ABI of the MI355X (gfx950) GR-KAN safe Pade activation library
+ * (libgrkan.so).
+ *
+ * Pages cited
+ *   [FlashKAT notes]  "FlashKAT: Understanding and Addressing Performance
+ *                     Bottlenecks in the Kolmogorov-Arnold Transformer",
+ *                     Paper-Notes page (AAAI 2026), arXiv 2505.13813.
+ *
+ * The operation.  GR-KAN shares one rational function among the channels of
+ * each of n_groups contiguous channel groups and uses the "safe" Pade unit
+ * ([FlashKAT notes], section "KAT 的突破与残留问题"), with 6 numerator and 4
+ * denominator coefficients per group (section "损失函数 / 训练策略"):
+ *
+ *     F_g(x) = P_g(x) / (1 + |Q_g(x)|),
+ *     P_g(x) = a_g0 + a_g1 x + ... + a_g5 x^5,
+ *     Q_g(x) = b_g1 x + b_g2 x^2 + b_g3 x^3 + b_g4 x^4   (no constant term).
+ *
+ * Channel c of a row of d channels belongs to group c / (d / n_groups).
+ * The backward pass (section "2. 原始 KAT 的 atomic add 问题分析") produces
+ * dX elementwise and the coefficient gradients dA, dB, each summed over every
+ * element (all rows, all channels) of its group; with s = sign(Q),
+ * sign(0) = 0 and D = 1 + |Q|:
+ *
+ *     dX      = dY (P'/D - s P Q'/D^2)
+ *     dA[g,i] = sum dY x^i / D                (i = 0..5)
+ *     dB[g,j] = sum -dY s P x^(j+1) / D^2     (j = 0..3, i.e. b_g1..b_g4)
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are row-major [rows][d], rows = batch * sequence; x, y, dy and
+ *     dx have the I/O dtype `io`; A is fp32 [n_groups][6] (a_0..a_5), B is
+ *     fp32 [n_groups][4] (b_1..b_4), dA and dB are fp32 with the same shapes.
+ *     Arithmetic is fp32; group sums are carried in fp64 inside the library.
+ *   - All pointers are device pointers on the current HIP device, owned by
+ *     the caller.  The library allocates no device memory and keeps no state
+ *     beyond a per-device cache of launch limits.
+ *   - Work is enqueued on `stream` and the call returns without waiting.
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Arguments are validated before any HIP call; an invalid call changes
+ *     nothing on the device.  No C++ exception crosses this interface.
+ */
+#ifndef GRKAN_H
+#define GRKAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifndef GRKAN_API
+#define GRKAN_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GRKAN_OK = 0,
+    GRKAN_ERR_INVALID_ARG = 1, /* null pointer, bad shape, overlap, small workspace, bad flags */
+    GRKAN_ERR_UNSUPPORTED = 2, /* misaligned pointer, d/n_groups*bytes(io) not a multiple of 16
+                                  or above 16 KiB                                               */
+    GRKAN_ERR_HIP = 3          /* the HIP runtime reported an error on query or launch          */
+} grkan_status_t;
+
+typedef enum {
+    GRKAN_F32 = 0,  /* fp32 x, y, dy, dx                                   */
+    GRKAN_BF16 = 1  /* bf16 x, y, dy, dx; outputs rounded to nearest even  */
+} grkan_dtype_t;
+
+enum {
+    /* Backward: per-workgroup fp64 partial sums written to `workspace`, then
+       merged by a second kernel in a fixed order.  The result is bitwise
+       reproducible for a given shape, device and library build. */
+    GRKAN_DETERMINISTIC = 1u << 0,
+    /* Backward: the per-element atomic baseline (every element adds its ten
+       terms to dA/dB with global fp32 atomics), the scheme the pages identify
+       as the bottleneck ([FlashKAT notes], section "2. 原始 KAT 的 atomic add
+       问题分析").  For measurement and error comparison only. */
+    GRKAN_NAIVE_ATOMIC = 1u << 1
+};
+
+/*
+ * Forward: y = F(x) elementwise.
+ *   x, y      [rows][d], dtype io, 16-byte aligned; y == x (in place) is
+ *             allowed, any other overlap is GRKAN_ERR_INVALID_ARG.  May be
+ *             NULL when rows == 0.
+ *   A, B      fp32 coefficients [n_groups][6] and [n_groups][4], 4-byte aligned.
+ *   rows >= 0 (0 is a no-op), d >= 1, n_groups >= 1, d % n_groups == 0.
+ */
+GRKAN_API grkan_status_t grkan_forward(const void *x, void *y, const float *A, const float *B,
+                             int64_t rows, int64_t d, int32_t n_groups,
+                             grkan_dtype_t io, hipStream_t stream);
+
+/*
+ * Backward: dx = dy * dF/dx elementwise, and dA, dB = the group sums above.
+ *   x, dy     inputs [rows][d], dtype io, 16-byte aligned.
+ *   dx        output [rows][d], dtype io, 16-byte aligned; dx may equal x or
+ *             dy exactly (in place), any other overlap is INVALID_ARG.
+ *   dA, dB    fp32 outputs [n_groups][6], [n_groups][4]; overwritten, not
+ *             accumulated; must not overlap any other argument.  rows == 0
+ *             writes zeros.
+ *   flags     0 (one fp32 atomic add per coefficient per workgroup into dA,
+ *             dB after a zero fill), GRKAN_DETERMINISTIC, or
+ *             GRKAN_NAIVE_ATOMIC.  Other bits, or both, are INVALID_ARG.
+ *   workspace device memory of at least grkan_backward_workspace_size()
+ *             bytes, 16-byte aligned, for GRKAN_DETERMINISTIC; ignored (may
+ *             be NULL) otherwise.  Its contents on entry do not matter.  Two
+ *             calls in flight at once must not share one workspace.
+ */
+GRKAN_API grkan_status_t grkan_backward(const void *x, const void *dy, const float *A, const float *B,
+                              void *dx, float *dA, float *dB,
+                              int64_t rows, int64_t d, int32_t n_groups,
+                              grkan_dtype_t io, uint32_t flags,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace grkan_backward needs for these arguments (0 when it
+ * needs none, or for arguments grkan_backward would reject).  Host-only: it
+ * makes no HIP call and works without a GPU. */
+GRKAN_API size_t grkan_backward_workspace_size(int64_t rows, int64_t d, int32_t n_groups,
+                                     grkan_dtype_t io, uint32_t flags);
+
+/* Static English text for a status code (never NULL). */
+GRKAN_API const char *grkan_status_string(grkan_status_t status);
+
+/* Launch geometry the library uses on the current device for a pass
+ * (pass 0 = forward, 1 = backward).  Queries the device (CU count and
+ * occupancy) on first use. */
+typedef struct {
+    int32_t block;          /* threads per workgroup                           */
+    int32_t rows_per_iter;  /* rows one workgroup covers per loop iteration    */
+    int32_t unroll;         /* loop iterations whose loads are issued together */
+    int32_t slices;         /* workgroups per group                            */
+    int64_t grid;           /* workgroups in the launch = slices * n_groups    */
+    int32_t cus;            /* compute units on the device                     */
+    int32_t blocks_per_cu;  /* resident workgroups per CU for this kernel      */
+} grkan_launch_t;
+
+GRKAN_API grkan_status_t grkan_query_launch(int64_t rows, int64_t d, int32_t n_groups,
+                                  grkan_dtype_t io, int32_t pass, grkan_launch_t *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRKAN_H */

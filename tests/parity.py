@@ -1,0 +1,79 @@
+"""Comparison rules between the HIP path and the fp64 oracle.
+
+Tolerances (fixed here, used by every parity test):
+
+* Y and dX, elementwise, fp32 I/O:  |gpu - ref| <= 1e-5 * max(|ref|, M)
+  where M is the oracle's first-order rounding scale of that element (sums of
+  the absolute values of every term, see oracle/grkan_oracle.c).  For
+  elements away from zeros of the result, M ~ |ref| and this is the plain
+  relative 1e-5; next to a zero of P (or of dX) a relative test cannot hold
+  for any fp32 evaluation, and the scale M takes over.
+* bf16 I/O: the same plus half a bf16 ulp of the returned value (the
+  kernel rounds an fp32 result to nearest-even bf16).
+* dA and dB: |gpu - ref| <= 1e-4 * max(|ref|, 1e-2 * ||t||_2) + 1e-6, with
+  ||t||_2 the L2 norm of the group's terms.  Rounding every term in fp32
+  leaves an error of order 2^-24 * ||t||_2 whatever the summation; a sum
+  that cancels to |ref| << ||t||_2 is therefore compared at 1e-6 ||t||_2,
+  about 17 units of that floor.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+REL_ELEM = 1e-5
+REL_SUM = 1e-4
+SUM_FLOOR = 1e-2
+ABS_SUM = 1e-6
+
+
+def ulp_bf16(v: np.ndarray) -> np.ndarray:
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    out = np.zeros_like(a)
+    nz = a > 0
+    out[nz] = 2.0 ** (np.floor(np.log2(a[nz])) - 7)
+    return out
+
+
+def elem_tol(ref: np.ndarray, mag: np.ndarray, gpu: np.ndarray, io: str = "f32") -> np.ndarray:
+    tol = REL_ELEM * np.maximum(np.abs(ref), mag)
+    if io == "bf16":
+        tol = tol + 0.5 * ulp_bf16(gpu)
+    return tol
+
+
+def check_elem(name: str, gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, io: str = "f32") -> dict:
+    gpu = np.asarray(gpu, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    mag = np.asarray(mag, dtype=np.float64).ravel()
+    err = np.abs(gpu - ref)
+    tol = elem_tol(ref, mag, gpu, io)
+    bad = ~(err <= tol)
+    literal = int(np.sum(err > REL_ELEM * np.abs(ref) + (0.5 * ulp_bf16(gpu) if io == "bf16" else 0)))
+    stats = {"n": int(gpu.size), "bad": int(bad.sum()), "literal_rel_fail": literal,
+             "max_err_over_tol": float(np.max(err / np.maximum(tol, 1e-300))) if gpu.size else 0.0}
+    if bad.any():
+        i = np.flatnonzero(bad)[:8]
+        raise AssertionError(f"{name}: {stats['bad']}/{gpu.size} outside tolerance; first at {i.tolist()}: "
+                             f"gpu={gpu[i].tolist()} ref={ref[i].tolist()} tol={tol[i].tolist()}")
+    return stats
+
+
+def sum_tol(ref: np.ndarray, norm: np.ndarray) -> np.ndarray:
+    return REL_SUM * np.maximum(np.abs(ref), SUM_FLOOR * norm) + ABS_SUM
+
+
+def check_sums(name: str, gpu: np.ndarray, ref: np.ndarray, norm: np.ndarray) -> dict:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    err = np.abs(gpu - ref)
+    tol = sum_tol(ref, norm)
+    bad = ~(err <= tol)
+    literal = int(np.sum(err > np.maximum(REL_SUM * np.abs(ref), ABS_SUM)))
+    stats = {"bad": int(bad.sum()), "literal_fail": literal,
+             "max_rel": float(np.max(err / np.maximum(np.abs(ref), 1e-300))),
+             "max_err_over_norm": float(np.max(err / np.maximum(norm, 1e-300)))}
+    if bad.any():
+        idx = np.argwhere(bad)[:8].tolist()
+        raise AssertionError(f"{name}: {stats['bad']} coefficients outside tolerance at {idx}: "
+                             f"gpu={gpu[bad][:8].tolist()} ref={ref[bad][:8].tolist()} "
+                             f"tol={tol[bad][:8].tolist()}")
+    return stats

@@ -1,0 +1,125 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/grkan.h declares, and rejects invalid arguments before any HIP call
+(so these calls never touch a device; the pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grkan.h")
+LIB = os.path.join(ROOT, "gr_kan_rational_amd", "libgrkan.so")
+
+OK, INVALID, UNSUPPORTED, HIPERR = 0, 1, 2, 3
+F32, BF16 = 0, 1
+DET, NAIVE = 1, 2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    import torch  # noqa: F401  (load torch's HIP runtime first, as the binding does)
+
+    from gr_kan_rational_amd import binding
+
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"GRKAN_API\s+[\w\s\*]*?\b(grkan_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted([
+        "grkan_forward", "grkan_backward", "grkan_backward_workspace_size",
+        "grkan_status_string", "grkan_query_launch"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, word in ((OK, "OK"), (INVALID, "INVALID"), (UNSUPPORTED, "UNSUPPORTED"), (HIPERR, "HIP")):
+        assert word in lib.grkan_status_string(code).decode()
+    assert lib.grkan_status_string(99)
+
+
+def ws(lib, rows, d, n_g, io=F32, flags=DET):
+    return lib.grkan_backward_workspace_size(rows, d, n_g, io, flags)
+
+
+def test_workspace_size(lib):
+    # KAT-B: 201728 rows / 8 rows per step = 25216 steps, 4 steps per iteration -> 6304 slices of
+    # work, capped at 8192 / 8 = 1024 slices per group; 10 fp64 partials each.
+    assert ws(lib, 201728, 768, 8) == 8 * 1024 * 10 * 8
+    assert ws(lib, 16, 32, 8) == 8 * 1 * 10 * 8          # tiny: 1 step, one slice per group
+    assert ws(lib, 201728, 768, 8, flags=0) == 0            # atomic mode needs none
+    assert ws(lib, 201728, 768, 8, flags=NAIVE) == 0
+    assert ws(lib, 100, 770, 8) == 0                        # d % n_g != 0: rejected
+    assert ws(lib, 100, 40, 8) == 0                         # 5 channels * 4 B: not 16-byte vectors
+    assert ws(lib, 0, 768, 8) == 8 * 1 * 10 * 8
+
+
+P = 0x10000  # fake, 16-byte aligned "device" addresses: validation never dereferences them
+
+
+def fwd(lib, x=P, y=P + 0x100000, A=P + 0x200000, B=P + 0x300000, rows=4, d=64, n_g=8, io=F32):
+    return lib.grkan_forward(x, y, A, B, rows, d, n_g, io, None)
+
+
+def bwd(lib, x=P, dy=P + 0x100000, A=P + 0x200000, B=P + 0x300000, dx=P + 0x400000,
+        dA=P + 0x500000, dB=P + 0x600000, rows=4, d=64, n_g=8, io=F32, flags=DET,
+        ws_ptr=P + 0x700000, ws_bytes=1 << 20):
+    return lib.grkan_backward(x, dy, A, B, dx, dA, dB, rows, d, n_g, io, flags, ws_ptr, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), INVALID), (dict(B=None), INVALID), (dict(x=None), INVALID), (dict(y=None), INVALID),
+    (dict(rows=-1), INVALID), (dict(d=0), INVALID), (dict(n_g=0), INVALID), (dict(d=66), INVALID),
+    (dict(io=7), INVALID),
+    (dict(x=P + 4), UNSUPPORTED), (dict(y=P + 0x100008), UNSUPPORTED), (dict(A=P + 0x200002), UNSUPPORTED),
+    (dict(d=40), UNSUPPORTED),                       # d_g = 5 fp32 = 20 bytes per group row
+    (dict(d=8 * 4104, n_g=8), UNSUPPORTED),           # 16416 bytes per group row > 16 KiB
+    (dict(y=P + 16), INVALID),                       # partial overlap of y and x
+    (dict(y=P + 0x200000 - 16), INVALID),             # y runs into A
+])
+def test_forward_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_forward_empty_is_ok_without_device(lib):
+    # rows == 0 is a valid no-op that returns before any HIP call; null data pointers are fine.
+    assert fwd(lib, x=None, y=None, rows=0) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dA=None), INVALID), (dict(dB=None), INVALID), (dict(dx=None), INVALID), (dict(dy=None), INVALID),
+    (dict(flags=4), INVALID), (dict(flags=DET | NAIVE), INVALID),
+    (dict(ws_ptr=None), INVALID), (dict(ws_bytes=100), INVALID),
+    (dict(ws_ptr=P + 0x700008), UNSUPPORTED),
+    (dict(dx=P + 16), INVALID),                      # dx partially overlaps x
+    (dict(dA=P + 0x600000 + 8), INVALID),            # dA overlaps dB
+    (dict(dA=P + 64), INVALID),                      # dA inside x
+    (dict(ws_ptr=P + 0x400000 - 64), INVALID),       # workspace runs into dx
+    (dict(dy=P + 0x100002), UNSUPPORTED),
+    (dict(dB=P + 0x600001), UNSUPPORTED),
+])
+def test_backward_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_backward_atomic_mode_needs_no_workspace(lib):
+    # Validation passes; the call then needs the device.  Without one the HIP query fails
+    # cleanly with GRKAN_ERR_HIP rather than crashing.
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("only meaningful without a GPU")
+    assert bwd(lib, flags=0, ws_ptr=None, ws_bytes=0) == HIPERR

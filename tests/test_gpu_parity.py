@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+* reduced sizes: every workload's recipe at a row count that spans several
+  row tiles per workgroup plus a ragged tail, compared element by element;
+* full sizes (the launch configuration the benchmark times): sampled
+  elements computed one by one by the oracle, and the full group sums;
+* special values, exactness invariants, determinism, edge cases.
+Tolerances: tests/parity.py.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gr_kan_rational_amd import synth
+from oracle import oracle as orc
+import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def gk():
+    import gr_kan_rational_amd.binding as b
+
+    b.load_library()
+    return b
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a: np.ndarray, io: str) -> torch.Tensor:
+    if io == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def to_host(t: torch.Tensor, io: str) -> np.ndarray:
+    """fp32 host copy (bf16 values are exact in fp32)."""
+    if io == "bf16":
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def dev_inputs(inp):
+    io = inp["workload"].io
+    return (to_dev(inp["x"], io), to_dev(inp["dy"], io),
+            torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV))
+
+
+REDUCED_ROWS = {"tiny": 16, "kat-t": 1000, "kat-s-hid": 301, "kat-b": 1001, "kat-b-hid-bf16": 203}
+
+
+@pytest.mark.parametrize("name", list(REDUCED_ROWS))
+@pytest.mark.parametrize("deterministic", [True, False])
+def test_parity_reduced(gk, name, deterministic):
+    inp = synth.make_inputs(name, rows=REDUCED_ROWS[name])
+    w = inp["workload"]
+    log(f"[parity_reduced] {name} rows={w.rows} d={w.d} io={w.io} det={deterministic}")
+    x, dy, A, B = dev_inputs(inp)
+    y = gk.grkan_forward(x, A, B, w.n_groups)
+    dx, dA, dB = gk.grkan_backward(x, dy, A, B, w.n_groups, deterministic=deterministic)
+    torch.cuda.synchronize()
+    ref = orc.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io)
+    parity.check_elem(f"{name} Y", to_host(y, w.io), ref["y"], ref["ymag"], w.io)
+    parity.check_elem(f"{name} dX", to_host(dx, w.io), ref["dx"], ref["dxmag"], w.io)
+    parity.check_sums(f"{name} dA", dA.cpu().numpy(), ref["dA"], ref["nA"])
+    parity.check_sums(f"{name} dB", dB.cpu().numpy(), ref["dB"], ref["nB"])
+
+
+def sample_indices(w, n_random=200_000, seed=0):
+    """Random flat indices plus the first and last rows and every group boundary of row 0."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, w.elements, size=n_random, dtype=np.int64)
+    head = np.arange(0, 2 * w.d, dtype=np.int64)
+    tail = np.arange(w.elements - 2 * w.d, w.elements, dtype=np.int64)
+    return np.unique(np.concatenate([idx, head, tail]))
+
+
+@pytest.mark.parametrize("name", ["tiny", "kat-t", "kat-s-hid", "kat-b", "kat-b-hid-bf16"])
+def test_parity_full_size(gk, name):
+    """Full workload shapes in the benchmark's launch configuration."""
+    w = synth.WORKLOADS[name]
+    log(f"[parity_full] {name} shape=({w.batch},{w.seq},{w.d}) io={w.io}: generating inputs")
+    inp = synth.make_inputs(w)
+    x, dy, A, B = dev_inputs(inp)
+    log(f"[parity_full] {name}: forward + backward on GPU")
+    y = gk.grkan_forward(x, A, B, w.n_groups)
+    dx, dA, dB = gk.grkan_backward(x, dy, A, B, w.n_groups, deterministic=True)
+    _, dA_at, dB_at = gk.grkan_backward(x, dy, A, B, w.n_groups, deterministic=False)
+    torch.cuda.synchronize()
+    idx = sample_indices(w)
+    it = torch.from_numpy(idx).to(DEV)
+    ys = to_host(y.reshape(-1).index_select(0, it), w.io)
+    dxs = to_host(dx.reshape(-1).index_select(0, it), w.io)
+    del y, dx, x, dy
+    log(f"[parity_full] {name}: oracle on {idx.size} sampled elements and the full group sums")
+    rec = orc.points(inp["x"], inp["A"], inp["B"], w.n_groups, idx, dy=inp["dy"], io=w.io)
+    parity.check_elem(f"{name} Y[sampled]", ys, rec[:, orc.F], rec[:, orc.FMAG], w.io)
+    parity.check_elem(f"{name} dX[sampled]", dxs, rec[:, orc.DX], rec[:, orc.DXMAG], w.io)
+    ref = orc.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io, elements=False)
+    sa = parity.check_sums(f"{name} dA", dA.cpu().numpy(), ref["dA"], ref["nA"])
+    sb = parity.check_sums(f"{name} dB", dB.cpu().numpy(), ref["dB"], ref["nB"])
+    parity.check_sums(f"{name} dA atomic", dA_at.cpu().numpy(), ref["dA"], ref["nA"])
+    parity.check_sums(f"{name} dB atomic", dB_at.cpu().numpy(), ref["dB"], ref["nB"])
+    log(f"[parity_full] {name}: ok dA {sa} dB {sb}")
+
+
+def special_inputs():
+    """d = 64, 8 groups of 8 channels (32-byte group rows: a second geometry).
+
+    group 0: identity numerator, b = 0          group 1: b = 0, random a
+    group 2: Q = x (x - 0.75): exact root 0.75   group 3: Q = x (x^2 - 2): root sqrt 2
+    group 4: Q = x (x - 1)^3: values below fp64 resolution next to 1
+    groups 5-7: random coefficients.
+    x: +-0, fp32 neighbours of the roots, large |x| (8), random."""
+    rng = np.random.default_rng(7)
+    n_g, d = 8, 64
+    A = (rng.standard_normal((n_g, 6)) * 0.5).astype(np.float32)
+    B = (rng.standard_normal((n_g, 4)) * 0.5).astype(np.float32)
+    A[0] = [0, 1, 0, 0, 0, 0]
+    B[0] = 0
+    B[1] = 0
+    B[2] = [-0.75, 1, 0, 0]
+    B[3] = [-2, 0, 1, 0]
+    B[4] = [-1, 3, -3, 1]
+    rows = 48
+    x = rng.standard_normal((rows, d)).astype(np.float32)
+    f = np.float32
+    one, r2 = f(1), f(np.sqrt(2))
+    specials = [f(0), -f(0), f(0.75), np.nextafter(f(0.75), f(0)), np.nextafter(f(0.75), f(1)),
+                r2, np.nextafter(r2, f(0)), np.nextafter(r2, f(2)), -r2,
+                one, np.nextafter(one, f(0)), np.nextafter(one, f(2)), f(8), f(-8), f(1e-30)]
+    for g in range(n_g):
+        for i, v in enumerate(specials):
+            x[i, g * 8 + i % 8] = v          # special value i of every group
+            x[i + 24, g * 8 + (i + 3) % 8] = v  # and again, in another column
+    dy = rng.standard_normal((rows, d)).astype(np.float32)
+    return x, dy, A, B
+
+
+def test_special_values(gk):
+    x, dy, A, B = special_inputs()
+    log("[special] x = +-0, near-root x, b = 0 groups, |x| = 8")
+    xt, dyt = torch.from_numpy(x).to(DEV), torch.from_numpy(dy).to(DEV)
+    At, Bt = torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV)
+    y = gk.grkan_forward(xt, At, Bt, 8)
+    for det in (True, False):
+        dx, dA, dB = gk.grkan_backward(xt, dyt, At, Bt, 8, deterministic=det)
+        ref = orc.run(x, A, B, 8, dy=dy)
+        parity.check_elem("special Y", y.cpu().numpy(), ref["y"], ref["ymag"])
+        parity.check_elem("special dX", dx.cpu().numpy(), ref["dx"], ref["dxmag"])
+        parity.check_sums("special dA", dA.cpu().numpy(), ref["dA"], ref["nA"])
+        parity.check_sums("special dB", dB.cpu().numpy(), ref["dB"], ref["nB"])
+        # the exact-sign cases: dX at the roots must take s from the exact Q, not from fp32 noise
+        assert np.all(dB.cpu().numpy()[:2] == 0)
+
+
+def test_identity_is_exact(gk):
+    """a = x, b = 0 in every group: Y == X and dX == dY bitwise (+0 for -0 allowed)."""
+    inp = synth.make_inputs("kat-b", rows=333)
+    x, dy, _, _ = dev_inputs(inp)
+    A = torch.tensor([[0, 1, 0, 0, 0, 0]] * 8, dtype=torch.float32, device=DEV)
+    B = torch.zeros((8, 4), dtype=torch.float32, device=DEV)
+    y = gk.grkan_forward(x, A, B, 8)
+    dx, dA, dB = gk.grkan_backward(x, dy, A, B, 8)
+    assert torch.equal(y, x) and torch.equal(dx, dy)
+    assert torch.all(dB == 0)
+    A_id = np.tile(np.array([0, 1, 0, 0, 0, 0], np.float32), (8, 1))
+    ref = orc.run(inp["x"], A_id, np.zeros((8, 4), np.float32), 8, dy=inp["dy"], elements=False)
+    parity.check_sums("identity dA", dA.cpu().numpy(), ref["dA"], ref["nA"])
+
+
+def test_deterministic_mode_is_bitwise_stable_and_linear(gk):
+    inp = synth.make_inputs("kat-t", rows=4000)
+    x, dy, A, B = dev_inputs(inp)
+    r1 = gk.grkan_backward(x, dy, A, B, 8, deterministic=True)
+    r2 = gk.grkan_backward(x, dy, A, B, 8, deterministic=True)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    r3 = gk.grkan_backward(x, 2 * dy, A, B, 8, deterministic=True)
+    for a, b in zip(r1, r3):
+        assert torch.equal(2 * a, b)
+
+
+def test_groups_do_not_interact(gk):
+    """Changing group 5's coefficients leaves every other group's outputs bitwise unchanged."""
+    inp = synth.make_inputs("kat-b", rows=257)
+    x, dy, A, B = dev_inputs(inp)
+    y1 = gk.grkan_forward(x, A, B, 8)
+    dx1, dA1, dB1 = gk.grkan_backward(x, dy, A, B, 8)
+    A2, B2 = A.clone(), B.clone()
+    A2[5] += 0.25
+    B2[5] *= -1.5
+    y2 = gk.grkan_forward(x, A2, B2, 8)
+    dx2, dA2, dB2 = gk.grkan_backward(x, dy, A2, B2, 8)
+    keep = torch.ones(768, dtype=torch.bool, device=DEV)
+    keep[5 * 96:6 * 96] = False
+    assert torch.equal(y1[:, keep], y2[:, keep]) and torch.equal(dx1[:, keep], dx2[:, keep])
+    other = [g for g in range(8) if g != 5]
+    assert torch.equal(dA1[other], dA2[other]) and torch.equal(dB1[other], dB2[other])
+    assert not torch.equal(y1[:, ~keep], y2[:, ~keep])
+
+
+def test_empty_input(gk):
+    x = torch.empty((0, 768), dtype=torch.float32, device=DEV)
+    A = torch.randn(8, 6, device=DEV)
+    B = torch.randn(8, 4, device=DEV)
+    y = gk.grkan_forward(x, A, B, 8)
+    assert y.shape == (0, 768)
+    for det in (True, False):
+        dA = torch.full((8, 6), float("nan"), device=DEV)
+        dB = torch.full((8, 4), float("nan"), device=DEV)
+        gk.grkan_backward(x, x, A, B, 8, deterministic=det, dA=dA, dB=dB)
+        assert torch.all(dA == 0) and torch.all(dB == 0)
+
+
+def test_in_place(gk):
+    inp = synth.make_inputs("kat-b", rows=100)
+    x, dy, A, B = dev_inputs(inp)
+    y = gk.grkan_forward(x, A, B, 8)
+    dx, dA, dB = gk.grkan_backward(x, dy, A, B, 8)
+    xc, dyc = x.clone(), dy.clone()
+    gk.grkan_forward(xc, A, B, 8, out=xc)
+    assert torch.equal(xc, y)
+    _, dA2, dB2 = gk.grkan_backward(x, dyc, A, B, 8, dx=dyc)
+    assert torch.equal(dyc, dx) and torch.equal(dA2, dA) and torch.equal(dB2, dB)
+
+
+def test_errors_surface_as_exceptions(gk):
+    x = torch.randn(10, 769, device=DEV)[:, 1:]  # not contiguous rows
+    A = torch.randn(8, 6, device=DEV)
+    B = torch.randn(8, 4, device=DEV)
+    with pytest.raises(ValueError):
+        gk.grkan_forward(x, A, B, 8)
+    flat = torch.randn(10 * 768 + 1, device=DEV)[1:].view(10, 768)  # 4-byte misaligned
+    with pytest.raises(gk.GRKANError) as e:
+        gk.grkan_forward(flat, A, B, 8)
+    assert e.value.status == gk.GRKAN_ERR_UNSUPPORTED
+    with pytest.raises(gk.GRKANError):
+        gk.grkan_forward(torch.randn(4, 40, device=DEV), A, B, 8)  # 20-byte group rows
+    with pytest.raises(gk.GRKANError) as e:
+        gk.grkan_backward(torch.randn(4, 768, device=DEV), torch.randn(4, 768, device=DEV), A, B, 8,
+                          workspace=torch.empty(8, dtype=torch.uint8, device=DEV))
+    assert e.value.status == gk.GRKAN_ERR_INVALID_ARG
+
+
+def test_launch_geometry(gk):
+    g = gk.grkan_query_launch(201728, 768, 8, gk.GRKAN_F32, 1)
+    log(f"[geometry] KAT-B backward: {g}")
+    assert g["grid"] == g["slices"] * 8
+    assert g["grid"] <= g["cus"] * g["blocks_per_cu"]  # one wave of resident workgroups
+    assert g["grid"] >= 4 * g["cus"]
+    assert g["block"] == 192 and g["rows_per_iter"] == 8
+
+
+def test_naive_baseline(gk):
+    """The per-element-atomic baseline computes the same dX and, up to its fp32 atomic rounding,
+    the same sums."""
+    inp = synth.make_inputs("kat-b", rows=401)
+    x, dy, A, B = dev_inputs(inp)
+    dx_n, dA_n, dB_n = gk.grkan_backward(x, dy, A, B, 8, naive=True)
+    dx, dA, dB = gk.grkan_backward(x, dy, A, B, 8)
+    torch.cuda.synchronize()
+    ref = orc.run(inp["x"], inp["A"], inp["B"], 8, dy=inp["dy"])
+    parity.check_elem("naive dX", dx_n.cpu().numpy(), ref["dx"], ref["dxmag"])
+    for got, r, n in ((dA_n, ref["dA"], ref["nA"]), (dB_n, ref["dB"], ref["nB"])):
+        err = np.abs(got.cpu().numpy() - r)
+        assert np.all(err <= 1e-3 * np.maximum(np.abs(r), n) + 1e-6)
+
+
+def test_autograd_function(gk):
+    inp = synth.make_inputs("kat-t", rows=50)
+    x, dy, A, B = dev_inputs(inp)
+    xg, Ag, Bg = x.clone().requires_grad_(), A.clone().requires_grad_(), B.clone().requires_grad_()
+    y = gk.GRKANFunction.apply(xg, Ag, Bg, 8)
+    y.backward(dy)
+    dx, dA, dB = gk.grkan_backward(x, dy, A, B, 8)
+    assert torch.equal(y.detach(), gk.grkan_forward(x, A, B, 8))
+    assert torch.equal(xg.grad, dx) and torch.equal(Ag.grad, dA) and torch.equal(Bg.grad, dB)
