@@ -90,9 +90,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="kat-b")
-    ap.add_argument("--mode", choices=["deterministic", "atomic"], default="deterministic")
+    ap.add_argument("--mode", choices=["deterministic", "block_atomic"], default="deterministic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of one workload tensor (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -111,8 +113,20 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    gk.load_library()
     w = synth.WORKLOADS[args.workload]
+    if args.copy_probe:
+        # A plain copy of known size: what FETCH_SIZE / WRITE_SIZE read for it calibrates the
+        # counters that measure the GR-KAN kernels' HBM traffic.
+        nbytes = w.elements * w.io_bytes
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
+                          "copies": max(1, args.steps)}), flush=True)
+        return 0
+    gk.load_library()
     io = gk.GRKAN_BF16 if w.io == "bf16" else gk.GRKAN_F32
     log(f"workload {w.name} [{w.batch},{w.seq},{w.d}] {w.io}: generating inputs")
     inp = synth.make_inputs(w)
@@ -130,17 +144,15 @@ def main() -> int:
     dx = torch.empty_like(x)
     dA = torch.empty((w.n_groups, 6), dtype=torch.float32, device=dev)
     dB = torch.empty((w.n_groups, 4), dtype=torch.float32, device=dev)
-    det = args.mode == "deterministic"
-    flags = gk.GRKAN_DETERMINISTIC if det else 0
-    ws_bytes = gk.grkan_backward_workspace_size(w.rows, w.d, w.n_groups, io, flags)
+    ws_bytes = gk.grkan_backward_workspace_size(w.rows, w.d, w.n_groups, io, 0)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def fwd():
         gk.grkan_forward(x, A, B, w.n_groups, out=y, stream=stream)
 
-    def bwd(deterministic=det, naive=False):
-        gk.grkan_backward(x, dy, A, B, w.n_groups, deterministic=deterministic, naive=naive,
+    def bwd(mode=args.mode):
+        gk.grkan_backward(x, dy, A, B, w.n_groups, mode=mode,
                           dx=dx, dA=dA, dB=dB, workspace=ws, stream=stream)
 
     log(f"warmup {args.warmup} steps")
@@ -208,16 +220,16 @@ def main() -> int:
             g = json.load(f)
         ref = (np.array(g["dA"]), np.array(g["dB"]))
     errors = {}
-    other = "atomic" if det else "deterministic"
-    detail[f"bwd_{other}_ms"] = time_one(lambda: bwd(deterministic=not det), 10)
-    for mode in ("deterministic", "atomic"):
-        bwd(deterministic=(mode == "deterministic"))
+    other = "block_atomic" if args.mode == "deterministic" else "deterministic"
+    detail[f"bwd_{other}_ms"] = time_one(lambda: bwd(other), 10)
+    for mode in ("deterministic", "block_atomic"):
+        bwd(mode)
         torch.cuda.synchronize()
         if ref is not None:
             errors[mode] = {"dA": error_stats(dA.cpu().numpy(), ref[0]), "dB": error_stats(dB.cpu().numpy(), ref[1])}
     if not args.no_naive:
         log("naive per-element-atomic backward (one run)")
-        detail["bwd_naive_ms"] = time_one(lambda: bwd(naive=True), 1)
+        detail["bwd_naive_ms"] = time_one(lambda: bwd("naive"), 1)
         if ref is not None:
             errors["naive_per_element_atomic"] = {"dA": error_stats(dA.cpu().numpy(), ref[0]),
                                                   "dB": error_stats(dB.cpu().numpy(), ref[1])}

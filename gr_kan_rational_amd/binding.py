@@ -17,8 +17,9 @@ LIB_PATH = os.path.join(_HERE, "libgrkan.so")
 
 GRKAN_OK, GRKAN_ERR_INVALID_ARG, GRKAN_ERR_UNSUPPORTED, GRKAN_ERR_HIP = 0, 1, 2, 3
 GRKAN_F32, GRKAN_BF16 = 0, 1
-GRKAN_DETERMINISTIC = 1 << 0
+GRKAN_BLOCK_ATOMIC = 1 << 0
 GRKAN_NAIVE_ATOMIC = 1 << 1
+_MODES = {"deterministic": 0, "block_atomic": GRKAN_BLOCK_ATOMIC, "naive": GRKAN_NAIVE_ATOMIC}
 
 
 class GRKANError(RuntimeError):
@@ -32,7 +33,7 @@ class grkan_launch_t(ctypes.Structure):
         ("block", ctypes.c_int32),
         ("rows_per_iter", ctypes.c_int32),
         ("unroll", ctypes.c_int32),
-        ("slices", ctypes.c_int32),
+        ("tiles", ctypes.c_int64),
         ("grid", ctypes.c_int64),
         ("cus", ctypes.c_int32),
         ("blocks_per_cu", ctypes.c_int32),
@@ -117,20 +118,20 @@ def grkan_forward(x: torch.Tensor, A: torch.Tensor, B: torch.Tensor, n_groups: i
 
 
 def grkan_backward_workspace_size(rows: int, d: int, n_groups: int, io: int = GRKAN_F32,
-                                  flags: int = GRKAN_DETERMINISTIC) -> int:
+                                  flags: int = 0) -> int:
     return int(load_library().grkan_backward_workspace_size(rows, d, n_groups, io, flags))
 
 
 def grkan_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
-                   n_groups: int = 8, deterministic: bool = True, naive: bool = False,
+                   n_groups: int = 8, mode: str = "deterministic",
                    dx: torch.Tensor | None = None, dA: torch.Tensor | None = None,
                    dB: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                    stream=None):
     """(dx, dA, dB) of the group-rational activation, computed by ``grkan_backward``.
 
-    ``deterministic`` selects the two-stage fixed-order reduction (the
-    default); otherwise one fp32 atomic per coefficient per workgroup.
-    ``naive`` selects the per-element-atomic baseline (measurement only).
+    ``mode``: "deterministic" (the two-stage fixed-order reduction, default),
+    "block_atomic" (one fp32 atomic per coefficient per workgroup) or "naive"
+    (ten fp32 atomics per element); the last two are for comparison only.
     """
     lib = load_library()
     io = _io(x)
@@ -138,7 +139,9 @@ def grkan_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B: torch.
         raise ValueError("dy must match x")
     _check_coefs(A, B, n_groups, x.device)
     rows, d = _rows_d(x)
-    flags = GRKAN_NAIVE_ATOMIC if naive else (GRKAN_DETERMINISTIC if deterministic else 0)
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    flags = _MODES[mode]
     dx = torch.empty_like(x) if dx is None else dx
     dA = torch.empty((n_groups, 6), dtype=torch.float32, device=x.device) if dA is None else dA
     dB = torch.empty((n_groups, 4), dtype=torch.float32, device=x.device) if dB is None else dB
@@ -155,7 +158,8 @@ def grkan_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B: torch.
 
 
 def grkan_query_launch(rows: int, d: int, n_groups: int, io: int, pass_: int) -> dict:
-    """Launch geometry on the current device (pass_ 0 = forward, 1 = backward)."""
+    """Launch geometry on the current device (pass_ 0 = forward, 1 = backward,
+    2 = backward with GRKAN_BLOCK_ATOMIC)."""
     out = grkan_launch_t()
     st = load_library().grkan_query_launch(rows, d, n_groups, io, pass_, ctypes.byref(out))
     if st != GRKAN_OK:

@@ -8,13 +8,13 @@
 //
 // Launch plan.  The pages' Algorithm 2 (section "3. FlashKAT 核函数重构
 // （Algorithm 2）") uses a grid of ceil(rows / S_block) row tiles x n_g groups.
-// Here the number of row slices per group is instead derived from the device:
-// slices = (CUs x resident workgroups per CU) / n_groups, capped by the work
-// available, so a launch is one full wave of resident workgroups, each with an
-// equal share of row steps.
+// Here likewise: tiles of unroll x rows_per_iter rows, one workgroup per
+// (tile, group).  The plan depends only on the shape and dtype, never on the
+// device, so the deterministic mode gives the same bits on every device.
 #include <limits.h>
 #include <stdint.h>
 
+#include <cstdlib>
 #include <mutex>
 
 #include "grkan.h"
@@ -25,7 +25,6 @@ using namespace grkan;
 namespace {
 
 constexpr int kCoefs = 10;
-constexpr int64_t kSliceBudget = 8192;  // upper bound on workgroups per launch, all groups
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -41,9 +40,9 @@ bool bad_alias(const void *p, const void *q, size_t n) { return p != q && overla
 
 int io_bytes(grkan_dtype_t io) { return io == GRKAN_BF16 ? 2 : 4; }
 
-// Shape checks and the device-independent part of the plan.
+// Shape checks and the launch plan (a function of the shape and dtype only).
 grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, grkan_dtype_t io, int pass,
-                          Geometry *G) {
+                          bool atomic_mode, Geometry *G) {
     if (io != GRKAN_F32 && io != GRKAN_BF16) return GRKAN_ERR_INVALID_ARG;
     if (rows < 0 || d <= 0 || n_groups <= 0 || d % n_groups != 0) return GRKAN_ERR_INVALID_ARG;
     const int es = io_bytes(io);
@@ -53,87 +52,46 @@ grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, grkan_dtype
     const int64_t seg_vecs = seg_bytes / 16;
     if (seg_vecs > 1024) return GRKAN_ERR_UNSUPPORTED;
 
-    int block, rpi;
-    if (seg_vecs <= 256) {
-        // Most rows per step that fit 256 threads with the fewest idle lanes in
-        // the last wave (a wave is 64 lanes); ties go to the larger block.
-        int best_k = 1;
-        double best_eff = -1.0;
-        for (int k = 1; k * seg_vecs <= 256; ++k) {
-            const int w = k * (int)seg_vecs;
-            const double eff = (double)w / (64.0 * ((w + 63) / 64));
-            if (eff >= best_eff) {
-                best_eff = eff;
-                best_k = k;
-            }
-        }
-        rpi = best_k;
-        block = best_k * (int)seg_vecs;
-    } else {
-        rpi = 1;
-        block = (int)seg_vecs;
+    // Rows per pass: the whole-wave block (a multiple of 64 lanes, so the DPP
+    // wave sums see only real lanes) closest to the kernel's target size; if
+    // no multiple of seg_vecs up to 1024 is a multiple of 64, pad the block
+    // with idle lanes instead.
+    const int kTargetBlock = target_block(io, pass, atomic_mode);
+    int rpi = 0;
+    for (int k = 1; k * seg_vecs <= 1024; ++k) {
+        const int w = k * (int)seg_vecs;
+        if (w % 64 != 0) continue;
+        if (rpi == 0 || std::abs(w - kTargetBlock) < std::abs(rpi * (int)seg_vecs - kTargetBlock)) rpi = k;
     }
+    if (rpi == 0) {
+        rpi = kTargetBlock / (int)seg_vecs;
+        if (rpi < 1) rpi = 1;
+    }
+    const int lanes = rpi * (int)seg_vecs;
+    const int u = unroll(io, pass);
     G->rows = rows;
     G->row_vecs = d * es / 16;
     G->seg_vecs = (int32_t)seg_vecs;
     G->rows_per_iter = rpi;
-    G->block = block;
+    G->lanes = lanes;
+    G->block = (lanes + 63) / 64 * 64;
     G->n_groups = n_groups;
-    G->steps = (rows + rpi - 1) / rpi;
-    // Slices bounded by the work (at least one unrolled iteration each) and the
-    // global budget; the device bound is applied in plan_device.
-    const int64_t u = unroll(io, pass);
-    int64_t cap = (kSliceBudget + n_groups - 1) / n_groups;
-    int64_t work = (G->steps + u - 1) / u;
-    if (work < 1) work = 1;
-    G->slices = (int32_t)(work < cap ? work : cap);
+    G->unroll = u;
+    const int64_t tile_rows = (int64_t)u * rpi;
+    G->tiles = (rows + tile_rows - 1) / tile_rows;
+    G->grid = 8 * (int64_t)n_groups * ((G->tiles + 7) / 8);
+    if (G->grid > INT32_MAX) return GRKAN_ERR_UNSUPPORTED;
     return GRKAN_OK;
 }
 
-// Per-device launch limits, filled on first use.
-struct DevCache {
-    int cus = 0;
-    // occupancy by (io, pass, block/64 - 1 .. for blocks that are multiples of
-    // 1..1024); entries are cached per exact block size below.
-};
+size_t partials_bytes(const Geometry &G) {
+    return (size_t)G.n_groups * kCoefs * (size_t)G.tiles * sizeof(float);
+}
 
+// Per-device CU count and occupancy, for grkan_query_launch only.
 constexpr int kMaxDev = 64;
 std::mutex g_mu;
 int g_cus[kMaxDev];
-// resident blocks per CU, indexed [device][io][pass][block]; 0 = unknown
-short g_occ[kMaxDev][2][2][1025];
-
-grkan_status_t plan_device(grkan_dtype_t io, int pass, Geometry *G, int *cus_out, int *occ_out) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return GRKAN_ERR_HIP;
-    if (dev < 0 || dev >= kMaxDev) return GRKAN_ERR_UNSUPPORTED;
-    const int ioi = (io == GRKAN_BF16) ? 1 : 0;
-    int cus, occ;
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        cus = g_cus[dev];
-        occ = g_occ[dev][ioi][pass][G->block];
-    }
-    if (cus == 0) {
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return GRKAN_ERR_HIP;
-    }
-    if (occ == 0) {
-        if (occupancy(io, pass, G->block, &occ) != hipSuccess) return GRKAN_ERR_HIP;
-        if (occ <= 0) return GRKAN_ERR_UNSUPPORTED;
-    }
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        g_cus[dev] = cus;
-        g_occ[dev][ioi][pass][G->block] = (short)occ;
-    }
-    int64_t by_device = ((int64_t)cus * occ) / G->n_groups;
-    if (by_device < 1) by_device = 1;
-    if (by_device < G->slices) G->slices = (int32_t)by_device;
-    if (cus_out) *cus_out = cus;
-    if (occ_out) *occ_out = occ;
-    return GRKAN_OK;
-}
 
 grkan_status_t from_hip(hipError_t e) { return e == hipSuccess ? GRKAN_OK : GRKAN_ERR_HIP; }
 
@@ -153,7 +111,7 @@ extern "C" grkan_status_t grkan_forward(const void *x, void *y, const float *A, 
                                         int64_t rows, int64_t d, int32_t n_groups,
                                         grkan_dtype_t io, hipStream_t stream) {
     Geometry G;
-    grkan_status_t st = plan_shape(rows, d, n_groups, io, 0, &G);
+    grkan_status_t st = plan_shape(rows, d, n_groups, io, 0, false, &G);
     if (st != GRKAN_OK) return st;
     if (!A || !B) return GRKAN_ERR_INVALID_ARG;
     if (!aligned(A, 4) || !aligned(B, 4)) return GRKAN_ERR_UNSUPPORTED;
@@ -165,18 +123,16 @@ extern "C" grkan_status_t grkan_forward(const void *x, void *y, const float *A, 
     const size_t cb = (size_t)n_groups * 6 * 4, bb = (size_t)n_groups * 4 * 4;
     if (overlap(y, bytes, A, cb) || overlap(y, bytes, B, bb)) return GRKAN_ERR_INVALID_ARG;
 
-    st = plan_device(io, 0, &G, nullptr, nullptr);
-    if (st != GRKAN_OK) return st;
     FwdArgs a{x, y, A, B, G};
     return from_hip(launch_forward(io, a, stream));
 }
 
 extern "C" size_t grkan_backward_workspace_size(int64_t rows, int64_t d, int32_t n_groups,
                                                 grkan_dtype_t io, uint32_t flags) {
-    if (!(flags & GRKAN_DETERMINISTIC)) return 0;
+    if (flags != 0) return 0;
     Geometry G;
-    if (plan_shape(rows, d, n_groups, io, 1, &G) != GRKAN_OK) return 0;
-    return (size_t)n_groups * (size_t)G.slices * kCoefs * sizeof(double);
+    if (plan_shape(rows, d, n_groups, io, 1, false, &G) != GRKAN_OK) return 0;
+    return partials_bytes(G);
 }
 
 extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const float *A,
@@ -185,10 +141,10 @@ extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const fl
                                          grkan_dtype_t io, uint32_t flags, void *workspace,
                                          size_t workspace_bytes, hipStream_t stream) {
     Geometry G;
-    grkan_status_t st = plan_shape(rows, d, n_groups, io, 1, &G);
+    if (flags & ~(uint32_t)(GRKAN_BLOCK_ATOMIC | GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
+    if ((flags & GRKAN_BLOCK_ATOMIC) && (flags & GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
+    grkan_status_t st = plan_shape(rows, d, n_groups, io, 1, flags != 0, &G);
     if (st != GRKAN_OK) return st;
-    if (flags & ~(uint32_t)(GRKAN_DETERMINISTIC | GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
-    if ((flags & GRKAN_DETERMINISTIC) && (flags & GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
     if (!A || !B || !dA || !dB) return GRKAN_ERR_INVALID_ARG;
     if (!aligned(A, 4) || !aligned(B, 4) || !aligned(dA, 4) || !aligned(dB, 4))
         return GRKAN_ERR_UNSUPPORTED;
@@ -206,9 +162,9 @@ extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const fl
     for (int i = 0; i < 5; ++i)
         if (overlap(dA, ab, others[i], sizes[i]) || overlap(dB, bb, others[i], sizes[i]))
             return GRKAN_ERR_INVALID_ARG;
-    const bool det = (flags & GRKAN_DETERMINISTIC) != 0;
+    const bool det = flags == 0;
     if (det && rows > 0) {
-        const size_t need = (size_t)n_groups * (size_t)G.slices * kCoefs * sizeof(double);
+        const size_t need = partials_bytes(G);
         if (!workspace || workspace_bytes < need) return GRKAN_ERR_INVALID_ARG;
         if (!aligned(workspace, 16)) return GRKAN_ERR_UNSUPPORTED;
         for (int i = 0; i < 5; ++i)
@@ -224,9 +180,7 @@ extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const fl
         if (st != GRKAN_OK) return st;
         return from_hip(launch_naive(io, x, dy, dx, A, B, dA, dB, rows, d, n_groups, stream));
     }
-    st = plan_device(io, 1, &G, nullptr, nullptr);
-    if (st != GRKAN_OK) return st;
-    BwdArgs a{x, dy, dx, A, B, dA, dB, static_cast<double *>(workspace),
+    BwdArgs a{x, dy, dx, A, B, dA, dB, static_cast<float *>(workspace),
               det ? kModePartials : kModeAtomic, G};
     if (!det) {
         st = from_hip(launch_zero(dA, dB, n_groups, stream));
@@ -235,24 +189,34 @@ extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const fl
     }
     st = from_hip(launch_backward(io, a, stream));
     if (st != GRKAN_OK) return st;
-    return from_hip(launch_merge(a.partials, n_groups, G.slices, dA, dB, stream));
+    return from_hip(launch_merge(a.partials, n_groups, G.tiles, dA, dB, stream));
 }
 
 extern "C" grkan_status_t grkan_query_launch(int64_t rows, int64_t d, int32_t n_groups,
                                              grkan_dtype_t io, int32_t pass,
                                              grkan_launch_t *out) {
-    if (!out || (pass != 0 && pass != 1)) return GRKAN_ERR_INVALID_ARG;
+    if (!out || pass < 0 || pass > 2) return GRKAN_ERR_INVALID_ARG;
     Geometry G;
-    grkan_status_t st = plan_shape(rows, d, n_groups, io, pass, &G);
+    grkan_status_t st = plan_shape(rows, d, n_groups, io, pass ? 1 : 0, pass == 2, &G);
     if (st != GRKAN_OK) return st;
-    int cus = 0, occ = 0;
-    st = plan_device(io, pass, &G, &cus, &occ);
-    if (st != GRKAN_OK) return st;
+    int dev = 0, cus = 0, occ = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return GRKAN_ERR_HIP;
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        cus = g_cus[dev];
+    }
+    if (cus == 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return GRKAN_ERR_HIP;
+        std::lock_guard<std::mutex> lock(g_mu);
+        g_cus[dev] = cus;
+    }
+    if (occupancy(io, pass ? 1 : 0, G.block, &occ) != hipSuccess) return GRKAN_ERR_HIP;
     out->block = G.block;
     out->rows_per_iter = G.rows_per_iter;
-    out->unroll = unroll(io, pass);
-    out->slices = G.slices;
-    out->grid = (int64_t)G.slices * n_groups;
+    out->unroll = G.unroll;
+    out->tiles = G.tiles;
+    out->grid = G.grid;
     out->cus = cus;
     out->blocks_per_cu = occ;
     return GRKAN_OK;

@@ -110,16 +110,18 @@ __device__ static inline float rational(float x, const Coefs &c) {
 
 // Constants of the backward pass derived from one group's coefficients.
 struct BwdCoefs {
-    float a[kNumA];     // a_0..a_5
+    float a[kNumA];       // a_0..a_5
     float da[kNumA - 1];  // i * a_i, i = 1..5   (P')
-    float b[kNumB];     // b_1..b_4
-    float db[kNumB];    // j * b_j, j = 1..4   (Q')
-    float kb[kNumB];    // 2^-18 |b_j|: rounding guard of the sign of Q
-    bool q_zero;        // b_1 = .. = b_4 = 0: Q vanishes identically, s = 0
+    float b[kNumB];       // b_1..b_4
+    float db[kNumB];      // j * b_j, j = 1..4   (Q')
+    float kguard;         // 2^-18 * (|b_1| + .. + |b_4|): rounding guard of sign(Q)
+    bool q_zero;          // b_1 = .. = b_4 = 0: Q vanishes identically, s = 0
 };
 
-// Margin of the sign guard: |fl(q) - q| stays below ~5 * 2^-24 * sum|b_j||x|^(j-1)
-// for the evaluation order used here; 2^-18 leaves a factor > 10 of slack.
+// The sign guard.  The fp32 Q below differs from the exact Q(x) by at most
+// about 6 * 2^-24 * sum_j |b_j| |x|^j, and sum_j |b_j| |x|^j is at most
+// (sum_j |b_j|) * (|x| + x^4).  So |Q| > 2^-18 (sum_j |b_j|) (|x| + x^4)
+// -- ten times that bound -- proves Q != 0 and sign(fl(Q)) = sign(Q).
 constexpr float kSignGuard = 1.0f / 262144.0f;
 
 __device__ static inline BwdCoefs derive(const Coefs &c) {
@@ -128,12 +130,14 @@ __device__ static inline BwdCoefs derive(const Coefs &c) {
     for (int i = 0; i < kNumA; ++i) k.a[i] = c.a[i];
 #pragma unroll
     for (int i = 1; i < kNumA; ++i) k.da[i - 1] = (float)i * c.a[i];
+    float bsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < kNumB; ++j) {
         k.b[j] = c.b[j];
         k.db[j] = (float)(j + 1) * c.b[j];
-        k.kb[j] = kSignGuard * fabsf(c.b[j]);
+        bsum += fabsf(c.b[j]);
     }
+    k.kguard = kSignGuard * bsum;
     k.q_zero = (c.b[0] == 0.0f) && (c.b[1] == 0.0f) && (c.b[2] == 0.0f) && (c.b[3] == 0.0f);
     return k;
 }
@@ -163,48 +167,45 @@ __device__ static inline int sign_q_exact(float xf, const BwdCoefs &k) {
     return (q > 0.0) - (q < 0.0);
 }
 
-// Q(x) = x q(x) in fp32 and its rounding scale 2^-18 * sum_j |b_j| |x|^j.
-// When |Q| is above the scale, Q != 0 and the fp32 sign of Q is the true one.
-// The backward pass and its correction pass both decide through this one
-// function, so they always agree on which elements are guarded.
-struct QGuard {
-    float Q;
+// Everything the backward needs about one element, fast fp32 evaluation.
+// s = sign(Q) is taken from the fp32 Q; `sure` says whether the guard proves
+// that sign right.  When it does not (x == 0, x within rounding of a root of
+// Q, NaN), the element still gets the fp32 sign here and exact_fix() later
+// swaps in the exact one.  One function so that the hot loop and the fix
+// agree bit for bit.
+struct ElemBwd {
+    float dx;   // dY (P'/D - s P Q'/D^2)
+    float w;    // dY / D          (dA terms: w x^i)
+    float v;    // dY P / D^2
+    float sv;   // s v             (dB terms: -sv x^j)
+    float Qd;   // Q'
+    float wPd;  // w P'
     bool sure;
 };
-__device__ static inline QGuard q_guard(float x, float x2, float x3, const BwdCoefs &k) {
-    const float q = fmaf(k.b[3], x3, fmaf(k.b[2], x2, fmaf(k.b[1], x, k.b[0])));
-    const float Q = x * q;
-    const float ax = fabsf(x);
-    const float guard = ax * fmaf(k.kb[3], fabsf(x3), fmaf(k.kb[2], x2, fmaf(k.kb[1], ax, k.kb[0])));
-    return QGuard{Q, fabsf(Q) > guard};
-}
 
-// Per-element backward, fast part.  Returns dX and adds the element's ten
-// gradient terms into acc (dA terms dY x^i / D, then dB terms -dY s P x^j / D^2).
-//
-// s = sign(Q) is taken from the fp32 Q when q_guard() is sure of it.
-// Otherwise -- x == 0, a group with b = 0, x within rounding of a root of Q,
-// NaN -- the element is computed with s = 0 and *guarded* is set; the caller
-// later applies exact_sign_terms() to add the s-terms with the exact sign.
-// The hot loop thus has no data-dependent branch and a small register
-// footprint.
-__device__ static inline float backward_element(float x, float dy, const BwdCoefs &k,
-                                                float (&acc)[kNumCoef], bool &guarded) {
-    const float x2 = x * x;
-    const float x3 = x2 * x;
-    const float x4 = x2 * x2;
-    const float x5 = x4 * x;
+__device__ static inline ElemBwd backward_element(float x, float x2, float x3, float x4, float x5,
+                                                  float dy, const BwdCoefs &k) {
     const float P = fmaf(k.a[5], x5, fmaf(k.a[4], x4, fmaf(k.a[3], x3, fmaf(k.a[2], x2,
                     fmaf(k.a[1], x, k.a[0])))));
     const float Pd = fmaf(k.da[4], x4, fmaf(k.da[3], x3, fmaf(k.da[2], x2, fmaf(k.da[1], x, k.da[0]))));
+    const float q = fmaf(k.b[3], x3, fmaf(k.b[2], x2, fmaf(k.b[1], x, k.b[0])));
     const float Qd = fmaf(k.db[3], x3, fmaf(k.db[2], x2, fmaf(k.db[1], x, k.db[0])));
-    const QGuard qg = q_guard(x, x2, x3, k);
-    const float r = __builtin_amdgcn_rcpf(1.0f + fabsf(qg.Q));
-    const float w = dy * r;      // dY / D
-    const float v = w * (P * r); // dY P / D^2
-    guarded = !qg.sure;
-    const float sv_fast = __uint_as_float(__float_as_uint(v) ^ (__float_as_uint(qg.Q) & 0x80000000u));
-    const float sv = qg.sure ? sv_fast : 0.0f;   // s * v
+    const float Q = x * q;
+    const float r = __builtin_amdgcn_rcpf(1.0f + fabsf(Q));
+    ElemBwd e;
+    e.w = dy * r;
+    e.v = e.w * (P * r);
+    e.sv = __uint_as_float(__float_as_uint(e.v) ^ (__float_as_uint(Q) & 0x80000000u));
+    e.sure = fabsf(Q) > k.kguard * (fabsf(x) + x4);
+    e.Qd = Qd;
+    e.wPd = e.w * Pd;
+    e.dx = fmaf(-e.sv, Qd, e.wPd);
+    return e;
+}
+
+// Adds one element's ten gradient terms (dA: w x^i; dB: -sv x^j) to acc.
+__device__ static inline void accumulate(float w, float sv, float x, float x2, float x3, float x4,
+                                         float x5, float (&acc)[kNumCoef]) {
     acc[0] += w;
     acc[1] = fmaf(w, x, acc[1]);
     acc[2] = fmaf(w, x2, acc[2]);
@@ -215,35 +216,43 @@ __device__ static inline float backward_element(float x, float dy, const BwdCoef
     acc[7] = fmaf(-sv, x2, acc[7]);
     acc[8] = fmaf(-sv, x3, acc[8]);
     acc[9] = fmaf(-sv, x4, acc[9]);
-    return fmaf(-sv, Qd, w * Pd);
 }
 
-// The s-terms a guarded element is missing, with s = sign(x) sign(q(x))
-// decided exactly (Q is exactly 0 at x = 0 and for a group with b = 0).
-// Returns false when s = 0 (nothing to add); otherwise sets ddx (to add to
-// dX) and tb[0..3] (to add to the dB sums).
-__device__ static inline bool exact_sign_terms(float x, float dy, const BwdCoefs &k, float &ddx,
-                                               float (&tb)[kNumB]) {
-    if (x == 0.0f || k.q_zero) return false;
-    const int s = sign_q_exact(x, k) * ((x > 0.0f) ? 1 : -1);
-    if (s == 0) return false;
-    const float x2 = x * x;
-    const float x3 = x2 * x;
-    const float x4 = x2 * x2;
-    const float x5 = x4 * x;
-    const float P = fmaf(k.a[5], x5, fmaf(k.a[4], x4, fmaf(k.a[3], x3, fmaf(k.a[2], x2,
-                    fmaf(k.a[1], x, k.a[0])))));
-    const float Qd = fmaf(k.db[3], x3, fmaf(k.db[2], x2, fmaf(k.db[1], x, k.db[0])));
-    const QGuard qg = q_guard(x, x2, x3, k);
-    const float r = __builtin_amdgcn_rcpf(1.0f + fabsf(qg.Q));
-    const float v = (dy * r) * (P * r);
-    const float sv = (s > 0) ? v : -v;
-    tb[0] = -sv * x;
-    tb[1] = -sv * x2;
-    tb[2] = -sv * x3;
-    tb[3] = -sv * x4;
-    ddx = -sv * Qd;
-    return true;
+// For an element whose sign was not proven: recomputes it, decides
+// s = sign(x) sign(q(x)) exactly (0 at x == 0), replaces the dB terms that
+// were accumulated with the fp32 sign and returns the exact dX.
+__device__ static inline float exact_fix(float x, float dy, const BwdCoefs &k, float (&acc)[kNumCoef]) {
+    const float x2 = x * x, x3 = x2 * x, x4 = x2 * x2, x5 = x4 * x;
+    const ElemBwd e = backward_element(x, x2, x3, x4, x5, dy, k);
+    if (e.sure) return e.dx;
+    const int s = (x == 0.0f || k.q_zero) ? 0 : sign_q_exact(x, k) * ((x > 0.0f) ? 1 : -1);
+    const float sv = (s == 0) ? 0.0f : ((s > 0) ? e.v : -e.v);
+    const float diff = e.sv - sv;  // undo -e.sv x^j, add -sv x^j
+    acc[6] = fmaf(diff, x, acc[6]);
+    acc[7] = fmaf(diff, x2, acc[7]);
+    acc[8] = fmaf(diff, x3, acc[8]);
+    acc[9] = fmaf(diff, x4, acc[9]);
+    return fmaf(-sv, e.Qd, e.wPd);
+}
+
+// ------------------------------------------------------ wave/block sums
+
+template <int CTRL, int ROW_MASK>
+__device__ static inline float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                  ROW_MASK, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave with DPP moves; the total ends in lane 63.
+// Fixed order (deterministic).  Requires all 64 lanes to exist.
+__device__ static inline float wave_sum_to_lane63(float v) {
+    v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]: pairs
+    v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]: quads
+    v += dpp_f32<0x141, 0xF>(v);  // row_half_mirror: groups of 8
+    v += dpp_f32<0x140, 0xF>(v);  // row_mirror: rows of 16
+    v += dpp_f32<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+    v += dpp_f32<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+    return v;
 }
 
 }  // namespace grkan

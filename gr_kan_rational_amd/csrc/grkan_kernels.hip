@@ -12,24 +12,27 @@
 // （Algorithm 2）") restructures the backward as a 2D grid of row tiles x
 // groups in which a block loads its group's coefficients once, accumulates
 // all of its gradient terms locally and then makes one global update per
-// coefficient, instead of one atomic per element and coefficient.  Here the
-// same (row slice, group) decomposition is shaped for CDNA4:
-//   * the launch is 1D with the group index fastest (blockIdx % n_groups), so
-//     consecutive workgroups -- which the dispatcher deals round-robin to the
-//     8 XCDs -- read neighbouring parts of the same rows, and with 8 groups
-//     every XCD keeps one group (its coefficients and its 128-byte lines);
-//   * the grid is sized to the resident capacity of the device (CUs x
-//     workgroups per CU), one wave of workgroups, each walking an equal
-//     contiguous range of row steps -- no tail of half-filled rounds;
-//   * a workgroup's lanes tile rows_per_iter rows x the group's 16-byte
-//     vectors, so every global access is a 16-byte load/store, a wave reads
-//     whole 128-byte lines, and a lane's column (hence its group) is fixed;
-//   * the gradient terms of one loop iteration are summed in fp32 registers,
-//     then carried in fp64 per lane, reduced across the wave by butterfly
-//     shuffles and across waves through LDS, and leave the workgroup either as
-//     ten fp32 atomics (one per coefficient, as in the pages' Algorithm 2) or
-//     as ten fp64 partials merged afterwards in a fixed order (the two-stage
-//     reduction of [PolyKAN]), which makes the result bitwise reproducible.
+// coefficient, instead of one atomic per element and coefficient.  The same
+// (row tile, group) decomposition is kept here, shaped for CDNA4 and HBM3E:
+//   * One workgroup per (tile, group), short-lived: it issues all its 16-byte
+//     loads at once, computes, stores and exits.  A large grid of such
+//     workgroups, dispatched in order, keeps the set of addresses in flight
+//     small and moving forward through memory, which HBM serves best; a
+//     persistent loop would also wait, each iteration, for the previous
+//     iteration's stores (gfx9 counts stores and loads in one counter).
+//   * The dispatcher deals consecutive workgroups round-robin to the 8 XCDs;
+//     workgroup b is mapped so that XCD (b mod 8) takes whole row tiles (all
+//     groups of tiles b mod 8, +8, +16, ...).  The 8 XCDs then work on
+//     different rows at any moment rather than all on the same ones.
+//   * Lanes cover rows_per_iter rows x the group's 16-byte vectors: each wave
+//     reads whole 128-byte lines, and a lane's group -- hence coefficients,
+//     which sit in scalar registers -- is the workgroup's.
+//   * Backward: the tile's gradient terms are summed in fp32 registers (at
+//     most 16 terms per lane), across the wave by DPP and across waves in
+//     LDS, then leave the workgroup as ten fp32 atomics (one per coefficient,
+//     as in the pages' Algorithm 2) or as ten partials merged afterwards in
+//     fp64 in a fixed order (the two-stage reduction of [PolyKAN]), which is
+//     bitwise reproducible: the tiling depends only on the shape.
 #include "grkan_device.h"
 #include "grkan_launch.h"
 
@@ -39,41 +42,59 @@ constexpr bool kNonTemporal = true;  // stream-once data: do not keep it in the 
 constexpr int kMaxBlock = 1024;
 constexpr int kMaxWaves = kMaxBlock / 64;
 
+// Tuning per (I/O type, pass): U = passes per workgroup (all of a lane's
+// loads are issued together), block = target workgroup size.  Chosen by
+// measurement on MI355X at the KAT-B shapes: the backward prefers small
+// blocks (its ~110 VGPRs allow 4 waves per SIMD; 3-wave blocks fill that
+// better than 6-wave ones) and 4 passes to amortise the block reduction.
 template <class IO, int pass> struct Tune;
-template <> struct Tune<float, 0> { static constexpr int U = 4; };
-template <> struct Tune<bf16io, 0> { static constexpr int U = 2; };
-template <> struct Tune<float, 1> { static constexpr int U = 4; };
-template <> struct Tune<bf16io, 1> { static constexpr int U = 2; };
+template <> struct Tune<float, 0> { static constexpr int U = 2, block = 384; };
+template <> struct Tune<bf16io, 0> { static constexpr int U = 2, block = 192; };
+template <> struct Tune<float, 1> { static constexpr int U = 4, block = 192; };
+template <> struct Tune<bf16io, 1> { static constexpr int U = 2, block = 192; };
+// One fp32 atomic per coefficient per workgroup serialises on the few cache
+// lines of dA and dB in L2, so the atomic mode uses 4x larger workgroups.
+constexpr int kAtomicModeBlock = 768;
 
 int unroll(grkan_dtype_t io, int pass) {
     if (io == GRKAN_BF16) return pass ? Tune<bf16io, 1>::U : Tune<bf16io, 0>::U;
     return pass ? Tune<float, 1>::U : Tune<float, 0>::U;
 }
 
-// Step range [s0, s1) of this workgroup, and the lane's vector offset.
-struct LaneMap {
-    int g;
-    int slice;
-    int64_t s0, s1, s1_full;
-    int64_t step_vecs;
-    int64_t lane_vec;
-    int roff;
+int target_block(grkan_dtype_t io, int pass, bool atomic_mode) {
+    if (pass == 1 && atomic_mode) return kAtomicModeBlock;
+    if (io == GRKAN_BF16) return pass ? Tune<bf16io, 1>::block : Tune<bf16io, 0>::block;
+    return pass ? Tune<float, 1>::block : Tune<float, 0>::block;
+}
+
+// (tile, group) of this workgroup; false for the padding workgroups of the
+// last round of 8 tiles.
+__device__ static inline bool tile_of(const Geometry &G, int &g, int64_t &tile) {
+    const int64_t b = blockIdx.x;
+    const int64_t k = b >> 3;
+    tile = (k / G.n_groups) * 8 + (b & 7);
+    g = (int)(k % G.n_groups);
+    return tile < G.tiles;
+}
+
+// Lane placement inside a tile.
+struct Lane {
+    int64_t off;     // vector offset of pass 0
+    int64_t stride;  // vectors between passes (rows_per_iter rows)
+    int64_t row;     // row of pass 0
+    bool active;     // one of the tile's `lanes` (not wave padding)
 };
 
-__device__ static inline LaneMap lane_map(const Geometry &G) {
-    LaneMap m;
-    m.g = blockIdx.x % G.n_groups;
-    m.slice = blockIdx.x / G.n_groups;
+__device__ static inline Lane lane_of(const Geometry &G, int g, int64_t tile, int U) {
     const int tid = threadIdx.x;
     const int col = tid % G.seg_vecs;
-    m.roff = tid / G.seg_vecs;
-    m.s0 = (int64_t)m.slice * G.steps / G.slices;
-    m.s1 = (int64_t)(m.slice + 1) * G.steps / G.slices;
-    const int64_t full = G.rows / G.rows_per_iter;  // steps whose rows all exist
-    m.s1_full = m.s1 < full ? m.s1 : full;
-    m.step_vecs = (int64_t)G.rows_per_iter * G.row_vecs;
-    m.lane_vec = (int64_t)m.roff * G.row_vecs + (int64_t)m.g * G.seg_vecs + col;
-    return m;
+    const int roff = tid / G.seg_vecs;
+    Lane l;
+    l.row = tile * (int64_t)U * G.rows_per_iter + roff;
+    l.off = l.row * G.row_vecs + (int64_t)g * G.seg_vecs + col;
+    l.stride = (int64_t)G.rows_per_iter * G.row_vecs;
+    l.active = tid < G.lanes;
+    return l;
 }
 
 // ----------------------------------------------------------------- forward
@@ -83,210 +104,174 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_fwd_kernel(FwdArgs a) {
     using V = Io<IO>;
     constexpr int E = V::kElems;
     const Geometry &G = a.geo;
-    const LaneMap m = lane_map(G);
-    const Coefs c = load_coefs(a.A, a.B, m.g);
-    const u32x4 *xp = static_cast<const u32x4 *>(a.x) + m.lane_vec;
-    u32x4 *yp = static_cast<u32x4 *>(a.y) + m.lane_vec;
+    int g;
+    int64_t tile;
+    if (!tile_of(G, g, tile)) return;
+    const Coefs c = load_coefs(a.A, a.B, g);
+    const Lane l = lane_of(G, g, tile, U);
+    const u32x4 *xp = static_cast<const u32x4 *>(a.x) + l.off;
+    u32x4 *yp = static_cast<u32x4 *>(a.y) + l.off;
 
-    int64_t s = m.s0;
-    for (; s + U <= m.s1_full; s += U) {
-        u32x4 in[U];
+    bool ok[U];
+    u32x4 in[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) in[u] = load16<kNonTemporal>(xp + (s + u) * m.step_vecs);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float f[E];
-            V::unpack(in[u], f);
-#pragma unroll
-            for (int e = 0; e < E; ++e) f[e] = rational(f[e], c);
-            store16<kNonTemporal>(yp + (s + u) * m.step_vecs, V::pack(f));
-        }
+    for (int u = 0; u < U; ++u) {
+        ok[u] = l.active && (l.row + (int64_t)u * G.rows_per_iter < G.rows);
+        in[u] = ok[u] ? load16<kNonTemporal>(xp + u * l.stride) : u32x4{0u, 0u, 0u, 0u};
     }
-    for (; s < m.s1; ++s) {
-        if (s * G.rows_per_iter + m.roff < G.rows) {
-            float f[E];
-            V::unpack(load16<kNonTemporal>(xp + s * m.step_vecs), f);
 #pragma unroll
-            for (int e = 0; e < E; ++e) f[e] = rational(f[e], c);
-            store16<kNonTemporal>(yp + s * m.step_vecs, V::pack(f));
-        }
+    for (int u = 0; u < U; ++u) {
+        float f[E];
+        V::unpack(in[u], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] = rational(f[e], c);
+        if (ok[u]) store16<kNonTemporal>(yp + u * l.stride, V::pack(f));
     }
 }
 
 // ---------------------------------------------------------------- backward
 
-// Sum v[0..N) over the workgroup; the totals are valid in threads 0..N-1 as
-// out (thread k holds total k).  Fixed order: butterfly within each wave,
-// then waves in index order.
-template <int N>
-__device__ static inline double block_sum(double (&v)[N], double (*lds)[N]) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int nwaves = (blockDim.x + 63) >> 6;
-    // Lanes [0, nlane) exist in this wave (the last wave of a block that is not
-    // a multiple of 64 is partial).  Reads of a lane that does not exist count
-    // as 0; every lane lane 0 depends on then holds a sum over existing lanes
-    // only, so lane 0 ends with the wave total.
-    const int nlane = min(64, (int)blockDim.x - wave * 64);
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-#pragma unroll
-        for (int mask = 32; mask >= 1; mask >>= 1) {
-            const double o = __shfl_xor(v[k], mask, 64);
-            v[k] += ((lane ^ mask) < nlane) ? o : 0.0;
-        }
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int k = 0; k < N; ++k) lds[wave][k] = v[k];
-    }
-    __syncthreads();
-    double t = 0.0;
-    if (threadIdx.x < N) {
-        for (int w = 0; w < nwaves; ++w) t += lds[w][threadIdx.x];
-    }
-    return t;
-}
-
-// Exact-sign correction of the steps [lo, hi) of one lane: re-reads x, dy and
-// the dx it stored, and for every guarded element adds the s-terms with the
-// exact sign (to dx in place and to the dB sums).  Runs only for lanes that
-// met a guarded element, over the steps that held one.
-template <class IO>
-__device__ __forceinline__ static void correct_steps(const u32x4 *xp, const u32x4 *dyp, u32x4 *dxp,
-                                                  const BwdCoefs &k, const Geometry &G,
-                                                  const LaneMap &m, int64_t lo, int64_t hi,
-                                                  double (&acc64)[kNumCoef]) {
+// One tile's elements: dX stored, the ten gradient sums of this lane in acc.
+// The rare exact-sign fix runs once per tile, before any dX is stored; it
+// re-reads x and dy, which is safe even when dx aliases x or dy.
+template <class IO, int U, bool QZERO>
+__device__ static inline void bwd_tile(const BwdArgs &a, const BwdCoefs &k, const Lane &l,
+                                       float (&acc)[kNumCoef]) {
     using V = Io<IO>;
     constexpr int E = V::kElems;
-    for (int64_t t = lo; t < hi; ++t) {
-        if (t * G.rows_per_iter + m.roff >= G.rows) break;
-        float xf[E], dyf[E], dxf[E];
-        V::unpack(xp[t * m.step_vecs], xf);
-        V::unpack(dyp[t * m.step_vecs], dyf);
-        V::unpack(dxp[t * m.step_vecs], dxf);
-        bool changed = false;
+    const Geometry &G = a.geo;
+    const u32x4 *xp = static_cast<const u32x4 *>(a.x) + l.off;
+    const u32x4 *dyp = static_cast<const u32x4 *>(a.dy) + l.off;
+    u32x4 *dxp = static_cast<u32x4 *>(a.dx) + l.off;
+
+    bool ok[U];
+    u32x4 xin[U], din[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        ok[u] = l.active && (l.row + (int64_t)u * G.rows_per_iter < G.rows);
+        xin[u] = ok[u] ? load16<kNonTemporal>(xp + u * l.stride) : u32x4{0u, 0u, 0u, 0u};
+        din[u] = ok[u] ? load16<kNonTemporal>(dyp + u * l.stride) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float dxf[U][E];
+    bool sure = true;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float xf[E], dyf[E];
+        V::unpack(xin[u], xf);
+        V::unpack(din[u], dyf);
+#pragma unroll
         for (int e = 0; e < E; ++e) {
-            const float x = xf[e];
-            const QGuard qg = q_guard(x, x * x, (x * x) * x, k);
-            float ddx, tb[kNumB];
-            if (!qg.sure && exact_sign_terms(x, dyf[e], k, ddx, tb)) {
-                dxf[e] += ddx;
-                for (int j = 0; j < kNumB; ++j) acc64[kNumA + j] += (double)tb[j];
-                changed = true;
+            const float x = xf[e], dy = dyf[e];
+            const float x2 = x * x, x3 = x2 * x, x4 = x2 * x2, x5 = x4 * x;
+            if constexpr (QZERO) {
+                // Q == 0: D = 1, s = 0: dX = dY P', dA terms dY x^i, no dB terms.
+                const float Pd = fmaf(k.da[4], x4, fmaf(k.da[3], x3, fmaf(k.da[2], x2,
+                                 fmaf(k.da[1], x, k.da[0]))));
+                dxf[u][e] = dy * Pd;
+                accumulate(dy, 0.0f, x, x2, x3, x4, x5, acc);
+            } else {
+                const ElemBwd eb = backward_element(x, x2, x3, x4, x5, dy, k);
+                accumulate(eb.w, eb.sv, x, x2, x3, x4, x5, acc);
+                dxf[u][e] = eb.dx;
+                sure = sure && eb.sure;
             }
         }
-        if (changed) dxp[t * m.step_vecs] = V::pack(dxf);
     }
+    if constexpr (!QZERO) {
+        // Rare: some element's sign of Q was not proven by the fp32 guard.
+        if (__builtin_expect(!sure, 0)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (ok[u]) {
+                    float xf[E], dyf[E];
+                    V::unpack(xp[u * l.stride], xf);
+                    V::unpack(dyp[u * l.stride], dyf);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) dxf[u][e] = exact_fix(xf[e], dyf[e], k, acc);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (ok[u]) store16<kNonTemporal>(dxp + u * l.stride, V::pack(dxf[u]));
 }
 
 template <class IO, int U>
 __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
-    using V = Io<IO>;
-    constexpr int E = V::kElems;
     const Geometry &G = a.geo;
-    const LaneMap m = lane_map(G);
-    const BwdCoefs k = derive(load_coefs(a.A, a.B, m.g));
-    const u32x4 *xp = static_cast<const u32x4 *>(a.x) + m.lane_vec;
-    const u32x4 *dyp = static_cast<const u32x4 *>(a.dy) + m.lane_vec;
-    u32x4 *dxp = static_cast<u32x4 *>(a.dx) + m.lane_vec;
+    int g;
+    int64_t tile;
+    if (!tile_of(G, g, tile)) return;
+    const BwdCoefs k = derive(load_coefs(a.A, a.B, g));
+    const Lane l = lane_of(G, g, tile, U);
+    float acc[kNumCoef];
+#pragma unroll
+    for (int i = 0; i < kNumCoef; ++i) acc[i] = 0.0f;
+    if (k.q_zero)
+        bwd_tile<IO, U, true>(a, k, l, acc);
+    else
+        bwd_tile<IO, U, false>(a, k, l, acc);
 
-    double acc64[kNumCoef];
+    // Workgroup sum of the ten terms: DPP within each wave (total in lane 63),
+    // then the waves in index order in fp64.
+    __shared__ float lds[kMaxWaves][kNumCoef];
+    const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < kNumCoef; ++i) acc64[i] = 0.0;
-    // Steps [fix_lo, fix_hi) hold every guarded element of this lane.
-    int64_t fix_lo = m.s1, fix_hi = m.s0;
-
-    int64_t s = m.s0;
-    for (; s + U <= m.s1_full; s += U) {
-        u32x4 xin[U], din[U];
+    for (int i = 0; i < kNumCoef; ++i) acc[i] = wave_sum_to_lane63(acc[i]);
+    if ((threadIdx.x & 63) == 63) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            xin[u] = load16<kNonTemporal>(xp + (s + u) * m.step_vecs);
-            din[u] = load16<kNonTemporal>(dyp + (s + u) * m.step_vecs);
-        }
-        float acc[kNumCoef];
-#pragma unroll
-        for (int i = 0; i < kNumCoef; ++i) acc[i] = 0.0f;
-        bool any = false;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float xf[E], dyf[E], dxf[E];
-            V::unpack(xin[u], xf);
-            V::unpack(din[u], dyf);
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                bool gd;
-                dxf[e] = backward_element(xf[e], dyf[e], k, acc, gd);
-                any |= gd;
-            }
-            store16<kNonTemporal>(dxp + (s + u) * m.step_vecs, V::pack(dxf));
-        }
-#pragma unroll
-        for (int i = 0; i < kNumCoef; ++i) acc64[i] += (double)acc[i];
-        fix_lo = (any && s < fix_lo) ? s : fix_lo;
-        fix_hi = any ? s + U : fix_hi;
+        for (int i = 0; i < kNumCoef; ++i) lds[wave][i] = acc[i];
     }
-    for (; s < m.s1; ++s) {
-        if (s * G.rows_per_iter + m.roff < G.rows) {
-            float xf[E], dyf[E], dxf[E];
-            V::unpack(load16<kNonTemporal>(xp + s * m.step_vecs), xf);
-            V::unpack(load16<kNonTemporal>(dyp + s * m.step_vecs), dyf);
-            float acc[kNumCoef];
-#pragma unroll
-            for (int i = 0; i < kNumCoef; ++i) acc[i] = 0.0f;
-            bool any = false;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                bool gd;
-                dxf[e] = backward_element(xf[e], dyf[e], k, acc, gd);
-                any |= gd;
-            }
-            store16<kNonTemporal>(dxp + s * m.step_vecs, V::pack(dxf));
-#pragma unroll
-            for (int i = 0; i < kNumCoef; ++i) acc64[i] += (double)acc[i];
-            fix_lo = (any && s < fix_lo) ? s : fix_lo;
-            fix_hi = any ? s + 1 : fix_hi;
-        }
-    }
-    if (__builtin_expect(fix_lo < fix_hi, 0) && !k.q_zero)
-        correct_steps<IO>(xp, dyp, dxp, k, G, m, fix_lo, fix_hi, acc64);
-
-    __shared__ double lds[kMaxWaves][kNumCoef];
-    const double total = block_sum<kNumCoef>(acc64, lds);
+    __syncthreads();
     const int t = threadIdx.x;
     if (t < kNumCoef) {
+        const int nwaves = G.block >> 6;
+        double total = 0.0;
+        for (int w = 0; w < nwaves; ++w) total += (double)lds[w][t];
         if (a.mode == kModePartials) {
-            a.partials[((int64_t)m.g * G.slices + m.slice) * kNumCoef + t] = total;
+            a.partials[((int64_t)g * kNumCoef + t) * G.tiles + tile] = (float)total;
         } else {
-            float *dst = (t < kNumA) ? (a.dA + m.g * kNumA + t) : (a.dB + m.g * kNumB + (t - kNumA));
+            float *dst = (t < kNumA) ? (a.dA + g * kNumA + t) : (a.dB + g * kNumB + (t - kNumA));
             unsafeAtomicAdd(dst, (float)total);
         }
     }
 }
 
-// Second stage of the deterministic mode: one wave per group adds that
-// group's slice partials in a fixed order and writes fp32 dA, dB.
-__global__ __launch_bounds__(64) void grkan_merge_kernel(const double *__restrict__ partials,
-                                                          int32_t slices, float *__restrict__ dA,
-                                                          float *__restrict__ dB) {
-    const int g = blockIdx.x;
-    const int lane = threadIdx.x;
-    double acc[kNumCoef];
+// Second stage of the deterministic mode: workgroup (g, k) adds the tile
+// partials of group g, coefficient k in a fixed order in fp64.  Each thread
+// issues all of its loads before adding, so the kernel costs about one memory
+// round trip rather than one per loop iteration.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeLoads = 8;
+__global__ __launch_bounds__(kMergeThreads) void grkan_merge_kernel(const float *__restrict__ partials,
+                                                                    int64_t tiles, float *__restrict__ dA,
+                                                                    float *__restrict__ dB) {
+    const int gk = blockIdx.x;
+    const float *p = partials + (int64_t)gk * tiles;
+    double s = 0.0;
+    for (int64_t base = 0; base < tiles; base += (int64_t)kMergeThreads * kMergeLoads) {
+        float v[kMergeLoads];
 #pragma unroll
-    for (int i = 0; i < kNumCoef; ++i) acc[i] = 0.0;
-    const double *base = partials + (int64_t)g * slices * kNumCoef;
-    for (int p = lane; p < slices; p += 64) {
+        for (int i = 0; i < kMergeLoads; ++i) {
+            const int64_t t = base + (int64_t)i * kMergeThreads + threadIdx.x;
+            v[i] = (t < tiles) ? p[t] : 0.0f;
+        }
 #pragma unroll
-        for (int i = 0; i < kNumCoef; ++i) acc[i] += base[(int64_t)p * kNumCoef + i];
+        for (int i = 0; i < kMergeLoads; ++i) s += (double)v[i];
     }
 #pragma unroll
-    for (int i = 0; i < kNumCoef; ++i) {
-#pragma unroll
-        for (int mask = 32; mask >= 1; mask >>= 1) acc[i] += __shfl_xor(acc[i], mask, 64);
+    for (int mask = 32; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask, 64);
+    __shared__ double lds[kMergeThreads / 64];
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double total = 0.0;
+        for (int w = 0; w < kMergeThreads / 64; ++w) total += lds[w];
+        const int g = gk / kNumCoef, k = gk % kNumCoef;
+        if (k < kNumA) dA[g * kNumA + k] = (float)total;
+        else dB[g * kNumB + k - kNumA] = (float)total;
     }
-    if (lane < kNumA) dA[g * kNumA + lane] = (float)acc[lane];
-    else if (lane < kNumCoef) dB[g * kNumB + lane - kNumA] = (float)acc[lane];
 }
 
 __global__ __launch_bounds__(256) void grkan_zero_kernel(float *__restrict__ dA,
@@ -300,16 +285,14 @@ __global__ __launch_bounds__(256) void grkan_zero_kernel(float *__restrict__ dA,
 
 template <class IO>
 static hipError_t fwd_impl(const FwdArgs &a, hipStream_t s) {
-    const int64_t grid = (int64_t)a.geo.slices * a.geo.n_groups;
-    hipLaunchKernelGGL((grkan_fwd_kernel<IO, Tune<IO, 0>::U>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((grkan_fwd_kernel<IO, Tune<IO, 0>::U>), dim3((unsigned)a.geo.grid),
                        dim3(a.geo.block), 0, s, a);
     return hipGetLastError();
 }
 
 template <class IO>
 static hipError_t bwd_impl(const BwdArgs &a, hipStream_t s) {
-    const int64_t grid = (int64_t)a.geo.slices * a.geo.n_groups;
-    hipLaunchKernelGGL((grkan_bwd_kernel<IO, Tune<IO, 1>::U>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((grkan_bwd_kernel<IO, Tune<IO, 1>::U>), dim3((unsigned)a.geo.grid),
                        dim3(a.geo.block), 0, s, a);
     return hipGetLastError();
 }
@@ -322,10 +305,10 @@ hipError_t launch_backward(grkan_dtype_t io, const BwdArgs &a, hipStream_t s) {
     return io == GRKAN_BF16 ? bwd_impl<bf16io>(a, s) : bwd_impl<float>(a, s);
 }
 
-hipError_t launch_merge(const double *partials, int32_t n_groups, int32_t slices, float *dA,
+hipError_t launch_merge(const float *partials, int32_t n_groups, int64_t tiles, float *dA,
                         float *dB, hipStream_t s) {
-    hipLaunchKernelGGL(grkan_merge_kernel, dim3((unsigned)n_groups), dim3(64), 0, s, partials,
-                       slices, dA, dB);
+    hipLaunchKernelGGL(grkan_merge_kernel, dim3((unsigned)(n_groups * kNumCoef)), dim3(kMergeThreads), 0, s,
+                       partials, tiles, dA, dB);
     return hipGetLastError();
 }
 

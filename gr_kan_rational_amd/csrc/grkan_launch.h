@@ -10,18 +10,21 @@
 namespace grkan {
 
 // Geometry of one launch over a [rows][d] tensor split into n_groups groups.
-// A workgroup (group g, slice p) walks "steps" of rows_per_iter rows; its
-// lanes tile those rows x the group's seg_vecs 16-byte vectors, so a lane
-// always touches the same column of the group and only the row changes.
+// The tensor is cut into tiles of unroll * rows_per_iter rows; one workgroup
+// handles one (tile, group) pair: its `lanes` threads cover rows_per_iter
+// rows x the group's seg_vecs 16-byte vectors, `unroll` times over.  The
+// block is `lanes` rounded up to whole waves (the extra lanes idle).
 struct Geometry {
     int64_t rows;
     int64_t row_vecs;       // 16-byte vectors per row (d * bytes / 16)
     int32_t seg_vecs;       // 16-byte vectors per group per row
-    int32_t rows_per_iter;  // rows covered by one step of a workgroup
-    int32_t block;          // threads per workgroup = rows_per_iter * seg_vecs
+    int32_t rows_per_iter;  // rows covered by one pass of a workgroup's lanes
+    int32_t lanes;          // rows_per_iter * seg_vecs
+    int32_t block;          // lanes rounded up to a multiple of 64
     int32_t n_groups;
-    int32_t slices;         // workgroups per group
-    int64_t steps;          // ceil(rows / rows_per_iter)
+    int32_t unroll;         // passes per tile
+    int64_t tiles;          // ceil(rows / (unroll * rows_per_iter))
+    int64_t grid;           // 8 * n_groups * ceil(tiles / 8)
 };
 
 struct FwdArgs {
@@ -42,17 +45,19 @@ struct BwdArgs {
     const float *B;
     float *dA;
     float *dB;
-    double *partials;  // [n_groups][slices][10] in kModePartials
+    float *partials;  // [n_groups][10][tiles] in kModePartials
     int32_t mode;
     Geometry geo;
 };
 
-// Compile-time loop unroll (steps whose loads are issued together).
+// Passes per workgroup and target workgroup size of a kernel (pass 0 =
+// forward, 1 = backward; the backward's atomic mode has its own block size).
 int unroll(grkan_dtype_t io, int pass);
+int target_block(grkan_dtype_t io, int pass, bool atomic_mode);
 
 hipError_t launch_forward(grkan_dtype_t io, const FwdArgs &a, hipStream_t s);
 hipError_t launch_backward(grkan_dtype_t io, const BwdArgs &a, hipStream_t s);
-hipError_t launch_merge(const double *partials, int32_t n_groups, int32_t slices, float *dA,
+hipError_t launch_merge(const float *partials, int32_t n_groups, int64_t tiles, float *dA,
                         float *dB, hipStream_t s);
 hipError_t launch_zero(float *dA, float *dB, int32_t n_groups, hipStream_t s);
 hipError_t launch_naive(grkan_dtype_t io, const void *x, const void *dy, void *dx, const float *A,

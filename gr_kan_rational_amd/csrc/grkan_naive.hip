@@ -46,14 +46,10 @@ __global__ __launch_bounds__(256) void grkan_bwd_naive_kernel(const void *x, con
 #pragma unroll
         for (int c = 0; c < kNumCoef; ++c) acc[c] = 0.0f;
         const float xv = Scalar<IO>::load(x, i), dyv = Scalar<IO>::load(dy, i);
-        bool guarded;
-        float dxv = backward_element(xv, dyv, k, acc, guarded);
-        float ddx, tb[kNumB];
-        if (guarded && exact_sign_terms(xv, dyv, k, ddx, tb)) {
-            dxv += ddx;
-#pragma unroll
-            for (int j = 0; j < kNumB; ++j) acc[kNumA + j] += tb[j];
-        }
+        const float x2 = xv * xv, x3 = x2 * xv, x4 = x2 * x2, x5 = x4 * xv;
+        const ElemBwd e = backward_element(xv, x2, x3, x4, x5, dyv, k);
+        accumulate(e.w, e.sv, xv, x2, x3, x4, x5, acc);
+        const float dxv = e.sure ? e.dx : exact_fix(xv, dyv, k, acc);
         Scalar<IO>::store(dx, i, dxv);
 #pragma unroll
         for (int c = 0; c < kNumA; ++c) unsafeAtomicAdd(dA + g * kNumA + c, acc[c]);

@@ -68,15 +68,18 @@ typedef enum {
 } grkan_dtype_t;
 
 enum {
-    /* Backward: per-workgroup fp64 partial sums written to `workspace`, then
-       merged by a second kernel in a fixed order.  The result is bitwise
-       reproducible for a given shape, device and library build. */
-    GRKAN_DETERMINISTIC = 1u << 0,
-    /* Backward: the per-element atomic baseline (every element adds its ten
-       terms to dA/dB with global fp32 atomics), the scheme the pages identify
-       as the bottleneck ([FlashKAT notes], section "2. 原始 KAT 的 atomic add
-       问题分析").  For measurement and error comparison only. */
-    GRKAN_NAIVE_ATOMIC = 1u << 1
+    /* Backward reduction schemes.  The default (flags = 0) writes one partial
+       sum per (row tile, group, coefficient) to `workspace` and merges them
+       with a second kernel in fp64 in a fixed order: bitwise reproducible for
+       a given shape and library build, on any device, and accurate to the
+       fp32 rounding of the individual terms.  The two flags below select the
+       schemes the pages compare ([FlashKAT notes], sections "2. 原始 KAT 的
+       atomic add 问题分析" and "3. FlashKAT 核函数重构（Algorithm 2）"); they
+       are kept for measurement and their fp32 accumulation error grows with
+       the number of workgroups or elements, as the pages' rounding-error
+       table shows for their GPUs. */
+    GRKAN_BLOCK_ATOMIC = 1u << 0, /* one fp32 atomic add per coefficient per workgroup */
+    GRKAN_NAIVE_ATOMIC = 1u << 1  /* ten fp32 atomic adds per element (KAT's original) */
 };
 
 /*
@@ -99,13 +102,14 @@ GRKAN_API grkan_status_t grkan_forward(const void *x, void *y, const float *A, c
  *   dA, dB    fp32 outputs [n_groups][6], [n_groups][4]; overwritten, not
  *             accumulated; must not overlap any other argument.  rows == 0
  *             writes zeros.
- *   flags     0 (one fp32 atomic add per coefficient per workgroup into dA,
- *             dB after a zero fill), GRKAN_DETERMINISTIC, or
- *             GRKAN_NAIVE_ATOMIC.  Other bits, or both, are INVALID_ARG.
+ *   flags     0 (two-stage deterministic reduction), GRKAN_BLOCK_ATOMIC or
+ *             GRKAN_NAIVE_ATOMIC (both zero dA, dB first).  Other bits, or
+ *             both, are INVALID_ARG.
  *   workspace device memory of at least grkan_backward_workspace_size()
- *             bytes, 16-byte aligned, for GRKAN_DETERMINISTIC; ignored (may
- *             be NULL) otherwise.  Its contents on entry do not matter.  Two
- *             calls in flight at once must not share one workspace.
+ *             bytes, 16-byte aligned, for the default scheme; ignored (may
+ *             be NULL) with an atomic flag.  Its contents on entry do not
+ *             matter.  Two calls in flight at once must not share one
+ *             workspace.
  */
 GRKAN_API grkan_status_t grkan_backward(const void *x, const void *dy, const float *A, const float *B,
                               void *dx, float *dA, float *dB,
@@ -122,17 +126,17 @@ GRKAN_API size_t grkan_backward_workspace_size(int64_t rows, int64_t d, int32_t 
 /* Static English text for a status code (never NULL). */
 GRKAN_API const char *grkan_status_string(grkan_status_t status);
 
-/* Launch geometry the library uses on the current device for a pass
- * (pass 0 = forward, 1 = backward).  Queries the device (CU count and
- * occupancy) on first use. */
+/* Launch geometry of a pass (0 = forward, 1 = backward, 2 = backward with
+ * GRKAN_BLOCK_ATOMIC).  The geometry is a function of the shape and dtype;
+ * cus and blocks_per_cu describe the current device (queried on first use). */
 typedef struct {
-    int32_t block;          /* threads per workgroup                           */
-    int32_t rows_per_iter;  /* rows one workgroup covers per loop iteration    */
-    int32_t unroll;         /* loop iterations whose loads are issued together */
-    int32_t slices;         /* workgroups per group                            */
-    int64_t grid;           /* workgroups in the launch = slices * n_groups    */
-    int32_t cus;            /* compute units on the device                     */
-    int32_t blocks_per_cu;  /* resident workgroups per CU for this kernel      */
+    int32_t block;          /* threads per workgroup                                  */
+    int32_t rows_per_iter;  /* rows a workgroup's lanes cover in one pass             */
+    int32_t unroll;         /* passes per workgroup (loads issued together)           */
+    int64_t tiles;          /* row tiles (unroll * rows_per_iter rows each)           */
+    int64_t grid;           /* workgroups: one per (tile, group), padded to 8 tiles   */
+    int32_t cus;            /* compute units on the device                            */
+    int32_t blocks_per_cu;  /* resident workgroups per CU for this kernel             */
 } grkan_launch_t;
 
 GRKAN_API grkan_status_t grkan_query_launch(int64_t rows, int64_t d, int32_t n_groups,

@@ -13,7 +13,7 @@ LIB = os.path.join(ROOT, "gr_kan_rational_amd", "libgrkan.so")
 
 OK, INVALID, UNSUPPORTED, HIPERR = 0, 1, 2, 3
 F32, BF16 = 0, 1
-DET, NAIVE = 1, 2
+DEFAULT, BLOCK, NAIVE = 0, 1, 2
 
 
 @pytest.fixture(scope="module")
@@ -51,20 +51,22 @@ def test_status_strings(lib):
     assert lib.grkan_status_string(99)
 
 
-def ws(lib, rows, d, n_g, io=F32, flags=DET):
+def ws(lib, rows, d, n_g, io=F32, flags=DEFAULT):
     return lib.grkan_backward_workspace_size(rows, d, n_g, io, flags)
 
 
 def test_workspace_size(lib):
-    # KAT-B: 201728 rows / 8 rows per step = 25216 steps, 4 steps per iteration -> 6304 slices of
-    # work, capped at 8192 / 8 = 1024 slices per group; 10 fp64 partials each.
-    assert ws(lib, 201728, 768, 8) == 8 * 1024 * 10 * 8
-    assert ws(lib, 16, 32, 8) == 8 * 1 * 10 * 8          # tiny: 1 step, one slice per group
-    assert ws(lib, 201728, 768, 8, flags=0) == 0            # atomic mode needs none
+    # KAT-B backward: 96 channels x 4 B = 24 vectors per group row; 8 rows x 24 = 192 lanes per
+    # pass, 4 passes -> 32-row tiles; ceil(201728 / 32) = 6304 tiles; one fp32 partial per
+    # (group, coefficient, tile).
+    assert ws(lib, 201728, 768, 8) == 8 * 10 * 6304 * 4
+    assert ws(lib, 16, 32, 8) == 8 * 10 * 1 * 4             # tiny: a single tile
+    assert ws(lib, 201728, 3072, 8, io=BF16) == 8 * 10 * 25216 * 4  # 48 vectors: 4 rows x 2 passes
+    assert ws(lib, 201728, 768, 8, flags=BLOCK) == 0        # atomic modes need none
     assert ws(lib, 201728, 768, 8, flags=NAIVE) == 0
     assert ws(lib, 100, 770, 8) == 0                        # d % n_g != 0: rejected
     assert ws(lib, 100, 40, 8) == 0                         # 5 channels * 4 B: not 16-byte vectors
-    assert ws(lib, 0, 768, 8) == 8 * 1 * 10 * 8
+    assert ws(lib, 0, 768, 8) == 0                          # no rows, no tiles
 
 
 P = 0x10000  # fake, 16-byte aligned "device" addresses: validation never dereferences them
@@ -75,7 +77,7 @@ def fwd(lib, x=P, y=P + 0x100000, A=P + 0x200000, B=P + 0x300000, rows=4, d=64, 
 
 
 def bwd(lib, x=P, dy=P + 0x100000, A=P + 0x200000, B=P + 0x300000, dx=P + 0x400000,
-        dA=P + 0x500000, dB=P + 0x600000, rows=4, d=64, n_g=8, io=F32, flags=DET,
+        dA=P + 0x500000, dB=P + 0x600000, rows=4, d=64, n_g=8, io=F32, flags=DEFAULT,
         ws_ptr=P + 0x700000, ws_bytes=1 << 20):
     return lib.grkan_backward(x, dy, A, B, dx, dA, dB, rows, d, n_g, io, flags, ws_ptr, ws_bytes, None)
 
@@ -101,7 +103,7 @@ def test_forward_empty_is_ok_without_device(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dA=None), INVALID), (dict(dB=None), INVALID), (dict(dx=None), INVALID), (dict(dy=None), INVALID),
-    (dict(flags=4), INVALID), (dict(flags=DET | NAIVE), INVALID),
+    (dict(flags=4), INVALID), (dict(flags=BLOCK | NAIVE), INVALID),
     (dict(ws_ptr=None), INVALID), (dict(ws_bytes=100), INVALID),
     (dict(ws_ptr=P + 0x700008), UNSUPPORTED),
     (dict(dx=P + 16), INVALID),                      # dx partially overlaps x
@@ -122,4 +124,4 @@ def test_backward_atomic_mode_needs_no_workspace(lib):
 
     if torch.cuda.is_available():
         pytest.skip("only meaningful without a GPU")
-    assert bwd(lib, flags=0, ws_ptr=None, ws_bytes=0) == HIPERR
+    assert bwd(lib, flags=BLOCK, ws_ptr=None, ws_bytes=0) == HIPERR
