@@ -235,24 +235,4 @@ __device__ static inline float exact_fix(float x, float dy, const BwdCoefs &k, f
     return fmaf(-sv, e.Qd, e.wPd);
 }
 
-// ------------------------------------------------------ wave/block sums
-
-template <int CTRL, int ROW_MASK>
-__device__ static inline float dpp_f32(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                                  ROW_MASK, 0xF, false));
-}
-
-// Sum over the 64 lanes of a wave with DPP moves; the total ends in lane 63.
-// Fixed order (deterministic).  Requires all 64 lanes to exist.
-__device__ static inline float wave_sum_to_lane63(float v) {
-    v += dpp_f32<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]: pairs
-    v += dpp_f32<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]: quads
-    v += dpp_f32<0x141, 0xF>(v);  // row_half_mirror: groups of 8
-    v += dpp_f32<0x140, 0xF>(v);  // row_mirror: rows of 16
-    v += dpp_f32<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
-    v += dpp_f32<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
-    return v;
-}
-
 }  // namespace grkan
