@@ -90,7 +90,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="kat-b")
     ap.add_argument("--mode", choices=["deterministic", "block_atomic"], default="deterministic")
     ap.add_argument("--no-cpu-baseline", action="store_true")

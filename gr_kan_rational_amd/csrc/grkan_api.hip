@@ -84,8 +84,9 @@ grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, grkan_dtype
     return GRKAN_OK;
 }
 
+// fp32 partials [n_groups][10][8 * ceil(tiles / 8)] (one slot per tile, grouped by XCD).
 size_t partials_bytes(const Geometry &G) {
-    return (size_t)G.n_groups * kCoefs * (size_t)G.tiles * sizeof(float);
+    return (size_t)G.n_groups * kCoefs * (size_t)(8 * ((G.tiles + 7) / 8)) * sizeof(float);
 }
 
 // Per-device CU count and occupancy, for grkan_query_launch only.

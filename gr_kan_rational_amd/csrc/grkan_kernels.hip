@@ -76,6 +76,16 @@ __device__ static inline bool tile_of(const Geometry &G, int &g, int64_t &tile) 
     return tile < G.tiles;
 }
 
+// Where a tile's partial sums go.  Tiles run on XCD (tile mod 8); slot
+// (tile mod 8) * ceil(tiles / 8) + tile / 8 puts the tiles of one XCD next to
+// each other, so that XCD's L2 assembles whole lines of partials before
+// writing them back instead of sending scattered 4-byte writes.
+__host__ __device__ static inline int64_t partial_tiles8(const Geometry &G) { return (G.tiles + 7) / 8; }
+__host__ __device__ static inline int64_t partial_slots(const Geometry &G) { return 8 * partial_tiles8(G); }
+__device__ static inline int64_t partial_slot(const Geometry &G, int64_t tile) {
+    return (tile & 7) * partial_tiles8(G) + (tile >> 3);
+}
+
 // Lane placement inside a tile.
 struct Lane {
     int64_t off;     // vector offset of pass 0
@@ -244,7 +254,7 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
     }
     if (t < kNumCoef) {
         if (a.mode == kModePartials) {
-            a.partials[((int64_t)g * kNumCoef + t) * G.tiles + tile] = (float)total;
+            a.partials[((int64_t)g * kNumCoef + t) * partial_slots(G) + partial_slot(G, tile)] = (float)total;
         } else {
             float *dst = (t < kNumA) ? (a.dA + g * kNumA + t) : (a.dB + g * kNumB + (t - kNumA));
             unsafeAtomicAdd(dst, (float)total);
@@ -262,14 +272,16 @@ __global__ __launch_bounds__(kMergeThreads) void grkan_merge_kernel(const float 
                                                                     int64_t tiles, float *__restrict__ dA,
                                                                     float *__restrict__ dB) {
     const int gk = blockIdx.x;
-    const float *p = partials + (int64_t)gk * tiles;
+    const int64_t t8 = (tiles + 7) / 8, slots = 8 * t8;
+    const float *p = partials + (int64_t)gk * slots;
     double s = 0.0;
-    for (int64_t base = 0; base < tiles; base += (int64_t)kMergeThreads * kMergeLoads) {
+    for (int64_t base = 0; base < slots; base += (int64_t)kMergeThreads * kMergeLoads) {
         float v[kMergeLoads];
 #pragma unroll
         for (int i = 0; i < kMergeLoads; ++i) {
-            const int64_t t = base + (int64_t)i * kMergeThreads + threadIdx.x;
-            v[i] = (t < tiles) ? p[t] : 0.0f;
+            const int64_t q = base + (int64_t)i * kMergeThreads + threadIdx.x;
+            const int64_t tile = (q % t8) * 8 + q / t8;  // slot -> tile; padding slots hold nothing
+            v[i] = (q < slots && tile < tiles) ? p[q] : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < kMergeLoads; ++i) s += (double)v[i];

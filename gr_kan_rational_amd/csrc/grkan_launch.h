@@ -45,7 +45,7 @@ struct BwdArgs {
     const float *B;
     float *dA;
     float *dB;
-    float *partials;  // [n_groups][10][tiles] in kModePartials
+    float *partials;  // [n_groups][10][8 * ceil(tiles / 8)] in kModePartials
     int32_t mode;
     Geometry geo;
 };

@@ -58,10 +58,12 @@ def ws(lib, rows, d, n_g, io=F32, flags=DEFAULT):
 def test_workspace_size(lib):
     # KAT-B backward: 96 channels x 4 B = 24 vectors per group row; 8 rows x 24 = 192 lanes per
     # pass, 4 passes -> 32-row tiles; ceil(201728 / 32) = 6304 tiles; one fp32 partial per
-    # (group, coefficient, tile).
+    # (group, coefficient, tile), slots rounded up to a multiple of 8 tiles.
     assert ws(lib, 201728, 768, 8) == 8 * 10 * 6304 * 4
-    assert ws(lib, 16, 32, 8) == 8 * 10 * 1 * 4             # tiny: a single tile
+    assert ws(lib, 16, 32, 8) == 8 * 10 * 8 * 4             # tiny: a single tile, 8 slots
     assert ws(lib, 201728, 3072, 8, io=BF16) == 8 * 10 * 25216 * 4  # 48 vectors: 4 rows x 2 passes
+    assert ws(lib, 1000, 768, 8) == 8 * 10 * 32 * 4         # 32 tiles of 32 rows (the last ragged)
+    assert ws(lib, 1025, 768, 8) == 8 * 10 * 40 * 4         # 33 tiles -> 40 slots
     assert ws(lib, 201728, 768, 8, flags=BLOCK) == 0        # atomic modes need none
     assert ws(lib, 201728, 768, 8, flags=NAIVE) == 0
     assert ws(lib, 100, 770, 8) == 0                        # d % n_g != 0: rejected
