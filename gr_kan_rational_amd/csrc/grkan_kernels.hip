@@ -44,8 +44,9 @@ constexpr int kMaxBlock = 1024;
 // Tuning per (I/O type, pass): U = passes per workgroup (all of a lane's
 // loads are issued together), block = target workgroup size.  Chosen by
 // measurement on MI355X at the KAT-B shapes: the backward prefers small
-// blocks (its ~110 VGPRs allow 4 waves per SIMD; 3-wave blocks fill that
-// better than 6-wave ones) and 4 passes to amortise the block reduction.
+// blocks (with ~90 VGPRs a SIMD holds 5 of its waves; 3-wave blocks fill
+// those slots in finer steps than 6-wave ones) and 4 passes to amortise the
+// block reduction.
 template <class IO, int pass> struct Tune;
 template <> struct Tune<float, 0> { static constexpr int U = 2, block = 384; };
 template <> struct Tune<bf16io, 0> { static constexpr int U = 2, block = 384; };
@@ -354,7 +355,8 @@ hipError_t occupancy(grkan_dtype_t io, int pass, int block, int *blocks_per_cu) 
     else
         fn = pass ? (const void *)grkan_bwd_kernel<float, Tune<float, 1>::U>
                   : (const void *)grkan_fwd_kernel<float, Tune<float, 0>::U>;
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, block, 0);
+    const size_t lds = pass ? (size_t)kNumCoef * block * sizeof(float) : 0;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, block, lds);
 }
 
 }  // namespace grkan
