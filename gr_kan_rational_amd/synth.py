@@ -18,6 +18,14 @@ generators stand in for them with i.i.d. normal data of the same shapes:
 with n_g = 8 groups, coefficients A [8, 6] and B [8, 4] ~ N(0, 0.5) and
 X ~ N(0, 1) everywhere; N(0, s) means standard deviation s.
 
+The PAU family (other numerator / denominator degrees m, n and group counts)
+uses the same recipe with A [n_g, m+1] and B [n_g, n]:
+
+    kat-b-pau       [1024, 197, 768]  fp32  n_g = 1,   (m, n) = (5, 4)  seed 6
+    kat-b-r32       [1024, 197, 768]  fp32  n_g = 8,   (m, n) = (3, 2)  seed 7
+    kat-b-r76       [1024, 197, 768]  fp32  n_g = 8,   (m, n) = (7, 6)  seed 8
+    kat-b-poly5     [1024, 197, 768]  fp32  n_g = 8,   (m, n) = (5, 0)  seed 9
+
 Recipe (reproducible, independent of the number of threads):
   * A then B from ``numpy.random.default_rng(seed)`` as float32 standard
     normals, multiplied by the std in float32;
@@ -38,7 +46,6 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 CHUNK = 1 << 22
-N_NUM, N_DEN = 6, 4
 
 
 @dataclass(frozen=True)
@@ -54,6 +61,8 @@ class Workload:
     dy_std: float
     seed: int
     identity_group0: bool = False
+    m: int = 5         # numerator degree (a_0..a_m)
+    n: int = 4         # denominator degree (b_1..b_n)
 
     @property
     def rows(self) -> int:
@@ -84,8 +93,22 @@ WORKLOADS = {
         Workload("kat-s-hid", 1024, 197, 1536, 8, "f32", 0.5, 1.0, 1e-2, 3, True),
         Workload("kat-b", 1024, 197, 768, 8, "f32", 0.5, 1.0, 1e-2, 4),
         Workload("kat-b-hid-bf16", 1024, 197, 3072, 8, "bf16", 0.5, 1.0, 1e-2, 5),
+        Workload("kat-b-pau", 1024, 197, 768, 1, "f32", 0.5, 1.0, 1e-2, 6),
+        Workload("kat-b-r32", 1024, 197, 768, 8, "f32", 0.5, 1.0, 1e-2, 7, m=3, n=2),
+        Workload("kat-b-r76", 1024, 197, 768, 8, "f32", 0.5, 1.0, 1e-2, 8, m=7, n=6),
+        Workload("kat-b-poly5", 1024, 197, 768, 8, "f32", 0.5, 1.0, 1e-2, 9, m=5, n=0),
     )
 }
+
+# The GR-KAN workloads (degrees (5, 4), 8 groups) and the PAU-family ones.
+GRKAN_WORKLOADS = ("tiny", "kat-t", "kat-s-hid", "kat-b", "kat-b-hid-bf16")
+PAU_WORKLOADS = ("kat-b-pau", "kat-b-r32", "kat-b-r76", "kat-b-poly5")
+
+
+def custom(name: str, rows: int, d: int, n_groups: int, m: int = 5, n: int = 4, io: str = "f32",
+           seed: int = 100, coef_std: float = 0.5, dy_std: float = 1e-2) -> Workload:
+    """A workload of the same recipe with any shape, group count and degrees."""
+    return Workload(name, rows, 1, d, n_groups, io, coef_std, 1.0, dy_std, seed, m=m, n=n)
 
 
 def _threads() -> int:
@@ -111,10 +134,11 @@ def bf16_to_f32(h: np.ndarray) -> np.ndarray:
 def coefficients(w: Workload) -> tuple[np.ndarray, np.ndarray]:
     rng = np.random.default_rng(w.seed)
     std = np.float32(w.coef_std)
-    A = rng.standard_normal((w.n_groups, N_NUM), dtype=np.float32) * std
-    B = rng.standard_normal((w.n_groups, N_DEN), dtype=np.float32) * std
+    A = rng.standard_normal((w.n_groups, w.m + 1), dtype=np.float32) * std
+    B = rng.standard_normal((w.n_groups, w.n), dtype=np.float32) * std
     if w.identity_group0:
-        A[0] = np.array([0, 1, 0, 0, 0, 0], dtype=np.float32)
+        A[0] = 0
+        A[0, 1] = 1
     return A.astype(np.float32), B.astype(np.float32)
 
 

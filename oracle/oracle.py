@@ -33,10 +33,23 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "grkan_oracle.c")
 _LIB = os.path.join(_HERE, "libgrkan_oracle.so")
 
-NA, NB = 6, 4           # numerator a_0..a_5, denominator b_1..b_4
+M, N = 5, 4             # GR-KAN's degrees: numerator a_0..a_5, denominator b_1..b_4
+NA, NB = M + 1, N
 NK = NA + NB
-# record layout of grkan_oracle_point (kept in step with the C enum)
-F, DX, TA, TB, FMAG, DXMAG, SIGN, DEN, NOUT = 0, 1, 2, 8, 12, 13, 14, 15, 16
+# record layout of grkan_oracle_point (kept in step with the C enum): six
+# scalars, then the m+1 numerator terms and the n denominator terms, then the
+# first-order rounding scale of each of those terms in the same order
+F, DX, FMAG, DXMAG, SIGN, DEN, T = 0, 1, 2, 3, 4, 5, 6
+
+
+def layout(m: int = M, n: int = N):
+    """(first numerator term, first denominator term, record length) for degrees (m, n);
+    the rounding scale of the term at column c sits at column c + m + 1 + n."""
+    return T, T + m + 1, T + 2 * (m + 1 + n)
+
+
+TA, TB, NOUT = layout()
+MAXDEG = 15
 
 _CHUNK_ELEMS = 1 << 16
 
@@ -64,16 +77,18 @@ def _lib():
         lib = ctypes.CDLL(_LIB)
         dp = ctypes.POINTER(ctypes.c_double)
         lp = ctypes.POINTER(ctypes.c_long)
-        lib.grkan_oracle_point.argtypes = [ctypes.c_double, ctypes.c_double, dp, dp, dp]
+        ci = ctypes.c_int
+        lib.grkan_oracle_point.argtypes = [ctypes.c_double, ctypes.c_double, ci, ci, dp, dp, dp]
         lib.grkan_oracle_point.restype = None
-        lib.grkan_oracle_rows.argtypes = [dp, dp, ctypes.c_long, ctypes.c_long, ctypes.c_int,
-                                          dp, dp, dp, dp, dp, dp, dp, dp]
-        lib.grkan_oracle_rows.restype = ctypes.c_int
+        lib.grkan_oracle_rows.argtypes = [dp, dp, ctypes.c_long, ctypes.c_long, ci, ci, ci,
+                                          dp, dp, dp, dp, dp, dp, dp, dp, dp]
+        lib.grkan_oracle_rows.restype = ci
         lib.grkan_oracle_points.argtypes = [dp, dp, lp, ctypes.c_long, ctypes.c_long,
-                                            ctypes.c_int, dp, dp, dp]
-        lib.grkan_oracle_points.restype = ctypes.c_int
-        lib.grkan_oracle_nout.restype = ctypes.c_int
-        if lib.grkan_oracle_nout() != NOUT:
+                                            ci, ci, ci, dp, dp, dp]
+        lib.grkan_oracle_points.restype = ci
+        lib.grkan_oracle_nout.argtypes = [ci, ci]
+        lib.grkan_oracle_nout.restype = ci
+        if any(lib.grkan_oracle_nout(m, n) != layout(m, n)[2] for m, n in ((5, 4), (0, 0), (7, 3))):
             raise RuntimeError("oracle library record layout does not match oracle.py")
         _lib_handle = lib
     return _lib_handle
@@ -129,36 +144,46 @@ def _load_f64(dst: np.ndarray, src: np.ndarray, io: str, local) -> np.ndarray:
     return dst
 
 
-def _coef(A, B, n_groups):
-    A = np.ascontiguousarray(np.asarray(A, dtype=np.float64).reshape(n_groups, NA))
-    B = np.ascontiguousarray(np.asarray(B, dtype=np.float64).reshape(n_groups, NB))
+def _degrees(m, n):
+    if not (0 <= m <= MAXDEG and 0 <= n <= MAXDEG):
+        raise ValueError(f"degrees (m, n) = ({m}, {n}) outside 0..{MAXDEG}")
+
+
+def _coef(A, B, n_groups, m=M, n=N):
+    _degrees(m, n)
+    A = np.ascontiguousarray(np.asarray(A, dtype=np.float64).reshape(n_groups, m + 1))
+    B = np.ascontiguousarray(np.asarray(B, dtype=np.float64).reshape(n_groups, n))
+    if n == 0:  # keep a valid pointer for an empty denominator
+        B = np.zeros((n_groups, 1), dtype=np.float64)
     return A, B
 
 
-def point(x: float, dy: float, a, b) -> np.ndarray:
-    """One element: the NOUT-record of grkan_oracle_point (a: 6 values, b: 4)."""
-    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64).reshape(NA))
-    b = np.ascontiguousarray(np.asarray(b, dtype=np.float64).reshape(NB))
-    out = np.zeros(NOUT, dtype=np.float64)
-    _lib().grkan_oracle_point(float(x), float(dy), _ptr(a), _ptr(b), _ptr(out))
+def point(x: float, dy: float, a, b, m: int = M, n: int = N) -> np.ndarray:
+    """One element: the record of grkan_oracle_point (a: m+1 values, b: n values)."""
+    A, B = _coef(a, b, 1, m, n)
+    out = np.zeros(layout(m, n)[2], dtype=np.float64)
+    _lib().grkan_oracle_point(float(x), float(dy), m, n, _ptr(A), _ptr(B), _ptr(out))
     return out
 
 
 def run(x, A, B, n_groups: int, dy=None, io: str = "f32", elements: bool = True,
-        nthreads: int | None = None) -> dict:
+        nthreads: int | None = None, m: int = M, n: int = N) -> dict:
     """Forward (and backward when ``dy`` is given) over a whole [..., d] tensor.
 
-    Returns a dict with fp64 arrays shaped like ``x`` for ``y``, ``ymag`` and,
-    with ``dy``, ``dx``, ``dxmag`` (only when ``elements``), and always, with
-    ``dy``, ``dA`` [n_g, 6], ``dB`` [n_g, 4] and the L2 norms of their terms
-    ``nA``, ``nB`` (same shapes).
+    Degrees (m, n): A is [n_g, m+1], B is [n_g, n].  Returns a dict with fp64
+    arrays shaped like ``x`` for ``y``, ``ymag`` and, with ``dy``, ``dx``,
+    ``dxmag`` (only when ``elements``), and always, with ``dy``, ``dA``
+    [n_g, m+1], ``dB`` [n_g, n], the L2 norms of their terms ``nA``, ``nB``
+    and the L2 norms of their terms' rounding scales ``mA``, ``mB`` (same
+    shapes).
     """
+    nk = m + 1 + n
     shape = x.shape
     d = shape[-1]
     rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
     x2 = x.reshape(rows, d)
     dy2 = None if dy is None else dy.reshape(rows, d)
-    A64, B64 = _coef(A, B, n_groups)
+    A64, B64 = _coef(A, B, n_groups, m, n)
     lib = _lib()
     res = {}
     if elements:
@@ -170,8 +195,9 @@ def run(x, A, B, n_groups: int, dy=None, io: str = "f32", elements: bool = True,
     step = max(1, _CHUNK_ELEMS // d)
     starts = list(range(0, rows, step))
     nchunk = len(starts)
-    sums = np.zeros((nchunk, n_groups * NK), dtype=np.float64)
-    sumsq = np.zeros((nchunk, n_groups * NK), dtype=np.float64)
+    sums = np.zeros((nchunk, n_groups * nk), dtype=np.float64)
+    sumsq = np.zeros((nchunk, n_groups * nk), dtype=np.float64)
+    magsq = np.zeros((nchunk, n_groups * nk), dtype=np.float64)
 
     local = threading.local()
 
@@ -185,18 +211,19 @@ def run(x, A, B, n_groups: int, dy=None, io: str = "f32", elements: bool = True,
     def work(ci):
         r0 = starts[ci]
         r1 = min(rows, r0 + step)
-        n = (r1 - r0) * d
-        xc = _load_f64(scratch("x", n), x2[r0:r1].reshape(-1), io, local)
+        ne = (r1 - r0) * d
+        xc = _load_f64(scratch("x", ne), x2[r0:r1].reshape(-1), io, local)
         dyc = None
         if dy2 is not None:
-            dyc = _load_f64(scratch("dy", n), dy2[r0:r1].reshape(-1), io, local)
+            dyc = _load_f64(scratch("dy", ne), dy2[r0:r1].reshape(-1), io, local)
         outs = {k: res[k][r0:r1] for k in res}  # row slices of C-contiguous arrays
         sp = _ptr(sums[ci]) if dy is not None else None
         sq = _ptr(sumsq[ci]) if dy is not None else None
-        rc = lib.grkan_oracle_rows(_ptr(xc), _ptr(dyc), r1 - r0, d, n_groups,
+        mq = _ptr(magsq[ci]) if dy is not None else None
+        rc = lib.grkan_oracle_rows(_ptr(xc), _ptr(dyc), r1 - r0, d, n_groups, m, n,
                                    _ptr(A64), _ptr(B64), _ptr(outs.get("y")),
                                    _ptr(outs.get("ymag")), _ptr(outs.get("dx")),
-                                   _ptr(outs.get("dxmag")), sp, sq)
+                                   _ptr(outs.get("dxmag")), sp, sq, mq)
         if rc != 0:
             raise ValueError("oracle rejected the shape")
 
@@ -211,25 +238,30 @@ def run(x, A, B, n_groups: int, dy=None, io: str = "f32", elements: bool = True,
     for k in list(res):
         res[k] = res[k].reshape(shape)
     if dy is not None:
-        tot = np.array([math.fsum(sums[:, k]) for k in range(n_groups * NK)]).reshape(n_groups, NK)
-        tot2 = np.array([math.fsum(sumsq[:, k]) for k in range(n_groups * NK)]).reshape(n_groups, NK)
+        tot = np.array([math.fsum(sums[:, k]) for k in range(n_groups * nk)]).reshape(n_groups, nk)
+        tot2 = np.array([math.fsum(sumsq[:, k]) for k in range(n_groups * nk)]).reshape(n_groups, nk)
+        tot3 = np.array([math.fsum(magsq[:, k]) for k in range(n_groups * nk)]).reshape(n_groups, nk)
         nrm = np.sqrt(tot2)
-        res["dA"], res["dB"] = tot[:, :NA].copy(), tot[:, NA:].copy()
-        res["nA"], res["nB"] = nrm[:, :NA].copy(), nrm[:, NA:].copy()
+        mag = np.sqrt(tot3)
+        res["dA"], res["dB"] = tot[:, :m + 1].copy(), tot[:, m + 1:].copy()
+        res["nA"], res["nB"] = nrm[:, :m + 1].copy(), nrm[:, m + 1:].copy()
+        res["mA"], res["mB"] = mag[:, :m + 1].copy(), mag[:, m + 1:].copy()
     return res
 
 
-def points(x, A, B, n_groups: int, flat_idx, dy=None, io: str = "f32") -> np.ndarray:
-    """Records [n, NOUT] for the elements at flat indices ``flat_idx`` of ``x``."""
+def points(x, A, B, n_groups: int, flat_idx, dy=None, io: str = "f32", m: int = M,
+           n: int = N) -> np.ndarray:
+    """Records [n_el, layout(m, n)[2]] for the elements at flat indices ``flat_idx`` of ``x``."""
     d = x.shape[-1]
     flat_idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
     xv = np.ascontiguousarray(to_f64(x.reshape(-1)[flat_idx], io))
     dyv = None if dy is None else np.ascontiguousarray(to_f64(dy.reshape(-1)[flat_idx], io))
-    A64, B64 = _coef(A, B, n_groups)
-    out = np.empty((flat_idx.size, NOUT), dtype=np.float64)
+    A64, B64 = _coef(A, B, n_groups, m, n)
+    out = np.empty((flat_idx.size, layout(m, n)[2]), dtype=np.float64)
     rc = _lib().grkan_oracle_points(_ptr(xv), _ptr(dyv),
                                     flat_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
-                                    flat_idx.size, d, n_groups, _ptr(A64), _ptr(B64), _ptr(out))
+                                    flat_idx.size, d, n_groups, m, n, _ptr(A64), _ptr(B64),
+                                    _ptr(out))
     if rc != 0:
         raise ValueError("oracle rejected the shape")
     return out

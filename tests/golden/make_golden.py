@@ -1,8 +1,8 @@
 """Write the fp64 oracle's group sums for each full-size workload.
 
 Output: tests/golden/<workload>.sums.json with dA, dB (the oracle's group sums
-over the whole workload) and nA, nB (L2 norms of the summed terms), as exact
-float reprs.  Calls only the oracle and the seeded input generator; the GPU
+over the whole workload), nA, nB (L2 norms of the summed terms) and mA, mB
+(L2 norms of the terms' rounding scales), as exact float reprs.  Calls only the oracle and the seeded input generator; the GPU
 parity tests check that a fresh oracle run reproduces these files, and the
 benchmark reads them to report the rounding error of the GPU reductions.
 
@@ -29,11 +29,13 @@ def make(name: str) -> dict:
     w = synth.WORKLOADS[name]
     t0 = time.time()
     inp = synth.make_inputs(w)
-    r = oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io, elements=False)
+    r = oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io, elements=False,
+                   m=w.m, n=w.n)
     out = {
         "workload": name,
         "shape": [w.batch, w.seq, w.d],
         "n_groups": w.n_groups,
+        "degrees": [w.m, w.n],
         "io": w.io,
         "seed": w.seed,
         "source": "oracle/grkan_oracle.c via oracle.oracle.run (fp64 terms, long double row sums, "
@@ -42,6 +44,8 @@ def make(name: str) -> dict:
         "dB": [[float(v) for v in row] for row in r["dB"]],
         "nA": [[float(v) for v in row] for row in r["nA"]],
         "nB": [[float(v) for v in row] for row in r["nB"]],
+        "mA": [[float(v) for v in row] for row in r["mA"]],
+        "mB": [[float(v) for v in row] for row in r["mB"]],
     }
     with open(path_for(name), "w") as f:
         json.dump(out, f, indent=1)
