@@ -73,12 +73,12 @@ def cpu_baseline(w, target_s: float = 10.0) -> dict:
     calib_rows = 256
     inp = synth.make_inputs(w, rows=calib_rows)
     t0 = time.perf_counter()
-    oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io)
+    oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io, m=w.m, n=w.n)
     dt = time.perf_counter() - t0
     rows = int(min(w.rows, max(calib_rows, calib_rows * target_s / max(dt, 1e-3))))
     inp = synth.make_inputs(w, rows=rows)
     t0 = time.perf_counter()
-    oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io)
+    oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io, m=w.m, n=w.n)
     dt = time.perf_counter() - t0
     n = rows * w.d
     return {"value": n / dt, "unit": "elements/s", "cores": oracle.threads(), "kind": "oracle",
@@ -140,22 +140,40 @@ def main() -> int:
 
     x, dy = to_dev(inp["x"]), to_dev(inp["dy"])
     A = torch.from_numpy(inp["A"]).to(dev)
-    B = torch.from_numpy(inp["B"]).to(dev)
+    B = torch.from_numpy(inp["B"]).to(dev) if w.n > 0 else None
     del inp
     y = torch.empty_like(x)
     dx = torch.empty_like(x)
-    dA = torch.empty((w.n_groups, 6), dtype=torch.float32, device=dev)
-    dB = torch.empty((w.n_groups, 4), dtype=torch.float32, device=dev)
-    ws_bytes = gk.grkan_backward_workspace_size(w.rows, w.d, w.n_groups, io, 0)
+    dA = torch.empty((w.n_groups, w.m + 1), dtype=torch.float32, device=dev)
+    dB = torch.empty((w.n_groups, w.n), dtype=torch.float32, device=dev) if w.n > 0 else None
+    # GR-KAN itself (degrees (5, 4)) goes through the grkan_* entry points, the other
+    # members of the PAU family through grkan_pau_*.
+    pau = (w.m, w.n) != (5, 4)
+    if pau:
+        ws_bytes = gk.grkan_pau_backward_workspace_size(w.rows, w.d, w.n_groups, w.m, w.n, io, 0)
+    else:
+        ws_bytes = gk.grkan_backward_workspace_size(w.rows, w.d, w.n_groups, io, 0)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def fwd():
-        gk.grkan_forward(x, A, B, w.n_groups, out=y, stream=stream)
+        if pau:
+            gk.grkan_pau_forward(x, A, B, w.n_groups, w.m, w.n, out=y, stream=stream)
+        else:
+            gk.grkan_forward(x, A, B, w.n_groups, out=y, stream=stream)
 
     def bwd(mode=args.mode):
-        gk.grkan_backward(x, dy, A, B, w.n_groups, mode=mode,
-                          dx=dx, dA=dA, dB=dB, workspace=ws, stream=stream)
+        if pau:
+            gk.grkan_pau_backward(x, dy, A, B, w.n_groups, w.m, w.n, mode=mode,
+                                  dx=dx, dA=dA, dB=dB, workspace=ws, stream=stream)
+        else:
+            gk.grkan_backward(x, dy, A, B, w.n_groups, mode=mode,
+                              dx=dx, dA=dA, dB=dB, workspace=ws, stream=stream)
+
+    def launch(pass_):
+        if pau:
+            return gk.grkan_pau_query_launch(w.rows, w.d, w.n_groups, w.m, w.n, io, pass_)
+        return gk.grkan_query_launch(w.rows, w.d, w.n_groups, io, pass_)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -210,8 +228,8 @@ def main() -> int:
         "fwdbwd_GBps": (fwd_bytes + bwd_bytes) / (ms_per_step * 1e-3) / 1e9,
         "two_reads_one_write_ceiling_GBps": (bwd_bytes / (ceil_ms * 1e-3) / 1e9) if ceil_ms else None,
         "bwd_frac_of_that_ceiling": (ceil_ms / bwd_ms) if ceil_ms else None,
-        "launch_fwd": gk.grkan_query_launch(w.rows, w.d, w.n_groups, io, 0),
-        "launch_bwd": gk.grkan_query_launch(w.rows, w.d, w.n_groups, io, 1),
+        "launch_fwd": launch(0),
+        "launch_bwd": launch(1),
         "device": torch.cuda.get_device_name(dev),
     }
 
@@ -234,25 +252,33 @@ def main() -> int:
             g = json.load(f)
         ref = (np.array(g["dA"]), np.array(g["dB"]))
     errors = {}
+
+    def grad_errors():
+        e = {"dA": error_stats(dA.cpu().numpy(), ref[0])}
+        if dB is not None:
+            e["dB"] = error_stats(dB.cpu().numpy(), ref[1])
+        return e
+
     other = "block_atomic" if args.mode == "deterministic" else "deterministic"
     detail[f"bwd_{other}_ms"] = time_one(lambda: bwd(other), 10)
     for mode in ("deterministic", "block_atomic"):
         bwd(mode)
         torch.cuda.synchronize()
         if ref is not None:
-            errors[mode] = {"dA": error_stats(dA.cpu().numpy(), ref[0]), "dB": error_stats(dB.cpu().numpy(), ref[1])}
-    if not args.no_naive:
+            errors[mode] = grad_errors()
+    if not args.no_naive and not pau:
         log("naive per-element-atomic backward (one run)")
         detail["bwd_naive_ms"] = time_one(lambda: bwd("naive"), 1)
         if ref is not None:
-            errors["naive_per_element_atomic"] = {"dA": error_stats(dA.cpu().numpy(), ref[0]),
-                                                  "dB": error_stats(dB.cpu().numpy(), ref[1])}
+            errors["naive_per_element_atomic"] = grad_errors()
     if errors:
         detail["grad_error_vs_fp64_oracle"] = errors
 
     traffic = traffic_from_profiles(w.name, bwd_bytes)
     out = {
-        "metric": "GR-KAN fwd+bwd elements/s and achieved HBM GB/s (% peak) at KAT-B shape",
+        "metric": ("GR-KAN fwd+bwd elements/s and achieved HBM GB/s (% peak) at KAT-B shape"
+                   if w.name == "kat-b" else
+                   f"GR-KAN/PAU fwd+bwd elements/s and achieved HBM GB/s (% peak), workload {w.name}"),
         "value": value,
         "unit": "elements/s",
         "n_gpus": 1,
@@ -265,10 +291,11 @@ def main() -> int:
         "dtype": "f32" if w.io == "f32" else "f32 (bf16 I/O)",
         "data": "synthetic",
         "config": {"workload": w.name, "shape": [w.batch, w.seq, w.d], "n_groups": w.n_groups,
-                   "io": w.io, "backward_mode": args.mode},
+                   "degrees": [w.m, w.n], "io": w.io, "backward_mode": args.mode},
         "roofline": {"bound": "hbm", "achieved": bwd_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": bwd_gbps / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "grkan_backward (main kernel + fixed-order merge)",
+                     "kernel": ("grkan_pau_backward" if pau else "grkan_backward")
+                               + " (main kernel + fixed-order merge)",
                      "algorithmic_bytes_per_launch": bwd_bytes},
         "detail": detail,
     }

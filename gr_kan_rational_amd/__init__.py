@@ -13,6 +13,11 @@ __all__ = [
     "GRKANFunction",
     "GRKANError",
     "grkan_query_launch",
+    "grkan_pau_forward",
+    "grkan_pau_backward",
+    "grkan_pau_backward_workspace_size",
+    "grkan_pau_query_launch",
+    "grkan_pau_supported",
     "load_library",
 ]
 

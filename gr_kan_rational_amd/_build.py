@@ -2,12 +2,14 @@
 
 Every translation unit is compiled for gfx950 only, with packed-FP32
 instruction selection disabled, then linked into ``libgrkan.so`` next to this
-file.  The baseline kernel's translation unit is compiled with the compiler's
+file.  The kernel source is compiled once per (numerator, denominator) degree
+pair listed in ``GRKAN_FOR_EACH_DEGREE`` (csrc/grkan_launch.h).  The baseline kernel's translation unit is compiled with the compiler's
 atomic optimizer off so that each lane's atomic stays a hardware atomic.
 """
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 from concurrent.futures import ThreadPoolExecutor
@@ -25,11 +27,26 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
 ]
-UNITS = {
-    "grkan_api.hip": [],
-    "grkan_kernels.hip": [],
-    "grkan_naive.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
-}
+LAUNCH_H = os.path.join(CSRC, "grkan_launch.h")
+
+
+def degree_pairs() -> list[tuple[int, int]]:
+    """The (m, n) pairs listed in GRKAN_FOR_EACH_DEGREE in grkan_launch.h."""
+    text = open(LAUNCH_H).read()
+    m = re.search(r"#define GRKAN_FOR_EACH_DEGREE\(X\)((?:\s*X\(\d+, \d+\))+)", text)
+    if not m:
+        raise RuntimeError("GRKAN_FOR_EACH_DEGREE not found in grkan_launch.h")
+    return [(int(a), int(b)) for a, b in re.findall(r"X\((\d+), (\d+)\)", m.group(1))]
+
+
+def units() -> list[tuple[str, list[str], str]]:
+    """(source, extra flags, object name) of every translation unit."""
+    out = [("grkan_api.hip", [], "grkan_api.o"),
+           ("grkan_merge.hip", [], "grkan_merge.o"),
+           ("grkan_naive.hip", ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"], "grkan_naive.o")]
+    for m, n in degree_pairs():
+        out.append(("grkan_kernels.hip", [f"-DGRKAN_M={m}", f"-DGRKAN_N={n}"], f"grkan_kernels_{m}_{n}.o"))
+    return out
 
 
 def hipcc() -> str:
@@ -44,18 +61,19 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
 
     def compile_unit(item):
-        name, extra = item
-        out = os.path.join(OBJ, name.replace(".hip", ".o"))
+        name, extra, obj = item
+        out = os.path.join(OBJ, obj)
         cmd = [cc, *COMMON, *extra, "-c", os.path.join(CSRC, name), "-o", out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {name}:\n{r.stderr}")
+            raise RuntimeError(f"hipcc failed on {name} {' '.join(extra)}:\n{r.stderr}")
         if verbose and r.stderr.strip():
             print(r.stderr)
         return out
 
-    with ThreadPoolExecutor(len(UNITS)) as ex:
-        objs = list(ex.map(compile_unit, UNITS.items()))
+    todo = units()
+    with ThreadPoolExecutor(min(len(todo), max(1, os.cpu_count() or 1), 16)) as ex:
+        objs = list(ex.map(compile_unit, todo))
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

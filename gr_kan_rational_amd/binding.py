@@ -37,6 +37,8 @@ class grkan_launch_t(ctypes.Structure):
         ("grid", ctypes.c_int64),
         ("cus", ctypes.c_int32),
         ("blocks_per_cu", ctypes.c_int32),
+        ("parts", ctypes.c_int32),
+        ("part_vecs", ctypes.c_int32),
     ]
 
 
@@ -62,6 +64,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grkan_status_string.restype = ctypes.c_char_p
     lib.grkan_query_launch.argtypes = [i64, i64, i32, ctypes.c_int, i32, ctypes.POINTER(grkan_launch_t)]
     lib.grkan_query_launch.restype = ctypes.c_int
+    lib.grkan_pau_supported.argtypes = [i32, i32]
+    lib.grkan_pau_supported.restype = ctypes.c_int
+    lib.grkan_pau_forward.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int, vp]
+    lib.grkan_pau_forward.restype = ctypes.c_int
+    lib.grkan_pau_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ctypes.c_int,
+                                       u32, vp, sz, vp]
+    lib.grkan_pau_backward.restype = ctypes.c_int
+    lib.grkan_pau_backward_workspace_size.argtypes = [i64, i64, i32, i32, i32, ctypes.c_int, u32]
+    lib.grkan_pau_backward_workspace_size.restype = sz
+    lib.grkan_pau_query_launch.argtypes = [i64, i64, i32, i32, i32, ctypes.c_int, i32,
+                                           ctypes.POINTER(grkan_launch_t)]
+    lib.grkan_pau_query_launch.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -88,8 +102,13 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _check_coefs(A: torch.Tensor, B: torch.Tensor, n_groups: int, dev) -> None:
-    for name, t, k in (("A", A, 6), ("B", B, 4)):
+GRKAN_M, GRKAN_N = 5, 4  # GR-KAN's numerator / denominator degrees
+
+
+def _check_coefs(A: torch.Tensor, B, n_groups: int, dev, m: int = GRKAN_M, n: int = GRKAN_N) -> None:
+    for name, t, k in (("A", A, m + 1), ("B", B, n)):
+        if k == 0 and t is None:
+            continue
         if t.dtype != torch.float32 or t.device != dev or not t.is_contiguous() or t.numel() != n_groups * k:
             raise ValueError(f"{name} must be a contiguous float32 [{n_groups}, {k}] tensor on {dev}")
 
@@ -101,25 +120,83 @@ def _rows_d(x: torch.Tensor):
     return (x.numel() // d if d else 0), d
 
 
-def grkan_forward(x: torch.Tensor, A: torch.Tensor, B: torch.Tensor, n_groups: int = 8,
-                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """y = F(x), the group-rational activation, computed by ``grkan_forward``."""
+def _forward(x, A, B, n_groups, m, n, out, stream, pau):
     lib = load_library()
     io = _io(x)
-    _check_coefs(A, B, n_groups, x.device)
+    _check_coefs(A, B, n_groups, x.device, m, n)
     rows, d = _rows_d(x)
     y = torch.empty_like(x) if out is None else out
     if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
         raise ValueError("out must match x")
-    st = lib.grkan_forward(_ptr(x), _ptr(y), _ptr(A), _ptr(B), rows, d, n_groups, io, ctypes.c_void_p(_stream(stream)))
+    s = ctypes.c_void_p(_stream(stream))
+    if pau:
+        st = lib.grkan_pau_forward(_ptr(x), _ptr(y), _ptr(A), _ptr(B), rows, d, n_groups, m, n, io, s)
+    else:
+        st = lib.grkan_forward(_ptr(x), _ptr(y), _ptr(A), _ptr(B), rows, d, n_groups, io, s)
     if st != GRKAN_OK:
-        raise GRKANError(st, "grkan_forward")
+        raise GRKANError(st, "grkan_pau_forward" if pau else "grkan_forward")
     return y
+
+
+def grkan_forward(x: torch.Tensor, A: torch.Tensor, B: torch.Tensor, n_groups: int = 8,
+                  out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = F(x), the group-rational activation, computed by ``grkan_forward``."""
+    return _forward(x, A, B, n_groups, GRKAN_M, GRKAN_N, out, stream, pau=False)
+
+
+def grkan_pau_forward(x: torch.Tensor, A: torch.Tensor, B, n_groups: int, m: int, n: int,
+                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = F(x) for numerator degree m and denominator degree n (``grkan_pau_forward``);
+    A is [n_groups, m+1], B is [n_groups, n] (None when n == 0)."""
+    return _forward(x, A, B, n_groups, m, n, out, stream, pau=True)
 
 
 def grkan_backward_workspace_size(rows: int, d: int, n_groups: int, io: int = GRKAN_F32,
                                   flags: int = 0) -> int:
     return int(load_library().grkan_backward_workspace_size(rows, d, n_groups, io, flags))
+
+
+def grkan_pau_backward_workspace_size(rows: int, d: int, n_groups: int, m: int, n: int,
+                                      io: int = GRKAN_F32, flags: int = 0) -> int:
+    return int(load_library().grkan_pau_backward_workspace_size(rows, d, n_groups, m, n, io, flags))
+
+
+def grkan_pau_supported(m: int, n: int) -> bool:
+    return bool(load_library().grkan_pau_supported(m, n))
+
+
+def _backward(x, dy, A, B, n_groups, m, n, mode, dx, dA, dB, workspace, stream, pau):
+    lib = load_library()
+    io = _io(x)
+    if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device or not dy.is_contiguous():
+        raise ValueError("dy must match x")
+    _check_coefs(A, B, n_groups, x.device, m, n)
+    rows, d = _rows_d(x)
+    if mode not in _MODES:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}")
+    flags = _MODES[mode]
+    dx = torch.empty_like(x) if dx is None else dx
+    dA = torch.empty((n_groups, m + 1), dtype=torch.float32, device=x.device) if dA is None else dA
+    if dB is None and n > 0:
+        dB = torch.empty((n_groups, n), dtype=torch.float32, device=x.device)
+    if pau:
+        ws_bytes = lib.grkan_pau_backward_workspace_size(rows, d, n_groups, m, n, io, flags)
+    else:
+        ws_bytes = lib.grkan_backward_workspace_size(rows, d, n_groups, io, flags)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    wsp = _ptr(workspace) if workspace is not None else None
+    wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    s = ctypes.c_void_p(_stream(stream))
+    if pau:
+        st = lib.grkan_pau_backward(_ptr(x), _ptr(dy), _ptr(A), _ptr(B), _ptr(dx), _ptr(dA), _ptr(dB),
+                                    rows, d, n_groups, m, n, io, flags, wsp, wsn, s)
+    else:
+        st = lib.grkan_backward(_ptr(x), _ptr(dy), _ptr(A), _ptr(B), _ptr(dx), _ptr(dA), _ptr(dB),
+                                rows, d, n_groups, io, flags, wsp, wsn, s)
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_pau_backward" if pau else "grkan_backward")
+    return dx, dA, dB
 
 
 def grkan_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
@@ -133,28 +210,17 @@ def grkan_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B: torch.
     "block_atomic" (one fp32 atomic per coefficient per workgroup) or "naive"
     (ten fp32 atomics per element); the last two are for comparison only.
     """
-    lib = load_library()
-    io = _io(x)
-    if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device or not dy.is_contiguous():
-        raise ValueError("dy must match x")
-    _check_coefs(A, B, n_groups, x.device)
-    rows, d = _rows_d(x)
-    if mode not in _MODES:
-        raise ValueError(f"mode must be one of {sorted(_MODES)}")
-    flags = _MODES[mode]
-    dx = torch.empty_like(x) if dx is None else dx
-    dA = torch.empty((n_groups, 6), dtype=torch.float32, device=x.device) if dA is None else dA
-    dB = torch.empty((n_groups, 4), dtype=torch.float32, device=x.device) if dB is None else dB
-    ws_bytes = lib.grkan_backward_workspace_size(rows, d, n_groups, io, flags)
-    if ws_bytes and workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-    wsp = _ptr(workspace) if workspace is not None else None
-    wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.grkan_backward(_ptr(x), _ptr(dy), _ptr(A), _ptr(B), _ptr(dx), _ptr(dA), _ptr(dB),
-                            rows, d, n_groups, io, flags, wsp, wsn, ctypes.c_void_p(_stream(stream)))
-    if st != GRKAN_OK:
-        raise GRKANError(st, "grkan_backward")
-    return dx, dA, dB
+    return _backward(x, dy, A, B, n_groups, GRKAN_M, GRKAN_N, mode, dx, dA, dB, workspace, stream,
+                     pau=False)
+
+
+def grkan_pau_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B, n_groups: int,
+                       m: int, n: int, mode: str = "deterministic",
+                       dx: torch.Tensor | None = None, dA: torch.Tensor | None = None,
+                       dB: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                       stream=None):
+    """(dx, dA, dB) for degrees (m, n) (``grkan_pau_backward``); dB is None when n == 0."""
+    return _backward(x, dy, A, B, n_groups, m, n, mode, dx, dA, dB, workspace, stream, pau=True)
 
 
 def grkan_query_launch(rows: int, d: int, n_groups: int, io: int, pass_: int) -> dict:
@@ -164,6 +230,16 @@ def grkan_query_launch(rows: int, d: int, n_groups: int, io: int, pass_: int) ->
     st = load_library().grkan_query_launch(rows, d, n_groups, io, pass_, ctypes.byref(out))
     if st != GRKAN_OK:
         raise GRKANError(st, "grkan_query_launch")
+    return {f: getattr(out, f) for f, _ in grkan_launch_t._fields_}
+
+
+def grkan_pau_query_launch(rows: int, d: int, n_groups: int, m: int, n: int, io: int,
+                           pass_: int) -> dict:
+    """grkan_query_launch for degrees (m, n)."""
+    out = grkan_launch_t()
+    st = load_library().grkan_pau_query_launch(rows, d, n_groups, m, n, io, pass_, ctypes.byref(out))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_pau_query_launch")
     return {f: getattr(out, f) for f, _ in grkan_launch_t._fields_}
 
 

@@ -9,8 +9,9 @@
 // Launch plan.  The pages' Algorithm 2 (section "3. FlashKAT 核函数重构
 // （Algorithm 2）") uses a grid of ceil(rows / S_block) row tiles x n_g groups.
 // Here likewise: tiles of unroll x rows_per_iter rows, one workgroup per
-// (tile, group).  The plan depends only on the shape and dtype, never on the
-// device, so the deterministic mode gives the same bits on every device.
+// (tile, group, column part).  The plan depends only on the shape, dtype and
+// degrees, never on the device, so the deterministic mode gives the same bits
+// on every device.
 #include <limits.h>
 #include <stdint.h>
 
@@ -24,7 +25,32 @@ using namespace grkan;
 
 namespace {
 
-constexpr int kCoefs = 10;
+// ------------------------------------------------------- degree dispatch
+
+struct DegreeOps {
+    int m, n;
+    int (*unroll)(grkan_dtype_t, int);
+    int (*target_block)(grkan_dtype_t, int, bool);
+    hipError_t (*forward)(grkan_dtype_t, const FwdArgs &, dim3, hipStream_t);
+    hipError_t (*backward)(grkan_dtype_t, const BwdArgs &, dim3, hipStream_t);
+    hipError_t (*occupancy)(grkan_dtype_t, int, int, int *);
+};
+
+#define GRKAN_DEGREE_ENTRY(M, N)                                                                \
+    {M, N, &Kernels<M, N>::unroll, &Kernels<M, N>::target_block, &Kernels<M, N>::forward,      \
+     &Kernels<M, N>::backward, &Kernels<M, N>::occupancy},
+const DegreeOps kDegrees[] = {GRKAN_FOR_EACH_DEGREE(GRKAN_DEGREE_ENTRY)};
+#undef GRKAN_DEGREE_ENTRY
+
+const DegreeOps *find_degree(int32_t m, int32_t n) {
+    for (const DegreeOps &d : kDegrees)
+        if (d.m == m && d.n == n) return &d;
+    return nullptr;
+}
+
+constexpr int32_t kGrkanM = 5, kGrkanN = 4;
+
+// ------------------------------------------------------------ validation
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -40,117 +66,158 @@ bool bad_alias(const void *p, const void *q, size_t n) { return p != q && overla
 
 int io_bytes(grkan_dtype_t io) { return io == GRKAN_BF16 ? 2 : 4; }
 
-// Shape checks and the launch plan (a function of the shape and dtype only).
-grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, grkan_dtype_t io, int pass,
-                          bool atomic_mode, Geometry *G) {
+constexpr int kMaxBlockThreads = 1024;
+constexpr int64_t kMaxGroups = 65535;
+constexpr int64_t kMaxLaneSpan = int64_t(1) << 31;  // bytes a workgroup's lanes may span
+
+// Shape checks and the launch plan (a function of the shape, dtype and degrees).
+grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, const DegreeOps &deg,
+                          grkan_dtype_t io, int pass, bool atomic_mode, Plan *P) {
     if (io != GRKAN_F32 && io != GRKAN_BF16) return GRKAN_ERR_INVALID_ARG;
     if (rows < 0 || d <= 0 || n_groups <= 0 || d % n_groups != 0) return GRKAN_ERR_INVALID_ARG;
     const int es = io_bytes(io);
     if (d > INT64_MAX / es || (rows > 0 && rows > INT64_MAX / (d * es))) return GRKAN_ERR_INVALID_ARG;
     const int64_t seg_bytes = (d / n_groups) * es;
     if (seg_bytes % 16 != 0) return GRKAN_ERR_UNSUPPORTED;
+    if (n_groups > kMaxGroups) return GRKAN_ERR_UNSUPPORTED;
     const int64_t seg_vecs = seg_bytes / 16;
-    if (seg_vecs > 1024) return GRKAN_ERR_UNSUPPORTED;
+    const int64_t row_bytes = d * es;
 
-    // Rows per pass: the whole-wave block (a multiple of 64 lanes, so the DPP
-    // wave sums see only real lanes) closest to the kernel's target size; if
-    // no multiple of seg_vecs up to 1024 is a multiple of 64, pad the block
-    // with idle lanes instead.
-    const int kTargetBlock = target_block(io, pass, atomic_mode);
-    int rpi = 0;
-    for (int k = 1; k * seg_vecs <= 1024; ++k) {
-        const int w = k * (int)seg_vecs;
-        if (w % 64 != 0) continue;
-        if (rpi == 0 || std::abs(w - kTargetBlock) < std::abs(rpi * (int)seg_vecs - kTargetBlock)) rpi = k;
+    // Column parts: a segment wider than the target block is split into
+    // parts of at most target lanes.  Rows per pass: for a one-part segment,
+    // the k with k * seg_vecs a whole number of waves closest to the target
+    // (partial waves otherwise).
+    const int target = deg.target_block(io, pass, atomic_mode);
+    int64_t parts = 1, part_vecs = seg_vecs;
+    int rpi = 1;
+    if (seg_vecs > target) {
+        parts = (seg_vecs + target - 1) / target;
+        part_vecs = (seg_vecs + parts - 1) / parts;
+        parts = (seg_vecs + part_vecs - 1) / part_vecs;
+    } else {
+        rpi = 0;
+        for (int k = 1; k * seg_vecs <= kMaxBlockThreads; ++k) {
+            const int w = k * (int)seg_vecs;
+            if (w % 64 != 0) continue;
+            if (rpi == 0 || std::abs(w - target) < std::abs(rpi * (int)seg_vecs - target)) rpi = k;
+        }
+        if (rpi == 0) rpi = target / (int)seg_vecs > 0 ? target / (int)seg_vecs : 1;
     }
-    if (rpi == 0) {
-        rpi = kTargetBlock / (int)seg_vecs;
-        if (rpi < 1) rpi = 1;
-    }
-    const int lanes = rpi * (int)seg_vecs;
-    const int u = unroll(io, pass);
-    G->rows = rows;
-    G->row_vecs = d * es / 16;
-    G->seg_vecs = (int32_t)seg_vecs;
-    G->rows_per_iter = rpi;
-    G->lanes = lanes;
-    G->block = (lanes + 63) / 64 * 64;
-    G->n_groups = n_groups;
-    G->unroll = u;
+    const int u = deg.unroll(io, pass);
+    if ((int64_t)u * rpi * row_bytes > kMaxLaneSpan) return GRKAN_ERR_UNSUPPORTED;
+    P->rows = rows;
+    P->d = d;
+    P->n_groups = n_groups;
+    P->m = deg.m;
+    P->n = deg.n;
+    P->es = es;
+    P->row_bytes = row_bytes;
+    P->seg_bytes = seg_bytes;
+    P->seg_vecs = (int32_t)seg_vecs;
+    P->parts = (int32_t)parts;
+    P->part_vecs = (int32_t)part_vecs;
+    P->rows_per_iter = rpi;
+    P->unroll = u;
+    P->block = (int32_t)part_vecs * rpi;
     const int64_t tile_rows = (int64_t)u * rpi;
-    G->tiles = (rows + tile_rows - 1) / tile_rows;
-    G->grid = 8 * (int64_t)n_groups * ((G->tiles + 7) / 8);
-    if (G->grid > INT32_MAX) return GRKAN_ERR_UNSUPPORTED;
+    P->tiles = (rows + tile_rows - 1) / tile_rows;
+    P->bundles = (P->tiles + 7) / 8;
+    P->ncoef = deg.m + 1 + deg.n;
+    // The merge indexes slots in 32 bits and puts their 8192-slot chunks on a grid dimension.
+    if (plan_slots(*P) > (int64_t)65535 * 8192) return GRKAN_ERR_UNSUPPORTED;
+    // Whole bundles per launch: workgroup indices below 2^31 and work-items
+    // (workgroups x block) below 2^32.
+    const int64_t per_bundle = 8 * parts * n_groups;
+    int64_t bpl = (int64_t(1) << 31) / per_bundle;
+    const int64_t by_items = ((int64_t(1) << 32) - 1) / (per_bundle * P->block);
+    if (by_items < bpl) bpl = by_items;
+    if (bpl < 1) return GRKAN_ERR_UNSUPPORTED;
+    P->bundles_per_launch = bpl;
+    P->div_gp = make_fastdiv((uint32_t)(parts * n_groups));
+    P->div_parts = make_fastdiv((uint32_t)parts);
     return GRKAN_OK;
 }
 
-// fp32 partials [n_groups][10][8 * ceil(tiles / 8)] (one slot per tile, grouped by XCD).
-size_t partials_bytes(const Geometry &G) {
-    return (size_t)G.n_groups * kCoefs * (size_t)(8 * ((G.tiles + 7) / 8)) * sizeof(float);
+// Workspace of the deterministic backward: fp32 partials
+// [n_groups][ncoef][slots], then (when the merge needs more than one chunk
+// per coefficient) fp64 chunk sums [n_groups][ncoef][chunks], 16-byte aligned.
+size_t partials_bytes(const Plan &P) {
+    return (size_t)P.n_groups * P.ncoef * (size_t)plan_slots(P) * sizeof(float);
+}
+size_t chunk_sums_offset(const Plan &P) { return (partials_bytes(P) + 15) / 16 * 16; }
+size_t workspace_need(const Plan &P) {
+    const uint32_t chunks = merge_chunks(plan_slots(P));
+    if (chunks <= 1) return partials_bytes(P);
+    return chunk_sums_offset(P) + (size_t)P.n_groups * P.ncoef * chunks * sizeof(double);
 }
 
-// Per-device CU count and occupancy, for grkan_query_launch only.
+// Per-device CU count, for grkan_query_launch only.
 constexpr int kMaxDev = 64;
 std::mutex g_mu;
 int g_cus[kMaxDev];
 
 grkan_status_t from_hip(hipError_t e) { return e == hipSuccess ? GRKAN_OK : GRKAN_ERR_HIP; }
 
-}  // namespace
-
-extern "C" const char *grkan_status_string(grkan_status_t status) {
-    switch (status) {
-    case GRKAN_OK: return "GRKAN_OK: success";
-    case GRKAN_ERR_INVALID_ARG: return "GRKAN_ERR_INVALID_ARG: invalid argument";
-    case GRKAN_ERR_UNSUPPORTED: return "GRKAN_ERR_UNSUPPORTED: unsupported shape or alignment";
-    case GRKAN_ERR_HIP: return "GRKAN_ERR_HIP: HIP runtime error";
-    }
-    return "GRKAN: unknown status";
+// Grid of one launch covering bundles [b0, b0 + nz).
+dim3 grid_of(const Plan &P, int64_t nz) {
+    return dim3((unsigned)(8 * (int64_t)P.parts * P.n_groups * nz));
 }
 
-extern "C" grkan_status_t grkan_forward(const void *x, void *y, const float *A, const float *B,
-                                        int64_t rows, int64_t d, int32_t n_groups,
-                                        grkan_dtype_t io, hipStream_t stream) {
-    Geometry G;
-    grkan_status_t st = plan_shape(rows, d, n_groups, io, 0, false, &G);
+grkan_status_t forward_impl(const void *x, void *y, const float *A, const float *B, int64_t rows,
+                            int64_t d, int32_t n_groups, int32_t m, int32_t n, grkan_dtype_t io,
+                            hipStream_t stream) {
+    const DegreeOps *deg = find_degree(m, n);
+    if (!deg) return (m < 0 || n < 0) ? GRKAN_ERR_INVALID_ARG : GRKAN_ERR_UNSUPPORTED;
+    Plan P;
+    grkan_status_t st = plan_shape(rows, d, n_groups, *deg, io, 0, false, &P);
     if (st != GRKAN_OK) return st;
-    if (!A || !B) return GRKAN_ERR_INVALID_ARG;
+    if (!A || (n > 0 && !B)) return GRKAN_ERR_INVALID_ARG;
     if (!aligned(A, 4) || !aligned(B, 4)) return GRKAN_ERR_UNSUPPORTED;
     if (rows == 0) return GRKAN_OK;
     if (!x || !y) return GRKAN_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(y, 16)) return GRKAN_ERR_UNSUPPORTED;
     const size_t bytes = (size_t)rows * (size_t)d * io_bytes(io);
     if (bad_alias(x, y, bytes)) return GRKAN_ERR_INVALID_ARG;
-    const size_t cb = (size_t)n_groups * 6 * 4, bb = (size_t)n_groups * 4 * 4;
-    if (overlap(y, bytes, A, cb) || overlap(y, bytes, B, bb)) return GRKAN_ERR_INVALID_ARG;
+    const size_t ab = (size_t)n_groups * (m + 1) * 4, bb = (size_t)n_groups * n * 4;
+    if (overlap(y, bytes, A, ab) || overlap(y, bytes, B, bb)) return GRKAN_ERR_INVALID_ARG;
 
-    FwdArgs a{x, y, A, B, G};
-    return from_hip(launch_forward(io, a, stream));
+    // ---- validation done; HIP calls from here on
+    for (int64_t b0 = 0; b0 < P.bundles; b0 += P.bundles_per_launch) {
+        const int64_t nz = (P.bundles - b0 < P.bundles_per_launch) ? P.bundles - b0 : P.bundles_per_launch;
+        FwdArgs a{x, y, A, B, P, b0};
+        st = from_hip(deg->forward(io, a, grid_of(P, nz), stream));
+        if (st != GRKAN_OK) return st;
+    }
+    return GRKAN_OK;
 }
 
-extern "C" size_t grkan_backward_workspace_size(int64_t rows, int64_t d, int32_t n_groups,
-                                                grkan_dtype_t io, uint32_t flags) {
+size_t workspace_impl(int64_t rows, int64_t d, int32_t n_groups, int32_t m, int32_t n,
+                      grkan_dtype_t io, uint32_t flags) {
     if (flags != 0) return 0;
-    Geometry G;
-    if (plan_shape(rows, d, n_groups, io, 1, false, &G) != GRKAN_OK) return 0;
-    return partials_bytes(G);
+    const DegreeOps *deg = find_degree(m, n);
+    if (!deg) return 0;
+    Plan P;
+    if (plan_shape(rows, d, n_groups, *deg, io, 1, false, &P) != GRKAN_OK) return 0;
+    return workspace_need(P);
 }
 
-extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const float *A,
-                                         const float *B, void *dx, float *dA, float *dB,
-                                         int64_t rows, int64_t d, int32_t n_groups,
-                                         grkan_dtype_t io, uint32_t flags, void *workspace,
-                                         size_t workspace_bytes, hipStream_t stream) {
-    Geometry G;
+grkan_status_t backward_impl(const void *x, const void *dy, const float *A, const float *B, void *dx,
+                             float *dA, float *dB, int64_t rows, int64_t d, int32_t n_groups,
+                             int32_t m, int32_t n, grkan_dtype_t io, uint32_t flags,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
     if (flags & ~(uint32_t)(GRKAN_BLOCK_ATOMIC | GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
     if ((flags & GRKAN_BLOCK_ATOMIC) && (flags & GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
-    grkan_status_t st = plan_shape(rows, d, n_groups, io, 1, flags != 0, &G);
+    const DegreeOps *deg = find_degree(m, n);
+    if (!deg) return (m < 0 || n < 0) ? GRKAN_ERR_INVALID_ARG : GRKAN_ERR_UNSUPPORTED;
+    if ((flags & GRKAN_NAIVE_ATOMIC) && (m != kGrkanM || n != kGrkanN)) return GRKAN_ERR_UNSUPPORTED;
+    Plan P;
+    grkan_status_t st = plan_shape(rows, d, n_groups, *deg, io, 1, flags != 0, &P);
     if (st != GRKAN_OK) return st;
-    if (!A || !B || !dA || !dB) return GRKAN_ERR_INVALID_ARG;
+    if (!A || !dA || (n > 0 && (!B || !dB))) return GRKAN_ERR_INVALID_ARG;
     if (!aligned(A, 4) || !aligned(B, 4) || !aligned(dA, 4) || !aligned(dB, 4))
         return GRKAN_ERR_UNSUPPORTED;
     const size_t bytes = (size_t)rows * (size_t)d * io_bytes(io);
-    const size_t ab = (size_t)n_groups * 6 * 4, bb = (size_t)n_groups * 4 * 4;
+    const size_t ab = (size_t)n_groups * (m + 1) * 4, bb = (size_t)n_groups * n * 4;
     if (rows > 0) {
         if (!x || !dy || !dx) return GRKAN_ERR_INVALID_ARG;
         if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16)) return GRKAN_ERR_UNSUPPORTED;
@@ -165,7 +232,7 @@ extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const fl
             return GRKAN_ERR_INVALID_ARG;
     const bool det = flags == 0;
     if (det && rows > 0) {
-        const size_t need = partials_bytes(G);
+        const size_t need = workspace_need(P);
         if (!workspace || workspace_bytes < need) return GRKAN_ERR_INVALID_ARG;
         if (!aligned(workspace, 16)) return GRKAN_ERR_UNSUPPORTED;
         for (int i = 0; i < 5; ++i)
@@ -175,30 +242,37 @@ extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const fl
     }
 
     // ---- validation done; HIP calls from here on
-    if (rows == 0) return from_hip(launch_zero(dA, dB, n_groups, stream));
+    const int64_t na = (int64_t)n_groups * (m + 1), nb = (int64_t)n_groups * n;
+    if (rows == 0) return from_hip(launch_zero(dA, dB, na, nb, stream));
     if (flags & GRKAN_NAIVE_ATOMIC) {
-        st = from_hip(launch_zero(dA, dB, n_groups, stream));
+        st = from_hip(launch_zero(dA, dB, na, nb, stream));
         if (st != GRKAN_OK) return st;
         return from_hip(launch_naive(io, x, dy, dx, A, B, dA, dB, rows, d, n_groups, stream));
     }
-    BwdArgs a{x, dy, dx, A, B, dA, dB, static_cast<float *>(workspace),
-              det ? kModePartials : kModeAtomic, G};
     if (!det) {
-        st = from_hip(launch_zero(dA, dB, n_groups, stream));
+        st = from_hip(launch_zero(dA, dB, na, nb, stream));
         if (st != GRKAN_OK) return st;
-        return from_hip(launch_backward(io, a, stream));
     }
-    st = from_hip(launch_backward(io, a, stream));
-    if (st != GRKAN_OK) return st;
-    return from_hip(launch_merge(a.partials, n_groups, G.tiles, dA, dB, stream));
+    float *partials = static_cast<float *>(workspace);
+    for (int64_t b0 = 0; b0 < P.bundles; b0 += P.bundles_per_launch) {
+        const int64_t nz = (P.bundles - b0 < P.bundles_per_launch) ? P.bundles - b0 : P.bundles_per_launch;
+        BwdArgs a{x, dy, dx, A, B, dA, dB, partials, det ? kModePartials : kModeAtomic, P, b0};
+        st = from_hip(deg->backward(io, a, grid_of(P, nz), stream));
+        if (st != GRKAN_OK) return st;
+    }
+    if (!det) return GRKAN_OK;
+    double *chunk_sums = reinterpret_cast<double *>(static_cast<char *>(workspace) + chunk_sums_offset(P));
+    return from_hip(launch_merge(partials, chunk_sums, n_groups, m, n, P.tiles, P.bundles, P.parts, dA, dB,
+                                 stream));
 }
 
-extern "C" grkan_status_t grkan_query_launch(int64_t rows, int64_t d, int32_t n_groups,
-                                             grkan_dtype_t io, int32_t pass,
-                                             grkan_launch_t *out) {
+grkan_status_t query_impl(int64_t rows, int64_t d, int32_t n_groups, int32_t m, int32_t n,
+                          grkan_dtype_t io, int32_t pass, grkan_launch_t *out) {
     if (!out || pass < 0 || pass > 2) return GRKAN_ERR_INVALID_ARG;
-    Geometry G;
-    grkan_status_t st = plan_shape(rows, d, n_groups, io, pass ? 1 : 0, pass == 2, &G);
+    const DegreeOps *deg = find_degree(m, n);
+    if (!deg) return (m < 0 || n < 0) ? GRKAN_ERR_INVALID_ARG : GRKAN_ERR_UNSUPPORTED;
+    Plan P;
+    grkan_status_t st = plan_shape(rows, d, n_groups, *deg, io, pass ? 1 : 0, pass == 2, &P);
     if (st != GRKAN_OK) return st;
     int dev = 0, cus = 0, occ = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return GRKAN_ERR_HIP;
@@ -212,13 +286,87 @@ extern "C" grkan_status_t grkan_query_launch(int64_t rows, int64_t d, int32_t n_
         std::lock_guard<std::mutex> lock(g_mu);
         g_cus[dev] = cus;
     }
-    if (occupancy(io, pass ? 1 : 0, G.block, &occ) != hipSuccess) return GRKAN_ERR_HIP;
-    out->block = G.block;
-    out->rows_per_iter = G.rows_per_iter;
-    out->unroll = G.unroll;
-    out->tiles = G.tiles;
-    out->grid = G.grid;
+    if (deg->occupancy(io, pass ? 1 : 0, P.block, &occ) != hipSuccess) return GRKAN_ERR_HIP;
+    out->block = P.block;
+    out->rows_per_iter = P.rows_per_iter;
+    out->unroll = P.unroll;
+    out->tiles = P.tiles;
+    out->grid = plan_grid(P);
     out->cus = cus;
     out->blocks_per_cu = occ;
+    out->parts = P.parts;
+    out->part_vecs = P.part_vecs;
     return GRKAN_OK;
+}
+
+}  // namespace
+
+extern "C" const char *grkan_status_string(grkan_status_t status) {
+    switch (status) {
+    case GRKAN_OK: return "GRKAN_OK: success";
+    case GRKAN_ERR_INVALID_ARG: return "GRKAN_ERR_INVALID_ARG: invalid argument";
+    case GRKAN_ERR_UNSUPPORTED: return "GRKAN_ERR_UNSUPPORTED: unsupported shape, degree or alignment";
+    case GRKAN_ERR_HIP: return "GRKAN_ERR_HIP: HIP runtime error";
+    }
+    return "GRKAN: unknown status";
+}
+
+// ----------------------------------------------------------------- GR-KAN
+
+extern "C" grkan_status_t grkan_forward(const void *x, void *y, const float *A, const float *B,
+                                        int64_t rows, int64_t d, int32_t n_groups,
+                                        grkan_dtype_t io, hipStream_t stream) {
+    return forward_impl(x, y, A, B, rows, d, n_groups, kGrkanM, kGrkanN, io, stream);
+}
+
+extern "C" size_t grkan_backward_workspace_size(int64_t rows, int64_t d, int32_t n_groups,
+                                                grkan_dtype_t io, uint32_t flags) {
+    return workspace_impl(rows, d, n_groups, kGrkanM, kGrkanN, io, flags);
+}
+
+extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const float *A,
+                                         const float *B, void *dx, float *dA, float *dB,
+                                         int64_t rows, int64_t d, int32_t n_groups,
+                                         grkan_dtype_t io, uint32_t flags, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
+    return backward_impl(x, dy, A, B, dx, dA, dB, rows, d, n_groups, kGrkanM, kGrkanN, io, flags,
+                         workspace, workspace_bytes, stream);
+}
+
+extern "C" grkan_status_t grkan_query_launch(int64_t rows, int64_t d, int32_t n_groups,
+                                             grkan_dtype_t io, int32_t pass,
+                                             grkan_launch_t *out) {
+    return query_impl(rows, d, n_groups, kGrkanM, kGrkanN, io, pass, out);
+}
+
+// ------------------------------------------------------------- PAU family
+
+extern "C" int grkan_pau_supported(int32_t m, int32_t n) { return find_degree(m, n) != nullptr; }
+
+extern "C" grkan_status_t grkan_pau_forward(const void *x, void *y, const float *A, const float *B,
+                                            int64_t rows, int64_t d, int32_t n_groups, int32_t m,
+                                            int32_t n, grkan_dtype_t io, hipStream_t stream) {
+    return forward_impl(x, y, A, B, rows, d, n_groups, m, n, io, stream);
+}
+
+extern "C" size_t grkan_pau_backward_workspace_size(int64_t rows, int64_t d, int32_t n_groups,
+                                                    int32_t m, int32_t n, grkan_dtype_t io,
+                                                    uint32_t flags) {
+    return workspace_impl(rows, d, n_groups, m, n, io, flags);
+}
+
+extern "C" grkan_status_t grkan_pau_backward(const void *x, const void *dy, const float *A,
+                                             const float *B, void *dx, float *dA, float *dB,
+                                             int64_t rows, int64_t d, int32_t n_groups, int32_t m,
+                                             int32_t n, grkan_dtype_t io, uint32_t flags,
+                                             void *workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+    return backward_impl(x, dy, A, B, dx, dA, dB, rows, d, n_groups, m, n, io, flags, workspace,
+                         workspace_bytes, stream);
+}
+
+extern "C" grkan_status_t grkan_pau_query_launch(int64_t rows, int64_t d, int32_t n_groups,
+                                                 int32_t m, int32_t n, grkan_dtype_t io,
+                                                 int32_t pass, grkan_launch_t *out) {
+    return query_impl(rows, d, n_groups, m, n, io, pass, out);
 }

@@ -1,16 +1,20 @@
-// grkan_device.h -- device-side building blocks of the GR-KAN kernels (gfx950).
+// grkan_device.h -- device-side building blocks of the GR-KAN / PAU kernels
+// (gfx950).
 //
 // Pages cited
 //   [FlashKAT notes]  "FlashKAT: Understanding and Addressing Performance
 //                     Bottlenecks in the Kolmogorov-Arnold Transformer",
 //                     Paper-Notes page (AAAI 2026), arXiv 2505.13813.
 //
-// The activation is F(x) = P(x) / (1 + |Q(x)|) with P of degree 5 (a_0..a_5)
-// and Q of degree 4 without constant term (b_1..b_4), one coefficient set per
-// channel group ([FlashKAT notes], sections "KAT 的突破与残留问题" and
-// "损失函数 / 训练策略").  Everything here is fp32 register arithmetic; the
-// only fp64 use is (a) the carry of the long gradient sums and (b) deciding
-// the sign of Q for the rare element whose fp32 Q is within rounding of 0.
+// The activation is F(x) = P(x) / (1 + |Q(x)|) with P of degree M (a_0..a_M)
+// and Q of degree N without constant term (b_1..b_N), one coefficient set per
+// channel group.  GR-KAN is M = 5, N = 4 ([FlashKAT notes], sections "KAT 的
+// 突破与残留问题" and "损失函数 / 训练策略"); the pages note that the same
+// kernel restructuring applies to PAU and its variants (section "局限性与未来
+// 工作"), i.e. to other (M, N), which the templates below cover.  N = 0 is a
+// plain polynomial.  Everything here is fp32 register arithmetic; the only
+// fp64 use is deciding the sign of Q for the rare element whose fp32 Q is
+// within rounding of 0.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,10 +25,6 @@ namespace grkan {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kNumA = 6;             // a_0..a_5
-constexpr int kNumB = 4;             // b_1..b_4
-constexpr int kNumCoef = kNumA + kNumB;
 
 // Tag type for bf16 storage (values are handled as fp32 in registers).
 struct bf16io {};
@@ -69,92 +69,169 @@ template <> struct Io<bf16io> {
     }
 };
 
-template <bool NT>
-__device__ static inline u32x4 load16(const u32x4 *p) {
-    if constexpr (NT) return __builtin_nontemporal_load(p);
-    else return *p;
+// ------------------------------------------------------------ windows
+//
+// The streaming kernels address each tensor through a window: a base pointer
+// (uniform, in scalar registers) and a byte length, plus a 32-bit per-lane
+// byte offset.  An access at an offset past the length is skipped -- a load
+// gives zeros, a store does nothing -- which is how the kernels handle the
+// ragged last row tile and ragged column parts with one code path.  Offsets
+// stay below 2^31 and lengths at most 2^31, so kOffsetOutOfRange is past
+// every window.  (Buffer-resource instructions do the same check in
+// hardware, but streamed ~3% slower than plain global loads and stores at
+// the KAT-B shapes on MI355X.)
+
+struct Span {
+    const char *p;
+    uint32_t n;
+};
+
+constexpr uint32_t kOffsetOutOfRange = 0x80000000u;
+constexpr int64_t kMaxWindow = int64_t(1) << 31;
+
+// The window [base, base + min(bytes, 2^31)).
+__device__ static inline Span make_span(const void *base, int64_t bytes) {
+    const int64_t n = bytes < kMaxWindow ? bytes : kMaxWindow;
+    return Span{static_cast<const char *>(base), (uint32_t)n};
 }
-template <bool NT>
-__device__ static inline void store16(u32x4 *p, u32x4 v) {
-    if constexpr (NT) __builtin_nontemporal_store(v, p);
-    else *p = v;
+
+// 16-byte accesses, non-temporal: the data is streamed once.
+__device__ static inline u32x4 win_load16(Span w, uint32_t off) {
+    return off < w.n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w.p + off))
+                     : u32x4{0u, 0u, 0u, 0u};
 }
+__device__ static inline void win_store16(Span w, uint32_t off, u32x4 v) {
+    if (off < w.n) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(const_cast<char *>(w.p) + off));
+}
+// A second read of data already loaded once, through a volatile access so
+// that the compiler issues it again instead of keeping the first load's
+// registers live until this point (the rare exact-sign path of the backward).
+__device__ static inline u32x4 win_reload16(Span w, uint32_t off) {
+    if (off >= w.n) return u32x4{0u, 0u, 0u, 0u};
+    return *reinterpret_cast<const volatile u32x4 *>(w.p + off);
+}
+
+// ------------------------------------------------------------ coefficients
+
+template <int M, int N> struct Deg {
+    static_assert(M >= 0 && N >= 0, "degrees");
+    static constexpr int kNumA = M + 1;          // a_0..a_M
+    static constexpr int kNumB = N;              // b_1..b_N
+    static constexpr int kNumCoef = M + 1 + N;   // gradient sums per group
+    static constexpr int kTop = M > N ? M : N;   // highest power of x needed
+};
 
 // Coefficients of one group.  Loaded with uniform addresses, so they live in
 // scalar registers; the derived constants below are computed once per
 // workgroup.
-struct Coefs {
-    float a[kNumA];
-    float b[kNumB];
+template <int M, int N> struct Coefs {
+    float a[M + 1];
+    float b[N > 0 ? N : 1];
 };
 
-__device__ static inline Coefs load_coefs(const float *__restrict__ A, const float *__restrict__ B,
-                                          int g) {
-    Coefs c;
+template <int M, int N>
+__device__ static inline Coefs<M, N> load_coefs(const float *__restrict__ A,
+                                                const float *__restrict__ B, int g) {
+    Coefs<M, N> c;
 #pragma unroll
-    for (int i = 0; i < kNumA; ++i) c.a[i] = A[g * kNumA + i];
+    for (int i = 0; i <= M; ++i) c.a[i] = A[g * (M + 1) + i];
 #pragma unroll
-    for (int j = 0; j < kNumB; ++j) c.b[j] = B[g * kNumB + j];
+    for (int j = 0; j < N; ++j) c.b[j] = B[g * N + j];
+    if constexpr (N == 0) c.b[0] = 0.0f;
     return c;
 }
 
-// Forward value, Horner form: 5 + 3 FMA, 1 mul, 1 add, 1 reciprocal, 1 mul.
-// D >= 1, so the hardware reciprocal (1 ulp) cannot under- or overflow.
-__device__ static inline float rational(float x, const Coefs &c) {
-    float P = fmaf(fmaf(fmaf(fmaf(fmaf(c.a[5], x, c.a[4]), x, c.a[3]), x, c.a[2]), x, c.a[1]), x,
-                   c.a[0]);
-    float q = fmaf(fmaf(fmaf(c.b[3], x, c.b[2]), x, c.b[1]), x, c.b[0]);
-    float D = 1.0f + fabsf(x * q);
-    return P * __builtin_amdgcn_rcpf(D);
+// Forward value, Horner form: M + (N - 1) FMA, 1 mul, 1 add, 1 reciprocal,
+// 1 mul.  D >= 1, so the hardware reciprocal (1 ulp) cannot under- or
+// overflow.
+template <int M, int N>
+__device__ static inline float rational(float x, const Coefs<M, N> &c) {
+    float P = c.a[M];
+#pragma unroll
+    for (int i = M - 1; i >= 0; --i) P = fmaf(P, x, c.a[i]);
+    if constexpr (N == 0) {
+        return P;
+    } else {
+        float q = c.b[N - 1];
+#pragma unroll
+        for (int j = N - 2; j >= 0; --j) q = fmaf(q, x, c.b[j]);
+        const float D = 1.0f + fabsf(x * q);
+        return P * __builtin_amdgcn_rcpf(D);
+    }
 }
 
-// Constants of the backward pass derived from one group's coefficients.
-struct BwdCoefs {
-    float a[kNumA];       // a_0..a_5
-    float da[kNumA - 1];  // i * a_i, i = 1..5   (P')
-    float b[kNumB];       // b_1..b_4
-    float db[kNumB];      // j * b_j, j = 1..4   (Q')
-    float kguard;         // 2^-18 * (|b_1| + .. + |b_4|): rounding guard of sign(Q)
-    bool q_zero;          // b_1 = .. = b_4 = 0: Q vanishes identically, s = 0
+// Powers x^0..x^K: even powers as squares, odd ones as x times the previous
+// (for K = 5: x^2 = x x, x^3 = x^2 x, x^4 = x^2 x^2, x^5 = x^4 x).
+template <int K> struct Pow {
+    float p[K + 1];
+    __device__ inline explicit Pow(float x) {
+        p[0] = 1.0f;
+        if constexpr (K >= 1) p[1] = x;
+#pragma unroll
+        for (int k = 2; k <= K; ++k) p[k] = (k % 2 == 0) ? p[k / 2] * p[k / 2] : p[k - 1] * x;
+    }
 };
 
-// The sign guard.  The fp32 Q below differs from the exact Q(x) by at most
-// about 6 * 2^-24 * sum_j |b_j| |x|^j, and sum_j |b_j| |x|^j is at most
-// (sum_j |b_j|) * (|x| + x^4).  So |Q| > 2^-18 (sum_j |b_j|) (|x| + x^4)
-// -- ten times that bound -- proves Q != 0 and sign(fl(Q)) = sign(Q).
-constexpr float kSignGuard = 1.0f / 262144.0f;
+// Constants of the backward pass derived from one group's coefficients.
+template <int M, int N> struct BwdCoefs {
+    float a[M + 1];              // a_0..a_M
+    float da[M > 0 ? M : 1];     // i * a_i, i = 1..M   (P')
+    float b[N > 0 ? N : 1];      // b_1..b_N
+    float db[N > 0 ? N : 1];     // j * b_j, j = 1..N   (Q')
+    float kguard;                // sign guard scale, see below
+    bool q_zero;                 // b = 0 (or N = 0): Q vanishes identically, s = 0
+};
 
-__device__ static inline BwdCoefs derive(const Coefs &c) {
-    BwdCoefs k;
+// The sign guard.  With powers formed as above and Q = x (b_1 + b_2 x + ...)
+// summed by FMAs over them, the fp32 Q differs from the exact Q(x) by at most
+// about (2N + 1) 2^-24 sum_j |b_j| |x|^j, and sum_j |b_j| |x|^j is at most
+// (sum_j |b_j|) (|x| + |x|^N).  So |Q| > (N + 4) 2^-21 (sum_j |b_j|)
+// (|x| + |x|^N) -- at least four times that bound -- proves Q != 0 and
+// sign(fl(Q)) = sign(Q).  (For GR-KAN's N = 4 the scale is 2^-18.)
+template <int N> constexpr float sign_guard_scale() { return (float)(N + 4) / 2097152.0f; }
+
+template <int M, int N>
+__device__ static inline BwdCoefs<M, N> derive(const Coefs<M, N> &c) {
+    BwdCoefs<M, N> k;
 #pragma unroll
-    for (int i = 0; i < kNumA; ++i) k.a[i] = c.a[i];
+    for (int i = 0; i <= M; ++i) k.a[i] = c.a[i];
 #pragma unroll
-    for (int i = 1; i < kNumA; ++i) k.da[i - 1] = (float)i * c.a[i];
+    for (int i = 1; i <= M; ++i) k.da[i - 1] = (float)i * c.a[i];
+    if constexpr (M == 0) k.da[0] = 0.0f;
     float bsum = 0.0f;
+    bool zero = true;
 #pragma unroll
-    for (int j = 0; j < kNumB; ++j) {
+    for (int j = 0; j < N; ++j) {
         k.b[j] = c.b[j];
         k.db[j] = (float)(j + 1) * c.b[j];
         bsum += fabsf(c.b[j]);
+        zero = zero && (c.b[j] == 0.0f);
     }
-    k.kguard = kSignGuard * bsum;
-    k.q_zero = (c.b[0] == 0.0f) && (c.b[1] == 0.0f) && (c.b[2] == 0.0f) && (c.b[3] == 0.0f);
+    if constexpr (N == 0) {
+        k.b[0] = 0.0f;
+        k.db[0] = 0.0f;
+    }
+    k.kguard = sign_guard_scale<N>() * bsum;
+    k.q_zero = zero;
     return k;
 }
 
-// sign of q(x) = b_1 + b_2 x + b_3 x^2 + b_4 x^3 by compensated Horner in fp64
-// (error-free products by FMA and error-free sums; Graillat, Langlois & Louvet,
-// "Compensated Horner scheme", 2005).  The result carries about twice fp64's
-// precision, enough to fix the sign of every fp32 x that is not an exact root.
-__device__ static inline int sign_q_exact(float xf, const BwdCoefs &k) {
+// sign of q(x) = b_1 + b_2 x + ... + b_N x^(N-1) by compensated Horner in
+// fp64 (error-free products by FMA and error-free sums; Graillat, Langlois &
+// Louvet, "Compensated Horner scheme", 2005).  The result carries about twice
+// fp64's precision, enough to fix the sign of every fp32 x that is not within
+// ~2^-100 (relative) of a root.
+template <int M, int N>
+__device__ static inline int sign_q_exact(float xf, const BwdCoefs<M, N> &k) {
     // The error-free transformations need every product and sum rounded on its
     // own: no contraction of s*x + b into one FMA.
 #pragma clang fp contract(off)
+    static_assert(N >= 1, "no denominator");
     const double x = (double)xf;
-    double s = (double)k.b[3];
+    double s = (double)k.b[N - 1];
     double c = 0.0;
 #pragma unroll
-    for (int j = 2; j >= 0; --j) {
+    for (int j = N - 2; j >= 0; --j) {
         double p = s * x;
         double pe = fma(s, x, -p);         // s*x = p + pe exactly
         double t = p + (double)k.b[j];
@@ -183,56 +260,95 @@ struct ElemBwd {
     bool sure;
 };
 
-__device__ static inline ElemBwd backward_element(float x, float x2, float x3, float x4, float x5,
-                                                  float dy, const BwdCoefs &k) {
-    const float P = fmaf(k.a[5], x5, fmaf(k.a[4], x4, fmaf(k.a[3], x3, fmaf(k.a[2], x2,
-                    fmaf(k.a[1], x, k.a[0])))));
-    const float Pd = fmaf(k.da[4], x4, fmaf(k.da[3], x3, fmaf(k.da[2], x2, fmaf(k.da[1], x, k.da[0]))));
-    const float q = fmaf(k.b[3], x3, fmaf(k.b[2], x2, fmaf(k.b[1], x, k.b[0])));
-    const float Qd = fmaf(k.db[3], x3, fmaf(k.db[2], x2, fmaf(k.db[1], x, k.db[0])));
-    const float Q = x * q;
-    const float r = __builtin_amdgcn_rcpf(1.0f + fabsf(Q));
+template <int M, int N, int K>
+__device__ static inline ElemBwd backward_element(const Pow<K> &X, float dy, const BwdCoefs<M, N> &k) {
+    static_assert(K >= M && K >= N, "powers");
+    const float x = X.p[K >= 1 ? 1 : 0];
+    float P = k.a[0];
+#pragma unroll
+    for (int i = 1; i <= M; ++i) P = fmaf(k.a[i], X.p[i], P);
+    float Pd = (M >= 1) ? k.da[0] : 0.0f;
+#pragma unroll
+    for (int i = 2; i <= M; ++i) Pd = fmaf(k.da[i - 1], X.p[i - 1], Pd);
     ElemBwd e;
-    e.w = dy * r;
-    e.v = e.w * (P * r);
-    e.sv = __uint_as_float(__float_as_uint(e.v) ^ (__float_as_uint(Q) & 0x80000000u));
-    e.sure = fabsf(Q) > k.kguard * (fabsf(x) + x4);
-    e.Qd = Qd;
-    e.wPd = e.w * Pd;
-    e.dx = fmaf(-e.sv, Qd, e.wPd);
+    if constexpr (N == 0) {
+        e.w = dy;
+        e.v = 0.0f;
+        e.sv = 0.0f;
+        e.Qd = 0.0f;
+        e.wPd = dy * Pd;
+        e.dx = e.wPd;
+        e.sure = true;
+    } else {
+        float q = k.b[0];
+#pragma unroll
+        for (int j = 1; j < N; ++j) q = fmaf(k.b[j], X.p[j], q);
+        float Qd = k.db[0];
+#pragma unroll
+        for (int j = 1; j < N; ++j) Qd = fmaf(k.db[j], X.p[j], Qd);
+        const float Q = x * q;
+        const float r = __builtin_amdgcn_rcpf(1.0f + fabsf(Q));
+        e.w = dy * r;
+        e.v = e.w * (P * r);
+        e.sv = __uint_as_float(__float_as_uint(e.v) ^ (__float_as_uint(Q) & 0x80000000u));
+        e.sure = fabsf(Q) > k.kguard * (fabsf(x) + fabsf(X.p[N]));
+        e.Qd = Qd;
+        e.wPd = e.w * Pd;
+        e.dx = fmaf(-e.sv, Qd, e.wPd);
+    }
     return e;
 }
 
-// Adds one element's ten gradient terms (dA: w x^i; dB: -sv x^j) to acc.
-__device__ static inline void accumulate(float w, float sv, float x, float x2, float x3, float x4,
-                                         float x5, float (&acc)[kNumCoef]) {
+// Adds one element's M + 1 + N gradient terms (dA: w x^i; dB: -sv x^j).
+template <int M, int N, int K>
+__device__ static inline void accumulate(float w, float sv, const Pow<K> &X,
+                                         float (&acc)[Deg<M, N>::kNumCoef]) {
     acc[0] += w;
-    acc[1] = fmaf(w, x, acc[1]);
-    acc[2] = fmaf(w, x2, acc[2]);
-    acc[3] = fmaf(w, x3, acc[3]);
-    acc[4] = fmaf(w, x4, acc[4]);
-    acc[5] = fmaf(w, x5, acc[5]);
-    acc[6] = fmaf(-sv, x, acc[6]);
-    acc[7] = fmaf(-sv, x2, acc[7]);
-    acc[8] = fmaf(-sv, x3, acc[8]);
-    acc[9] = fmaf(-sv, x4, acc[9]);
+#pragma unroll
+    for (int i = 1; i <= M; ++i) acc[i] = fmaf(w, X.p[i], acc[i]);
+#pragma unroll
+    for (int j = 1; j <= N; ++j) acc[M + j] = fmaf(-sv, X.p[j], acc[M + j]);
 }
 
 // For an element whose sign was not proven: recomputes it, decides
 // s = sign(x) sign(q(x)) exactly (0 at x == 0), replaces the dB terms that
 // were accumulated with the fp32 sign and returns the exact dX.
-__device__ static inline float exact_fix(float x, float dy, const BwdCoefs &k, float (&acc)[kNumCoef]) {
-    const float x2 = x * x, x3 = x2 * x, x4 = x2 * x2, x5 = x4 * x;
-    const ElemBwd e = backward_element(x, x2, x3, x4, x5, dy, k);
-    if (e.sure) return e.dx;
-    const int s = (x == 0.0f || k.q_zero) ? 0 : sign_q_exact(x, k) * ((x > 0.0f) ? 1 : -1);
-    const float sv = (s == 0) ? 0.0f : ((s > 0) ? e.v : -e.v);
-    const float diff = e.sv - sv;  // undo -e.sv x^j, add -sv x^j
-    acc[6] = fmaf(diff, x, acc[6]);
-    acc[7] = fmaf(diff, x2, acc[7]);
-    acc[8] = fmaf(diff, x3, acc[8]);
-    acc[9] = fmaf(diff, x4, acc[9]);
-    return fmaf(-sv, e.Qd, e.wPd);
+template <int M, int N>
+__device__ static inline float exact_fix(float x, float dy, const BwdCoefs<M, N> &k,
+                                         float (&acc)[Deg<M, N>::kNumCoef]) {
+    constexpr int K = Deg<M, N>::kTop;
+    const Pow<K> X(x);
+    const ElemBwd e = backward_element<M, N, K>(X, dy, k);
+    if constexpr (N == 0) {
+        return e.dx;
+    } else {
+        if (e.sure) return e.dx;
+        const int s = (x == 0.0f || k.q_zero) ? 0 : sign_q_exact<M, N>(x, k) * ((x > 0.0f) ? 1 : -1);
+        const float sv = (s == 0) ? 0.0f : ((s > 0) ? e.v : -e.v);
+        const float diff = e.sv - sv;  // undo -e.sv x^j, add -sv x^j
+#pragma unroll
+        for (int j = 1; j <= N; ++j) acc[M + j] = fmaf(diff, X.p[j], acc[M + j]);
+        return fmaf(-sv, e.Qd, e.wPd);
+    }
+}
+
+// backward_element with the exact sign: when the fp32 guard does not prove
+// sign(Q), s = sign(x) sign(q(x)) is decided exactly (0 at x == 0) and sv and
+// dX are recomputed with it.  Bit for bit equal to backward_element wherever
+// the guard holds.
+template <int M, int N, int K>
+__device__ static inline ElemBwd exact_element(const Pow<K> &X, float dy, const BwdCoefs<M, N> &k) {
+    ElemBwd e = backward_element<M, N, K>(X, dy, k);
+    if constexpr (N > 0) {
+        if (!e.sure) {
+            const float x = X.p[1];
+            const int s = (x == 0.0f || k.q_zero) ? 0 : sign_q_exact<M, N>(x, k) * ((x > 0.0f) ? 1 : -1);
+            e.sv = (s == 0) ? 0.0f : ((s > 0) ? e.v : -e.v);
+            e.dx = fmaf(-e.sv, e.Qd, e.wPd);
+            e.sure = true;
+        }
+    }
+    return e;
 }
 
 }  // namespace grkan

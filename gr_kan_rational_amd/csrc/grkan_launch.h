@@ -6,33 +6,64 @@
 #include <stdint.h>
 
 #include "grkan.h"
+#include "grkan_fastdiv.h"
 
 namespace grkan {
 
-// Geometry of one launch over a [rows][d] tensor split into n_groups groups.
-// The tensor is cut into tiles of unroll * rows_per_iter rows; one workgroup
-// handles one (tile, group) pair: its `lanes` threads cover rows_per_iter
-// rows x the group's seg_vecs 16-byte vectors, `unroll` times over.  The
-// block is `lanes` rounded up to whole waves (the extra lanes idle).
-struct Geometry {
+// Launch plan of one pass over a [rows][d] tensor split into n_groups groups
+// of d_g = d / n_groups contiguous channels, where a group's row segment is a
+// whole number of 16-byte vectors (seg_vecs of them).
+//
+// A segment is cut into `parts` column parts of at most part_vecs vectors (one
+// part unless the segment is wider than the kernel's target block).  The rows
+// are cut into tiles of unroll x rows_per_iter rows.  One workgroup handles
+// one (tile, group, part): a 2D block of part_vecs x rows_per_iter lanes, each
+// lane one 16-byte vector column of its part, `unroll` rows apart.
+//
+// Grid: one dimension, 8 * parts * n_groups workgroups per bundle of 8 row
+// tiles.  Workgroup b takes tile 8 (b / (8 parts n_groups)) + (b mod 8), and
+// (group, part) from (b / 8) mod (parts n_groups), group-major.  The
+// dispatcher deals workgroups to the 8 XCDs round-robin, so XCD (b mod 8)
+// takes whole row tiles.  (A 3D grid with the same linear order measured
+// ~2% slower on MI355X.)  Grids too large for one launch are split into
+// launches of whole bundles.
+struct Plan {
     int64_t rows;
-    int64_t row_vecs;       // 16-byte vectors per row (d * bytes / 16)
-    int32_t seg_vecs;       // 16-byte vectors per group per row
-    int32_t rows_per_iter;  // rows covered by one pass of a workgroup's lanes
-    int32_t lanes;          // rows_per_iter * seg_vecs
-    int32_t block;          // lanes rounded up to a multiple of 64
+    int64_t d;
     int32_t n_groups;
+    int32_t m, n;           // numerator / denominator degree
+    int32_t es;             // bytes per I/O element
+    int64_t row_bytes;      // d * es
+    int64_t seg_bytes;      // d_g * es
+    int32_t seg_vecs;       // 16-byte vectors per group row segment
+    int32_t parts;          // column parts per segment
+    int32_t part_vecs;      // vectors per part (the last part may be ragged)
+    int32_t rows_per_iter;  // rows covered by one pass of a workgroup's lanes
     int32_t unroll;         // passes per tile
+    int32_t block;          // part_vecs * rows_per_iter threads
     int64_t tiles;          // ceil(rows / (unroll * rows_per_iter))
-    int64_t grid;           // 8 * n_groups * ceil(tiles / 8)
+    int64_t bundles;        // ceil(tiles / 8)
+    int32_t ncoef;          // m + 1 + n gradient sums per group
+    int64_t bundles_per_launch;
+    FastDiv div_gp;         // division by parts * n_groups
+    FastDiv div_parts;      // division by parts
 };
+
+// Workgroups of a plan (padding workgroups of the last bundle included).
+__host__ __device__ inline int64_t plan_grid(const Plan &P) { return 8 * (int64_t)P.parts * P.n_groups * P.bundles; }
+
+// Partial-sum slots of the deterministic backward: one per (part, tile),
+// [parts][8 * bundles]; within a part, tile t sits at slot
+// (t mod 8) * bundles + t / 8, so the tiles of one XCD are adjacent.
+__host__ __device__ inline int64_t plan_slots(const Plan &P) { return (int64_t)P.parts * 8 * P.bundles; }
 
 struct FwdArgs {
     const void *x;
     void *y;
     const float *A;
     const float *B;
-    Geometry geo;
+    Plan plan;
+    int64_t bundle0;  // first bundle of this launch
 };
 
 enum BwdMode : int32_t { kModeAtomic = 0, kModePartials = 1 };
@@ -45,26 +76,39 @@ struct BwdArgs {
     const float *B;
     float *dA;
     float *dB;
-    float *partials;  // [n_groups][10][8 * ceil(tiles / 8)] in kModePartials
+    float *partials;  // [n_groups][ncoef][plan_slots] in kModePartials
     int32_t mode;
-    Geometry geo;
+    Plan plan;
+    int64_t bundle0;
 };
 
-// Passes per workgroup and target workgroup size of a kernel (pass 0 =
-// forward, 1 = backward; the backward's atomic mode has its own block size).
-int unroll(grkan_dtype_t io, int pass);
-int target_block(grkan_dtype_t io, int pass, bool atomic_mode);
+// Kernels of one degree pair, defined in grkan_kernels.hip (compiled once per
+// supported pair).  pass 0 = forward, 1 = backward.
+template <int M, int N> struct Kernels {
+    static int unroll(grkan_dtype_t io, int pass);
+    static int target_block(grkan_dtype_t io, int pass, bool atomic_mode);
+    static hipError_t forward(grkan_dtype_t io, const FwdArgs &a, dim3 grid, hipStream_t s);
+    static hipError_t backward(grkan_dtype_t io, const BwdArgs &a, dim3 grid, hipStream_t s);
+    static hipError_t occupancy(grkan_dtype_t io, int pass, int block, int *blocks_per_cu);
+};
 
-hipError_t launch_forward(grkan_dtype_t io, const FwdArgs &a, hipStream_t s);
-hipError_t launch_backward(grkan_dtype_t io, const BwdArgs &a, hipStream_t s);
-hipError_t launch_merge(const float *partials, int32_t n_groups, int64_t tiles, float *dA,
+// Degree pairs compiled into the library: (m, n) with a_0..a_m, b_1..b_n.
+// GR-KAN's (5, 4) first.
+#define GRKAN_FOR_EACH_DEGREE(X) X(5, 4) X(3, 2) X(4, 3) X(6, 5) X(7, 6) X(2, 1) X(4, 4) X(5, 0)
+
+// Degree-independent kernels (grkan_merge.hip).  The merge adds each
+// (group, coefficient)'s partials in chunks of 8192 slots; with more than one
+// chunk it needs merge_chunks(slots) fp64 chunk sums per (group,
+// coefficient) of scratch, after the partials in the workspace.
+uint32_t merge_chunks(int64_t slots);
+hipError_t launch_merge(const float *partials, double *chunk_sums, int32_t n_groups, int32_t m,
+                        int32_t n, int64_t tiles, int64_t bundles, int32_t parts, float *dA,
                         float *dB, hipStream_t s);
-hipError_t launch_zero(float *dA, float *dB, int32_t n_groups, hipStream_t s);
+hipError_t launch_zero(float *dA, float *dB, int64_t na, int64_t nb, hipStream_t s);
+
+// Per-element-atomic baseline, GR-KAN degrees only (grkan_naive.hip).
 hipError_t launch_naive(grkan_dtype_t io, const void *x, const void *dy, void *dx, const float *A,
                         const float *B, float *dA, float *dB, int64_t rows, int64_t d,
                         int32_t n_groups, hipStream_t s);
-
-// Resident workgroups per CU for the kernel of (io, pass) at this block size.
-hipError_t occupancy(grkan_dtype_t io, int pass, int block, int *blocks_per_cu);
 
 }  // namespace grkan

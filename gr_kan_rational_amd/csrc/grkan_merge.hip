@@ -1,0 +1,129 @@
+// grkan_merge.hip -- degree-independent kernels of the backward pass: the
+// fixed-order merge of the per-tile partial sums, and zeroing of dA / dB for
+// the atomic schemes.
+//
+// Pages cited
+//   [PolyKAN]  "PolyKAN: Efficient Fused GPU Operators for Polynomial
+//              Kolmogorov-Arnold Network Variants", abstract page
+//              (arXiv 2511.14852): a two-stage reduction of the coefficient
+//              gradients in place of atomics.
+#include "grkan_launch.h"
+
+namespace grkan {
+
+namespace {
+
+// Second stage of the deterministic backward: the partials of group g,
+// coefficient k -- one per (column part, row tile) -- are added in a fixed
+// order in fp64.  Workgroup (g, k, c) takes the c-th chunk of kMergeChunk
+// slots; each thread issues all of its loads before adding, so a chunk costs
+// about one memory round trip.  With one chunk per (g, k) (up to 8192 slots:
+// GR-KAN's 8 groups at KAT-B) the workgroup writes dA / dB directly;
+// otherwise (few groups, many tiles) it writes an fp64 chunk sum and
+// grkan_merge_chunks_kernel adds the chunk sums in order.  Slots are
+// [parts][8 * bundles]; within a part, slot r = (t mod 8) * bundles + t / 8
+// holds tile t, and the slots of tiles past the end hold nothing.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeLoads = 8;
+constexpr uint32_t kMergeChunk = (uint32_t)kMergeThreads * kMergeLoads;
+
+__device__ static inline void write_sum(int gk, int32_t na, int32_t nb, double total, float *dA,
+                                        float *dB) {
+    const int nc = na + nb;
+    const int g = gk / nc, k = gk % nc;
+    if (k < na) dA[g * na + k] = (float)total;
+    else dB[g * nb + k - na] = (float)total;
+}
+
+// fp64 sum over the workgroup of one value per thread, in a fixed order.
+template <int T>
+__device__ static inline double block_sum(double s) {
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask, 64);
+    __shared__ double lds[T / 64];
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = s;
+    __syncthreads();
+    double total = 0.0;
+    if (threadIdx.x == 0)
+        for (int w = 0; w < T / 64; ++w) total += lds[w];
+    return total;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void grkan_merge_kernel(
+    const float *__restrict__ partials, uint32_t tiles, uint32_t bundles, uint32_t slots,
+    int32_t na, int32_t nb, uint32_t chunks, double *__restrict__ chunk_sums,
+    float *__restrict__ dA, float *__restrict__ dB) {
+    const int gk = (int)blockIdx.x;
+    const uint32_t c = blockIdx.y;
+    const uint32_t per_part = 8u * bundles;
+    const float *p = partials + (int64_t)gk * slots;
+    float v[kMergeLoads];
+#pragma unroll
+    for (int i = 0; i < kMergeLoads; ++i) {
+        const uint32_t q = c * kMergeChunk + (uint32_t)i * kMergeThreads + threadIdx.x;
+        const uint32_t r = q % per_part;
+        const uint32_t tile = (r % bundles) * 8u + r / bundles;
+        v[i] = (q < slots && tile < tiles) ? p[q] : 0.0f;
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < kMergeLoads; ++i) s += (double)v[i];
+    const double total = block_sum<kMergeThreads>(s);
+    if (threadIdx.x == 0) {
+        if (chunks == 1) write_sum(gk, na, nb, total, dA, dB);
+        else chunk_sums[(int64_t)gk * chunks + c] = total;
+    }
+}
+
+constexpr int kChunkThreads = 256;
+
+__global__ __launch_bounds__(kChunkThreads) void grkan_merge_chunks_kernel(
+    const double *__restrict__ chunk_sums, uint32_t chunks, int32_t na, int32_t nb,
+    float *__restrict__ dA, float *__restrict__ dB) {
+    const int gk = (int)blockIdx.x;
+    const double *p = chunk_sums + (int64_t)gk * chunks;
+    double s = 0.0;
+    for (uint32_t c = threadIdx.x; c < chunks; c += kChunkThreads) s += p[c];
+    const double total = block_sum<kChunkThreads>(s);
+    if (threadIdx.x == 0) write_sum(gk, na, nb, total, dA, dB);
+}
+
+__global__ __launch_bounds__(256) void grkan_zero_kernel(float *__restrict__ dA, float *__restrict__ dB,
+                                                         int64_t na, int64_t nb) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < na) dA[i] = 0.0f;
+    if (i < nb) dB[i] = 0.0f;
+}
+
+}  // namespace
+
+uint32_t merge_chunks(int64_t slots) {
+    return (uint32_t)((slots + kMergeChunk - 1) / kMergeChunk);
+}
+
+hipError_t launch_merge(const float *partials, double *chunk_sums, int32_t n_groups, int32_t m,
+                        int32_t n, int64_t tiles, int64_t bundles, int32_t parts, float *dA,
+                        float *dB, hipStream_t s) {
+    const int32_t na = m + 1, nc = m + 1 + n;
+    const int64_t slots = (int64_t)parts * 8 * bundles;
+    const uint32_t chunks = merge_chunks(slots);
+    hipLaunchKernelGGL(grkan_merge_kernel, dim3((unsigned)(n_groups * nc), chunks), dim3(kMergeThreads), 0,
+                       s, partials, (uint32_t)tiles, (uint32_t)bundles, (uint32_t)slots, na, n, chunks,
+                       chunk_sums, dA, dB);
+    if (chunks == 1) return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(grkan_merge_chunks_kernel, dim3((unsigned)(n_groups * nc)), dim3(kChunkThreads), 0,
+                       s, chunk_sums, chunks, na, n, dA, dB);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero(float *dA, float *dB, int64_t na, int64_t nb, hipStream_t s) {
+    const int64_t n = na > nb ? na : nb;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(grkan_zero_kernel, dim3((unsigned)(blocks > 0 ? blocks : 1)), dim3(256), 0, s,
+                       dA, dB, na, nb);
+    return hipGetLastError();
+}
+
+}  // namespace grkan

@@ -33,6 +33,9 @@ template <> struct Scalar<bf16io> {
     }
 };
 
+constexpr int kM = 5, kN = 4;  // GR-KAN's degrees
+constexpr int kNumA = kM + 1, kNumB = kN, kNumCoef = kM + 1 + kN;
+
 template <class IO>
 __global__ __launch_bounds__(256) void grkan_bwd_naive_kernel(const void *x, const void *dy, void *dx,
                                                               const float *A, const float *B,
@@ -41,16 +44,15 @@ __global__ __launch_bounds__(256) void grkan_bwd_naive_kernel(const void *x, con
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         const int g = (int)((i % d) / d_g);
-        const BwdCoefs k = derive(load_coefs(A, B, g));
+        const BwdCoefs<kM, kN> k = derive<kM, kN>(load_coefs<kM, kN>(A, B, g));
         float acc[kNumCoef];
 #pragma unroll
         for (int c = 0; c < kNumCoef; ++c) acc[c] = 0.0f;
         const float xv = Scalar<IO>::load(x, i), dyv = Scalar<IO>::load(dy, i);
-        const float x2 = xv * xv, x3 = x2 * xv, x4 = x2 * x2, x5 = x4 * xv;
-        const ElemBwd e = backward_element(xv, x2, x3, x4, x5, dyv, k);
-        accumulate(e.w, e.sv, xv, x2, x3, x4, x5, acc);
-        const float dxv = e.sure ? e.dx : exact_fix(xv, dyv, k, acc);
-        Scalar<IO>::store(dx, i, dxv);
+        const Pow<kM> X(xv);
+        const ElemBwd e = exact_element<kM, kN, kM>(X, dyv, k);
+        accumulate<kM, kN>(e.w, e.sv, X, acc);
+        Scalar<IO>::store(dx, i, e.dx);
 #pragma unroll
         for (int c = 0; c < kNumA; ++c) unsafeAtomicAdd(dA + g * kNumA + c, acc[c]);
 #pragma unroll

@@ -38,6 +38,18 @@
  *     Faults inside a kernel surface at the caller's next synchronisation.
  *   - Arguments are validated before any HIP call; an invalid call changes
  *     nothing on the device.  No C++ exception crosses this interface.
+ *
+ * The PAU family.  The pages note that the same kernel restructuring applies
+ * to PAU and its variants ([FlashKAT notes], section "局限性与未来工作"): the
+ * safe rational unit with other numerator / denominator degrees (m, n),
+ *
+ *     F_g(x) = (a_g0 + ... + a_gm x^m) / (1 + |b_g1 x + ... + b_gn x^n|),
+ *
+ * with A [n_groups][m+1], B [n_groups][n] and m + 1 + n gradient sums per
+ * group; n = 0 is a plain polynomial (B, dB unused and may be NULL), and
+ * n_groups = 1 is a single PAU shared by all channels.  The grkan_pau_*
+ * entry points take (m, n) explicitly; the grkan_* ones are GR-KAN's
+ * (m, n) = (5, 4).  grkan_pau_supported() says which pairs are compiled in.
  */
 #ifndef GRKAN_H
 #define GRKAN_H
@@ -57,8 +69,8 @@ extern "C" {
 typedef enum {
     GRKAN_OK = 0,
     GRKAN_ERR_INVALID_ARG = 1, /* null pointer, bad shape, overlap, small workspace, bad flags */
-    GRKAN_ERR_UNSUPPORTED = 2, /* misaligned pointer, d/n_groups*bytes(io) not a multiple of 16
-                                  or above 16 KiB                                               */
+    GRKAN_ERR_UNSUPPORTED = 2, /* misaligned pointer, d/n_groups*bytes(io) not a multiple of 16,
+                                  more than 65535 groups, a degree pair not compiled in        */
     GRKAN_ERR_HIP = 3          /* the HIP runtime reported an error on query or launch          */
 } grkan_status_t;
 
@@ -127,20 +139,55 @@ GRKAN_API size_t grkan_backward_workspace_size(int64_t rows, int64_t d, int32_t 
 GRKAN_API const char *grkan_status_string(grkan_status_t status);
 
 /* Launch geometry of a pass (0 = forward, 1 = backward, 2 = backward with
- * GRKAN_BLOCK_ATOMIC).  The geometry is a function of the shape and dtype;
- * cus and blocks_per_cu describe the current device (queried on first use). */
+ * GRKAN_BLOCK_ATOMIC).  The geometry is a function of the shape, dtype and
+ * degrees; cus and blocks_per_cu describe the current device (queried on
+ * first use). */
 typedef struct {
-    int32_t block;          /* threads per workgroup                                  */
+    int32_t block;          /* threads per workgroup (part_vecs * rows_per_iter)      */
     int32_t rows_per_iter;  /* rows a workgroup's lanes cover in one pass             */
     int32_t unroll;         /* passes per workgroup (loads issued together)           */
     int64_t tiles;          /* row tiles (unroll * rows_per_iter rows each)           */
-    int64_t grid;           /* workgroups: one per (tile, group), padded to 8 tiles   */
+    int64_t grid;           /* workgroups: one per (tile, group, part), padded to 8
+                               tiles                                                  */
     int32_t cus;            /* compute units on the device                            */
     int32_t blocks_per_cu;  /* resident workgroups per CU for this kernel             */
+    int32_t parts;          /* column parts per group row segment                     */
+    int32_t part_vecs;      /* 16-byte vectors per part                               */
 } grkan_launch_t;
 
 GRKAN_API grkan_status_t grkan_query_launch(int64_t rows, int64_t d, int32_t n_groups,
                                   grkan_dtype_t io, int32_t pass, grkan_launch_t *out);
+
+/* 1 if the degree pair (m, n) is compiled into this library, else 0.
+ * Host-only. */
+GRKAN_API int grkan_pau_supported(int32_t m, int32_t n);
+
+/* grkan_forward for degrees (m, n): A [n_groups][m+1], B [n_groups][n]
+ * (B may be NULL when n == 0).  Pairs not compiled in return
+ * GRKAN_ERR_UNSUPPORTED, negative degrees GRKAN_ERR_INVALID_ARG. */
+GRKAN_API grkan_status_t grkan_pau_forward(const void *x, void *y, const float *A, const float *B,
+                                 int64_t rows, int64_t d, int32_t n_groups, int32_t m,
+                                 int32_t n, grkan_dtype_t io, hipStream_t stream);
+
+/* grkan_backward for degrees (m, n): dA [n_groups][m+1], dB [n_groups][n]
+ * (B and dB may be NULL when n == 0).  GRKAN_NAIVE_ATOMIC exists for
+ * (5, 4) only (GRKAN_ERR_UNSUPPORTED otherwise). */
+GRKAN_API grkan_status_t grkan_pau_backward(const void *x, const void *dy, const float *A,
+                                  const float *B, void *dx, float *dA, float *dB,
+                                  int64_t rows, int64_t d, int32_t n_groups, int32_t m,
+                                  int32_t n, grkan_dtype_t io, uint32_t flags,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes for grkan_pau_backward (0 when none is needed or the
+ * arguments would be rejected).  Host-only. */
+GRKAN_API size_t grkan_pau_backward_workspace_size(int64_t rows, int64_t d, int32_t n_groups,
+                                         int32_t m, int32_t n, grkan_dtype_t io,
+                                         uint32_t flags);
+
+/* grkan_query_launch for degrees (m, n). */
+GRKAN_API grkan_status_t grkan_pau_query_launch(int64_t rows, int64_t d, int32_t n_groups,
+                                      int32_t m, int32_t n, grkan_dtype_t io, int32_t pass,
+                                      grkan_launch_t *out);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,9 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "grkan_forward", "grkan_backward", "grkan_backward_workspace_size",
-        "grkan_status_string", "grkan_query_launch"])
+        "grkan_status_string", "grkan_query_launch",
+        "grkan_pau_supported", "grkan_pau_forward", "grkan_pau_backward",
+        "grkan_pau_backward_workspace_size", "grkan_pau_query_launch"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -58,10 +60,11 @@ def ws(lib, rows, d, n_g, io=F32, flags=DEFAULT):
 def test_workspace_size(lib):
     # KAT-B backward: 96 channels x 4 B = 24 vectors per group row; 8 rows x 24 = 192 lanes per
     # pass, 4 passes -> 32-row tiles; ceil(201728 / 32) = 6304 tiles; one fp32 partial per
-    # (group, coefficient, tile), slots rounded up to a multiple of 8 tiles.
+    # (group, coefficient, tile), slots rounded up to a multiple of 8 tiles.  Above 8192 slots
+    # the merge adds them in chunks and needs one fp64 chunk sum per (group, coefficient, chunk).
     assert ws(lib, 201728, 768, 8) == 8 * 10 * 6304 * 4
     assert ws(lib, 16, 32, 8) == 8 * 10 * 8 * 4             # tiny: a single tile, 8 slots
-    assert ws(lib, 201728, 3072, 8, io=BF16) == 8 * 10 * 25216 * 4  # 48 vectors: 4 rows x 2 passes
+    assert ws(lib, 201728, 3072, 8, io=BF16) == 8 * 10 * 25216 * 4 + 8 * 10 * 4 * 8  # 4 rows x 2 passes
     assert ws(lib, 1000, 768, 8) == 8 * 10 * 32 * 4         # 32 tiles of 32 rows (the last ragged)
     assert ws(lib, 1025, 768, 8) == 8 * 10 * 40 * 4         # 33 tiles -> 40 slots
     assert ws(lib, 201728, 768, 8, flags=BLOCK) == 0        # atomic modes need none
@@ -90,7 +93,7 @@ def bwd(lib, x=P, dy=P + 0x100000, A=P + 0x200000, B=P + 0x300000, dx=P + 0x4000
     (dict(io=7), INVALID),
     (dict(x=P + 4), UNSUPPORTED), (dict(y=P + 0x100008), UNSUPPORTED), (dict(A=P + 0x200002), UNSUPPORTED),
     (dict(d=40), UNSUPPORTED),                       # d_g = 5 fp32 = 20 bytes per group row
-    (dict(d=8 * 4104, n_g=8), UNSUPPORTED),           # 16416 bytes per group row > 16 KiB
+    (dict(d=65536 * 4, n_g=65536), UNSUPPORTED),      # more groups than a grid dimension holds
     (dict(y=P + 16), INVALID),                       # partial overlap of y and x
     (dict(y=P + 0x200000 - 16), INVALID),             # y runs into A
 ])
@@ -127,3 +130,62 @@ def test_backward_atomic_mode_needs_no_workspace(lib):
     if torch.cuda.is_available():
         pytest.skip("only meaningful without a GPU")
     assert bwd(lib, flags=BLOCK, ws_ptr=None, ws_bytes=0) == HIPERR
+
+
+# ---------------------------------------------------------------- PAU family
+
+PAIRS = [(5, 4), (3, 2), (4, 3), (6, 5), (7, 6), (2, 1), (4, 4), (5, 0)]
+
+
+def test_pau_supported_pairs(lib):
+    for m, n in PAIRS:
+        assert lib.grkan_pau_supported(m, n) == 1, (m, n)
+    for m, n in ((5, 3), (9, 9), (0, 0), (-1, 4), (8, 7)):
+        assert lib.grkan_pau_supported(m, n) == 0, (m, n)
+
+
+def pws(lib, rows, d, n_g, m, n, io=F32, flags=DEFAULT):
+    return lib.grkan_pau_backward_workspace_size(rows, d, n_g, m, n, io, flags)
+
+
+def test_pau_workspace_size(lib):
+    # One fp32 partial per (group, coefficient, part, tile); m + 1 + n coefficients.
+    assert pws(lib, 201728, 768, 8, 5, 4) == ws(lib, 201728, 768, 8)
+    assert pws(lib, 201728, 768, 8, 3, 2) == 8 * 6 * 6304 * 4     # 4 passes of 8 rows: 32-row tiles
+    assert pws(lib, 201728, 768, 8, 7, 6) == 8 * 14 * 12608 * 4 + 8 * 14 * 2 * 8  # 16-row tiles
+    assert pws(lib, 201728, 768, 8, 5, 0) == 8 * 6 * 6304 * 4     # polynomial: no dB sums
+    # n_groups = 1 (one PAU for all channels): a 192-vector segment, one row per pass, 4-row tiles
+    assert pws(lib, 201728, 768, 1, 5, 4) == 1 * 10 * 50432 * 4 + 1 * 10 * 7 * 8
+    # a 768-vector segment is cut into 4 parts of 192 vectors
+    assert pws(lib, 201728, 3072, 1, 5, 4) == 1 * 10 * 4 * 50432 * 4 + 1 * 10 * 25 * 8
+    # 1026 vectors per segment (16416 bytes): 6 parts of 171
+    assert pws(lib, 4, 8 * 4104, 8, 5, 4) == 8 * 10 * 6 * 8 * 4
+    assert pws(lib, 100, 768, 8, 5, 3) == 0                        # pair not compiled in
+    assert pws(lib, 100, 768, 8, 3, 2, flags=BLOCK) == 0
+
+
+def pfwd(lib, m, n, x=P, y=P + 0x100000, A=P + 0x200000, B=P + 0x300000, rows=4, d=64, n_g=8, io=F32):
+    return lib.grkan_pau_forward(x, y, A, B, rows, d, n_g, m, n, io, None)
+
+
+def pbwd(lib, m, n, x=P, dy=P + 0x100000, A=P + 0x200000, B=P + 0x300000, dx=P + 0x400000,
+         dA=P + 0x500000, dB=P + 0x600000, rows=4, d=64, n_g=8, io=F32, flags=DEFAULT,
+         ws_ptr=P + 0x700000, ws_bytes=1 << 20):
+    return lib.grkan_pau_backward(x, dy, A, B, dx, dA, dB, rows, d, n_g, m, n, io, flags, ws_ptr,
+                                  ws_bytes, None)
+
+
+@pytest.mark.parametrize("m,n,code", [((5), 3, UNSUPPORTED), (9, 9, UNSUPPORTED), (-1, 2, INVALID),
+                                      (3, -2, INVALID)])
+def test_pau_rejects_degrees(lib, m, n, code):
+    assert pfwd(lib, m, n) == code
+    assert pbwd(lib, m, n) == code
+
+
+def test_pau_rejects_before_any_device_call(lib):
+    assert pfwd(lib, 3, 2, B=None) == INVALID                      # n > 0 needs B
+    assert pbwd(lib, 3, 2, dB=None) == INVALID
+    assert pbwd(lib, 3, 2, flags=NAIVE) == UNSUPPORTED             # naive baseline: GR-KAN only
+    assert pbwd(lib, 7, 6, dA=P + 0x600000 - 8 * 8 * 4 + 8) == INVALID  # dA [8][8] runs into dB
+    # n = 0: B and dB may be NULL; rows == 0 returns before any HIP call
+    assert pfwd(lib, 5, 0, x=None, y=None, B=None, rows=0) == OK

@@ -78,8 +78,8 @@ def test_parity_reduced(gk, name, mode):
     n_add = atomic_adds(gk, w) if mode == "block_atomic" else 0
     parity.check_elem(f"{name} Y", to_host(y, w.io), ref["y"], ref["ymag"], w.io)
     parity.check_elem(f"{name} dX", to_host(dx, w.io), ref["dx"], ref["dxmag"], w.io)
-    parity.check_sums(f"{name} dA", dA.cpu().numpy(), ref["dA"], ref["nA"], n_add)
-    parity.check_sums(f"{name} dB", dB.cpu().numpy(), ref["dB"], ref["nB"], n_add)
+    parity.check_sums(f"{name} dA", dA.cpu().numpy(), ref["dA"], ref["nA"], n_add, ref["mA"])
+    parity.check_sums(f"{name} dB", dB.cpu().numpy(), ref["dB"], ref["nB"], n_add, ref["mB"])
 
 
 def sample_indices(w, n_random=200_000, seed=0):
@@ -113,11 +113,11 @@ def test_parity_full_size(gk, name):
     parity.check_elem(f"{name} Y[sampled]", ys, rec[:, orc.F], rec[:, orc.FMAG], w.io)
     parity.check_elem(f"{name} dX[sampled]", dxs, rec[:, orc.DX], rec[:, orc.DXMAG], w.io)
     ref = orc.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io, elements=False)
-    sa = parity.check_sums(f"{name} dA", dA.cpu().numpy(), ref["dA"], ref["nA"])
-    sb = parity.check_sums(f"{name} dB", dB.cpu().numpy(), ref["dB"], ref["nB"])
+    sa = parity.check_sums(f"{name} dA", dA.cpu().numpy(), ref["dA"], ref["nA"], mag=ref["mA"])
+    sb = parity.check_sums(f"{name} dB", dB.cpu().numpy(), ref["dB"], ref["nB"], mag=ref["mB"])
     n_add = atomic_adds(gk, w)
-    ta = parity.check_sums(f"{name} dA block_atomic", dA_at.cpu().numpy(), ref["dA"], ref["nA"], n_add)
-    tb = parity.check_sums(f"{name} dB block_atomic", dB_at.cpu().numpy(), ref["dB"], ref["nB"], n_add)
+    ta = parity.check_sums(f"{name} dA block_atomic", dA_at.cpu().numpy(), ref["dA"], ref["nA"], n_add, ref["mA"])
+    tb = parity.check_sums(f"{name} dB block_atomic", dB_at.cpu().numpy(), ref["dB"], ref["nB"], n_add, ref["mB"])
     log(f"[parity_full] {name}: ok dA {sa} dB {sb}; block_atomic dA {ta} dB {tb}")
     golden = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", f"{name}.sums.json")
     if os.path.exists(golden):
@@ -172,8 +172,8 @@ def test_special_values(gk):
         ref = orc.run(x, A, B, 8, dy=dy)
         parity.check_elem("special Y", y.cpu().numpy(), ref["y"], ref["ymag"])
         parity.check_elem("special dX", dx.cpu().numpy(), ref["dx"], ref["dxmag"])
-        parity.check_sums("special dA", dA.cpu().numpy(), ref["dA"], ref["nA"])
-        parity.check_sums("special dB", dB.cpu().numpy(), ref["dB"], ref["nB"])
+        parity.check_sums("special dA", dA.cpu().numpy(), ref["dA"], ref["nA"], mag=ref["mA"])
+        parity.check_sums("special dB", dB.cpu().numpy(), ref["dB"], ref["nB"], mag=ref["mB"])
         # the exact-sign cases: dX at the roots must take s from the exact Q, not from fp32 noise
         assert np.all(dB.cpu().numpy()[:2] == 0)
 
@@ -190,7 +190,7 @@ def test_identity_is_exact(gk):
     assert torch.all(dB == 0)
     A_id = np.tile(np.array([0, 1, 0, 0, 0, 0], np.float32), (8, 1))
     ref = orc.run(inp["x"], A_id, np.zeros((8, 4), np.float32), 8, dy=inp["dy"], elements=False)
-    parity.check_sums("identity dA", dA.cpu().numpy(), ref["dA"], ref["nA"])
+    parity.check_sums("identity dA", dA.cpu().numpy(), ref["dA"], ref["nA"], mag=ref["mA"])
 
 
 def test_deterministic_mode_is_bitwise_stable_and_linear(gk):
