@@ -33,12 +33,13 @@ struct DegreeOps {
     int (*target_block)(grkan_dtype_t, int, bool);
     hipError_t (*forward)(grkan_dtype_t, const FwdArgs &, dim3, hipStream_t);
     hipError_t (*backward)(grkan_dtype_t, const BwdArgs &, dim3, hipStream_t);
-    hipError_t (*occupancy)(grkan_dtype_t, int, int, int *);
+    hipError_t (*occupancy)(grkan_dtype_t, int, int, int *, bool);
+    void (*narrow_shape)(grkan_dtype_t, int, int *, int *, int *);
 };
 
 #define GRKAN_DEGREE_ENTRY(M, N)                                                                \
     {M, N, &Kernels<M, N>::unroll, &Kernels<M, N>::target_block, &Kernels<M, N>::forward,      \
-     &Kernels<M, N>::backward, &Kernels<M, N>::occupancy},
+     &Kernels<M, N>::backward, &Kernels<M, N>::occupancy, &Kernels<M, N>::narrow_shape},
 const DegreeOps kDegrees[] = {GRKAN_FOR_EACH_DEGREE(GRKAN_DEGREE_ENTRY)};
 #undef GRKAN_DEGREE_ENTRY
 
@@ -70,6 +71,53 @@ constexpr int kMaxBlockThreads = 1024;
 constexpr int64_t kMaxGroups = 65535;
 constexpr int64_t kMaxLaneSpan = int64_t(1) << 31;  // bytes a workgroup's lanes may span
 
+// Plan for groups whose row segment is not a whole number of 16-byte vectors:
+// one channel column per lane, 64 columns per workgroup, long row tiles.
+grkan_status_t plan_narrow(int64_t rows, int64_t d, int32_t n_groups, const DegreeOps &deg,
+                           grkan_dtype_t io, int pass, Plan *P) {
+    const int es = io_bytes(io);
+    const int64_t row_bytes = d * es;
+    if (d >= (int64_t(1) << 31)) return GRKAN_ERR_UNSUPPORTED;
+    int rl = 0, u = 0, it = 0;
+    deg.narrow_shape(io, pass, &rl, &u, &it);
+    const int64_t tile_rows = (int64_t)rl * u * it;
+    if (tile_rows * row_bytes > kMaxLaneSpan) return GRKAN_ERR_UNSUPPORTED;
+    *P = Plan{};
+    P->kind = kNarrow;
+    P->rows = rows;
+    P->d = d;
+    P->n_groups = n_groups;
+    P->m = deg.m;
+    P->n = deg.n;
+    P->es = es;
+    P->row_bytes = row_bytes;
+    P->seg_bytes = (d / n_groups) * es;
+    P->row_words = d;
+    P->cpb = 64;
+    P->ncb = (int32_t)((d + 63) / 64);
+    P->d_g = (int32_t)(d / n_groups);
+    // the most column blocks a run of d_g consecutive channels can touch
+    P->parts = (int32_t)((P->d_g - 1 + P->cpb - 1) / P->cpb + 1);
+    P->part_vecs = 64;
+    P->rows_per_iter = rl;
+    P->row_lanes = rl;
+    P->unroll = u;
+    P->iters = it;
+    P->block = 64 * rl;
+    P->tiles = (rows + tile_rows - 1) / tile_rows;
+    P->bundles = (P->tiles + 7) / 8;
+    P->ncoef = deg.m + 1 + deg.n;
+    if (plan_slots(*P) > (int64_t)65535 * 8192) return GRKAN_ERR_UNSUPPORTED;
+    int64_t tpl = (int64_t(1) << 31) / P->ncb;
+    const int64_t by_items = ((int64_t(1) << 32) - 1) / ((int64_t)P->ncb * P->block);
+    if (by_items < tpl) tpl = by_items;
+    if (tpl < 1) return GRKAN_ERR_UNSUPPORTED;
+    P->tiles_per_launch = tpl;
+    P->div_ncb = make_fastdiv((uint32_t)P->ncb);
+    P->div_dg = make_fastdiv((uint32_t)P->d_g);
+    return GRKAN_OK;
+}
+
 // Shape checks and the launch plan (a function of the shape, dtype and degrees).
 grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, const DegreeOps &deg,
                           grkan_dtype_t io, int pass, bool atomic_mode, Plan *P) {
@@ -78,7 +126,7 @@ grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, const Degre
     const int es = io_bytes(io);
     if (d > INT64_MAX / es || (rows > 0 && rows > INT64_MAX / (d * es))) return GRKAN_ERR_INVALID_ARG;
     const int64_t seg_bytes = (d / n_groups) * es;
-    if (seg_bytes % 16 != 0) return GRKAN_ERR_UNSUPPORTED;
+    if (seg_bytes % 16 != 0) return plan_narrow(rows, d, n_groups, deg, io, pass, P);
     if (n_groups > kMaxGroups) return GRKAN_ERR_UNSUPPORTED;
     const int64_t seg_vecs = seg_bytes / 16;
     const int64_t row_bytes = d * es;
@@ -105,6 +153,8 @@ grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, const Degre
     }
     const int u = deg.unroll(io, pass);
     if ((int64_t)u * rpi * row_bytes > kMaxLaneSpan) return GRKAN_ERR_UNSUPPORTED;
+    *P = Plan{};
+    P->kind = kSegment;
     P->rows = rows;
     P->d = d;
     P->n_groups = n_groups;
@@ -158,8 +208,16 @@ int g_cus[kMaxDev];
 
 grkan_status_t from_hip(hipError_t e) { return e == hipSuccess ? GRKAN_OK : GRKAN_ERR_HIP; }
 
-// Grid of one launch covering bundles [b0, b0 + nz).
+// Launches cover whole bundles of 8 tiles (segment plans) or whole tiles
+// (narrow plans).
+int64_t launch_units(const Plan &P) { return P.kind == kNarrow ? P.tiles : P.bundles; }
+int64_t units_per_launch(const Plan &P) {
+    return P.kind == kNarrow ? P.tiles_per_launch : P.bundles_per_launch;
+}
+
+// Grid of one launch covering nz units.
 dim3 grid_of(const Plan &P, int64_t nz) {
+    if (P.kind == kNarrow) return dim3((unsigned)(P.ncb * nz));
     return dim3((unsigned)(8 * (int64_t)P.parts * P.n_groups * nz));
 }
 
@@ -182,8 +240,8 @@ grkan_status_t forward_impl(const void *x, void *y, const float *A, const float 
     if (overlap(y, bytes, A, ab) || overlap(y, bytes, B, bb)) return GRKAN_ERR_INVALID_ARG;
 
     // ---- validation done; HIP calls from here on
-    for (int64_t b0 = 0; b0 < P.bundles; b0 += P.bundles_per_launch) {
-        const int64_t nz = (P.bundles - b0 < P.bundles_per_launch) ? P.bundles - b0 : P.bundles_per_launch;
+    for (int64_t b0 = 0; b0 < launch_units(P); b0 += units_per_launch(P)) {
+        const int64_t nz = (launch_units(P) - b0 < units_per_launch(P)) ? launch_units(P) - b0 : units_per_launch(P);
         FwdArgs a{x, y, A, B, P, b0};
         st = from_hip(deg->forward(io, a, grid_of(P, nz), stream));
         if (st != GRKAN_OK) return st;
@@ -254,16 +312,17 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
         if (st != GRKAN_OK) return st;
     }
     float *partials = static_cast<float *>(workspace);
-    for (int64_t b0 = 0; b0 < P.bundles; b0 += P.bundles_per_launch) {
-        const int64_t nz = (P.bundles - b0 < P.bundles_per_launch) ? P.bundles - b0 : P.bundles_per_launch;
+    for (int64_t b0 = 0; b0 < launch_units(P); b0 += units_per_launch(P)) {
+        const int64_t nz = (launch_units(P) - b0 < units_per_launch(P)) ? launch_units(P) - b0 : units_per_launch(P);
         BwdArgs a{x, dy, dx, A, B, dA, dB, partials, det ? kModePartials : kModeAtomic, P, b0};
         st = from_hip(deg->backward(io, a, grid_of(P, nz), stream));
         if (st != GRKAN_OK) return st;
     }
     if (!det) return GRKAN_OK;
     double *chunk_sums = reinterpret_cast<double *>(static_cast<char *>(workspace) + chunk_sums_offset(P));
-    return from_hip(launch_merge(partials, chunk_sums, n_groups, m, n, P.tiles, P.bundles, P.parts, dA, dB,
-                                 stream));
+    const bool narrow = P.kind == kNarrow;
+    return from_hip(launch_merge(partials, chunk_sums, n_groups, m, n, P.tiles, P.bundles, P.parts,
+                                 narrow ? P.d_g : 0, narrow ? P.cpb : 0, dA, dB, stream));
 }
 
 grkan_status_t query_impl(int64_t rows, int64_t d, int32_t n_groups, int32_t m, int32_t n,
@@ -286,12 +345,12 @@ grkan_status_t query_impl(int64_t rows, int64_t d, int32_t n_groups, int32_t m, 
         std::lock_guard<std::mutex> lock(g_mu);
         g_cus[dev] = cus;
     }
-    if (deg->occupancy(io, pass ? 1 : 0, P.block, &occ) != hipSuccess) return GRKAN_ERR_HIP;
+    if (deg->occupancy(io, pass ? 1 : 0, P.block, &occ, P.kind == kNarrow) != hipSuccess) return GRKAN_ERR_HIP;
     out->block = P.block;
     out->rows_per_iter = P.rows_per_iter;
     out->unroll = P.unroll;
     out->tiles = P.tiles;
-    out->grid = plan_grid(P);
+    out->grid = P.kind == kNarrow ? P.tiles * P.ncb : plan_grid(P);
     out->cus = cus;
     out->blocks_per_cu = occ;
     out->parts = P.parts;

@@ -111,6 +111,34 @@ __device__ static inline u32x4 win_reload16(Span w, uint32_t off) {
     return *reinterpret_cast<const volatile u32x4 *>(w.p + off);
 }
 
+// One I/O element per access, for the narrow-group kernels (one channel
+// column per lane): 4-byte fp32 or 2-byte bf16, non-temporal.
+template <class T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int kBytes = 4;
+    __device__ static inline float load(Span w, uint32_t off) {
+        return off < w.n ? __builtin_nontemporal_load(reinterpret_cast<const float *>(w.p + off)) : 0.0f;
+    }
+    __device__ static inline void store(Span w, uint32_t off, float v) {
+        if (off < w.n) __builtin_nontemporal_store(v, reinterpret_cast<float *>(const_cast<char *>(w.p) + off));
+    }
+};
+template <> struct Elem<bf16io> {
+    static constexpr int kBytes = 2;
+    // bf16 -> fp32 is exact; fp32 -> bf16 rounds to nearest even.
+    __device__ static inline float load(Span w, uint32_t off) {
+        if (off >= w.n) return 0.0f;
+        const unsigned short h = __builtin_nontemporal_load(reinterpret_cast<const unsigned short *>(w.p + off));
+        return __uint_as_float((uint32_t)h << 16);
+    }
+    __device__ static inline void store(Span w, uint32_t off, float v) {
+        if (off >= w.n) return;
+        const __bf16 h = (__bf16)v;
+        __builtin_nontemporal_store(__builtin_bit_cast(unsigned short, h),
+                                    reinterpret_cast<unsigned short *>(const_cast<char *>(w.p) + off));
+    }
+};
+
 // ------------------------------------------------------------ coefficients
 
 template <int M, int N> struct Deg {

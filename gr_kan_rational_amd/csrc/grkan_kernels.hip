@@ -292,8 +292,182 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
     }
 }
 
+// ------------------------------------------------------ narrow groups
+//
+// Groups whose row segment is not a whole number of 16-byte vectors (down to
+// one function per channel).  Lane (x, y) of a 64 x kNarrowRowLanes block owns
+// channel column c = 64 cb + x of the row tile, with that channel's
+// coefficients in its own registers, and walks rows y, y + kNarrowRowLanes,
+// ... of the tile in batches of U rows (loads issued together).  Each wave
+// reads 64 consecutive elements (256 or 128 bytes) per row.  The workgroup
+// then sums its lanes' terms over the row lanes and over the channels of
+// each group it touches, and writes one partial per (group, coefficient,
+// column block, tile).  Tiles are long (kNarrowRowLanes U iters rows) so
+// that these partials stay a small fraction of the traffic even with one
+// group per channel.
+
+constexpr int kNarrowCols = 64;
+constexpr int kNarrowRowLanes = 4;
+constexpr int kNarrowThreads = kNarrowCols * kNarrowRowLanes;
+constexpr int kNarrowUnroll = 4;
+// Tiles of 128 rows (forward) and 512 rows (backward: with one group per
+// channel the partials are then below 1% of the backward's traffic).
+constexpr int kNarrowFwdIters = 128 / (kNarrowRowLanes * kNarrowUnroll);
+constexpr int kNarrowBwdIters = 512 / (kNarrowRowLanes * kNarrowUnroll);
+
+struct NarrowPos {
+    int64_t tile;
+    int cb;
+};
+
+__device__ static inline NarrowPos narrow_pos(const Plan &P, int64_t tile0) {
+    const uint32_t b = blockIdx.x;
+    const uint32_t t = fastdiv(b, P.div_ncb);
+    NarrowPos p;
+    p.cb = (int)(b - t * (uint32_t)P.ncb);
+    p.tile = tile0 + t;
+    return p;
+}
+
+template <int U, int K>
+__device__ static inline Window narrow_window(const Plan &P, const NarrowPos &p, int64_t &ch) {
+    Window w;
+    const int64_t row0 = p.tile * (int64_t)(kNarrowRowLanes * U * K);
+    w.base = row0 * P.row_bytes + (int64_t)p.cb * kNarrowCols * P.es;
+    w.avail = P.rows * P.row_bytes - w.base;
+    ch = (int64_t)p.cb * kNarrowCols + threadIdx.x;
+    w.lane = (ch < P.d) ? (uint32_t)threadIdx.y * (uint32_t)P.row_bytes + (uint32_t)threadIdx.x * (uint32_t)P.es
+                        : kOffsetOutOfRange;
+    w.stride = (uint32_t)kNarrowRowLanes * (uint32_t)P.row_bytes;
+    return w;
+}
+
+// Group of this lane's channel (group 0 for lanes past the row, whose
+// accesses are all skipped).
+__device__ static inline int narrow_group(const Plan &P, int64_t ch) {
+    return ch < P.d ? (int)fastdiv((uint32_t)ch, P.div_dg) : 0;
+}
+
+template <class IO, int M, int N, int U, int K>
+__global__ __launch_bounds__(kNarrowThreads) void grkan_fwd_narrow_kernel(FwdArgs a) {
+    using V = Elem<IO>;
+    const Plan &P = a.plan;
+    const NarrowPos p = narrow_pos(P, a.bundle0);
+    if (p.tile >= P.tiles) return;
+    int64_t ch;
+    const Window w = narrow_window<U, K>(P, p, ch);
+    const Coefs<M, N> c = load_coefs<M, N>(a.A, a.B, narrow_group(P, ch));
+    const Span sx = make_span(at(a.x, w.base), w.avail);
+    const Span sy = make_span(at(a.y, w.base), w.avail);
+    for (int it = 0; it < K; ++it) {
+        float f[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) f[u] = V::load(sx, w.lane + (it * U + u) * w.stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) V::store(sy, w.lane + (it * U + u) * w.stride, rational<M, N>(f[u], c));
+    }
+}
+
+template <class IO, int M, int N, int U, int K>
+__global__ __launch_bounds__(kNarrowThreads) void grkan_bwd_narrow_kernel(BwdArgs a) {
+    using V = Elem<IO>;
+    constexpr int NC = Deg<M, N>::kNumCoef;
+    constexpr int KP = Deg<M, N>::kTop;
+    const Plan &P = a.plan;
+    const NarrowPos p = narrow_pos(P, a.bundle0);
+    if (p.tile >= P.tiles) return;
+    int64_t ch;
+    const Window w = narrow_window<U, K>(P, p, ch);
+    const BwdCoefs<M, N> k = derive<M, N>(load_coefs<M, N>(a.A, a.B, narrow_group(P, ch)));
+    const Span sx = make_span(at(a.x, w.base), w.avail);
+    const Span sdy = make_span(at(a.dy, w.base), w.avail);
+    const Span sdx = make_span(at(a.dx, w.base), w.avail);
+
+    // Sums per channel: fp32 over one batch (U terms), then fp32 across the
+    // batches (iters terms): no fp32 chain longer than 32.
+    float acc[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) acc[i] = 0.0f;
+    for (int it = 0; it < K; ++it) {
+        float xf[U], dyf[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            xf[u] = V::load(sx, w.lane + (it * U + u) * w.stride);
+            dyf[u] = V::load(sdy, w.lane + (it * U + u) * w.stride);
+        }
+        float part[NC];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) part[i] = 0.0f;
+        float dxf[U];
+        bool sure = true;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const Pow<KP> X(xf[u]);
+            const ElemBwd eb = backward_element<M, N, KP>(X, dyf[u], k);
+            accumulate<M, N>(eb.w, eb.sv, X, part);
+            dxf[u] = eb.dx;
+            sure = sure && eb.sure;
+        }
+        if constexpr (N > 0) {
+            // Rare: an element whose sign of Q the fp32 guard did not prove
+            // (x == 0, a root of Q, or b = 0 in its group): fix the batch.
+            if (__builtin_expect(!sure, 0)) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) dxf[u] = exact_fix<M, N>(xf[u], dyf[u], k, part);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) V::store(sdx, w.lane + (it * U + u) * w.stride, dxf[u]);
+#pragma unroll
+        for (int i = 0; i < NC; ++i) acc[i] += part[i];
+    }
+
+    // Workgroup sums in a fixed order: per channel over the row lanes, then
+    // per group over its channels in this column block, in fp64.
+    __shared__ float red[NC * kNarrowRowLanes * kNarrowCols];
+    __shared__ double ct[NC * kNarrowCols];
+    const int x = (int)threadIdx.x, y = (int)threadIdx.y;
+    const int t = y * kNarrowCols + x;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) red[(i * kNarrowRowLanes + y) * kNarrowCols + x] = acc[i];
+    __syncthreads();
+    for (int idx = t; idx < NC * kNarrowCols; idx += kNarrowThreads) {
+        const int i = idx / kNarrowCols, xx = idx % kNarrowCols;
+        double s = 0.0;
+#pragma unroll
+        for (int yy = 0; yy < kNarrowRowLanes; ++yy) s += (double)red[(i * kNarrowRowLanes + yy) * kNarrowCols + xx];
+        ct[idx] = s;
+    }
+    __syncthreads();
+    const int64_t c0 = (int64_t)p.cb * kNarrowCols;
+    const int64_t c1 = (c0 + kNarrowCols < P.d) ? c0 + kNarrowCols : P.d;
+    const int64_t g_lo = c0 / P.d_g, g_hi = (c1 - 1) / P.d_g;
+    const int nlg = (int)(g_hi - g_lo + 1);
+    for (int idx = t; idx < nlg * NC; idx += kNarrowThreads) {
+        const int64_t gg = g_lo + idx / NC;
+        const int i = idx % NC;
+        const int64_t lo = (gg * P.d_g > c0 ? gg * P.d_g : c0) - c0;
+        const int64_t hi = ((gg + 1) * P.d_g < c1 ? (gg + 1) * P.d_g : c1) - c0;
+        double s = 0.0;
+        for (int64_t c = lo; c < hi; ++c) s += ct[i * kNarrowCols + c];
+        if (a.mode == kModePartials) {
+            const int64_t part = (int64_t)p.cb - gg * P.d_g / P.cpb;
+            const int64_t slot = part * 8 * P.bundles + slot_in_part(P, p.tile);
+            a.partials[(gg * NC + i) * plan_slots(P) + slot] = (float)s;
+        } else {
+            float *dst = (i <= M) ? (a.dA + gg * (M + 1) + i) : (a.dB + gg * N + (i - M - 1));
+            unsafeAtomicAdd(dst, (float)s);
+        }
+    }
+}
+
 template <class IO, int M, int N>
 hipError_t fwd_impl(const FwdArgs &a, dim3 grid, hipStream_t s) {
+    if (a.plan.kind == kNarrow) {
+        hipLaunchKernelGGL((grkan_fwd_narrow_kernel<IO, M, N, kNarrowUnroll, kNarrowFwdIters>), grid,
+                           dim3(kNarrowCols, kNarrowRowLanes), 0, s, a);
+        return hipGetLastError();
+    }
     const dim3 block((unsigned)a.plan.part_vecs, (unsigned)a.plan.rows_per_iter);
     hipLaunchKernelGGL((grkan_fwd_kernel<IO, M, N, fwd_unroll<IO, M, N>()>), grid, block, 0, s, a);
     return hipGetLastError();
@@ -307,6 +481,11 @@ size_t bwd_lds_bytes(int block) {
 
 template <class IO, int M, int N>
 hipError_t bwd_impl(const BwdArgs &a, dim3 grid, hipStream_t s) {
+    if (a.plan.kind == kNarrow) {
+        hipLaunchKernelGGL((grkan_bwd_narrow_kernel<IO, M, N, kNarrowUnroll, kNarrowBwdIters>), grid,
+                           dim3(kNarrowCols, kNarrowRowLanes), 0, s, a);
+        return hipGetLastError();
+    }
     const dim3 block((unsigned)a.plan.part_vecs, (unsigned)a.plan.rows_per_iter);
     const size_t lds = bwd_lds_bytes<M, N>(a.plan.block);
     hipLaunchKernelGGL((grkan_bwd_kernel<IO, M, N, bwd_unroll<IO, M, N>()>), grid, block, lds, s, a);
@@ -319,6 +498,13 @@ template <int M, int N>
 int Kernels<M, N>::unroll(grkan_dtype_t io, int pass) {
     if (io == GRKAN_BF16) return pass ? bwd_unroll<bf16io, M, N>() : fwd_unroll<bf16io, M, N>();
     return pass ? bwd_unroll<float, M, N>() : fwd_unroll<float, M, N>();
+}
+
+template <int M, int N>
+void Kernels<M, N>::narrow_shape(grkan_dtype_t, int pass, int *row_lanes, int *unroll, int *iters) {
+    *row_lanes = kNarrowRowLanes;
+    *unroll = kNarrowUnroll;
+    *iters = pass ? kNarrowBwdIters : kNarrowFwdIters;
 }
 
 template <int M, int N>
@@ -338,7 +524,17 @@ hipError_t Kernels<M, N>::backward(grkan_dtype_t io, const BwdArgs &a, dim3 grid
 }
 
 template <int M, int N>
-hipError_t Kernels<M, N>::occupancy(grkan_dtype_t io, int pass, int block, int *blocks_per_cu) {
+hipError_t Kernels<M, N>::occupancy(grkan_dtype_t io, int pass, int block, int *blocks_per_cu, bool narrow) {
+    if (narrow) {
+        const void *fn;
+        if (io == GRKAN_BF16)
+            fn = pass ? (const void *)grkan_bwd_narrow_kernel<bf16io, M, N, kNarrowUnroll, kNarrowBwdIters>
+                      : (const void *)grkan_fwd_narrow_kernel<bf16io, M, N, kNarrowUnroll, kNarrowFwdIters>;
+        else
+            fn = pass ? (const void *)grkan_bwd_narrow_kernel<float, M, N, kNarrowUnroll, kNarrowBwdIters>
+                      : (const void *)grkan_fwd_narrow_kernel<float, M, N, kNarrowUnroll, kNarrowFwdIters>;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kNarrowThreads, 0);
+    }
     const void *fn;
     const size_t lds = pass ? bwd_lds_bytes<M, N>(block) : 0;
     if (io == GRKAN_BF16)

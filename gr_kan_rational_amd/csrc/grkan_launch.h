@@ -27,7 +27,10 @@ namespace grkan {
 // takes whole row tiles.  (A 3D grid with the same linear order measured
 // ~2% slower on MI355X.)  Grids too large for one launch are split into
 // launches of whole bundles.
+enum PlanKind : int32_t { kSegment = 0, kNarrow = 1 };
+
 struct Plan {
+    int32_t kind;           // kSegment, or kNarrow (below)
     int64_t rows;
     int64_t d;
     int32_t n_groups;
@@ -47,6 +50,22 @@ struct Plan {
     int64_t bundles_per_launch;
     FastDiv div_gp;         // division by parts * n_groups
     FastDiv div_parts;      // division by parts
+    // Narrow groups (a group row segment that is not a whole number of
+    // 16-byte vectors, e.g. one function per channel): each lane owns one
+    // channel column (with its own coefficients) over a long row tile; a
+    // workgroup is 64 channel columns x row_lanes rows.  `parts` is then the
+    // most column blocks one group spans, `unroll` the rows a lane loads at
+    // once and `iters` how many such batches it runs; a tile is
+    // row_lanes * unroll * iters rows.
+    int64_t row_words;      // channels per row
+    int32_t ncb;            // column blocks of 64 channels
+    int32_t cpb;            // channels per column block
+    int32_t d_g;            // channels per group
+    int32_t row_lanes;
+    int32_t iters;
+    int64_t tiles_per_launch;
+    FastDiv div_ncb;        // division by ncb
+    FastDiv div_dg;         // channel -> group
 };
 
 // Workgroups of a plan (padding workgroups of the last bundle included).
@@ -63,7 +82,7 @@ struct FwdArgs {
     const float *A;
     const float *B;
     Plan plan;
-    int64_t bundle0;  // first bundle of this launch
+    int64_t bundle0;  // first bundle (segment plans) or first tile (narrow plans) of this launch
 };
 
 enum BwdMode : int32_t { kModeAtomic = 0, kModePartials = 1 };
@@ -89,7 +108,10 @@ template <int M, int N> struct Kernels {
     static int target_block(grkan_dtype_t io, int pass, bool atomic_mode);
     static hipError_t forward(grkan_dtype_t io, const FwdArgs &a, dim3 grid, hipStream_t s);
     static hipError_t backward(grkan_dtype_t io, const BwdArgs &a, dim3 grid, hipStream_t s);
-    static hipError_t occupancy(grkan_dtype_t io, int pass, int block, int *blocks_per_cu);
+    static hipError_t occupancy(grkan_dtype_t io, int pass, int block, int *blocks_per_cu, bool narrow);
+    // Narrow-group launch shape: row lanes per block, rows loaded together,
+    // batches per tile.
+    static void narrow_shape(grkan_dtype_t io, int pass, int *row_lanes, int *unroll, int *iters);
 };
 
 // Degree pairs compiled into the library: (m, n) with a_0..a_m, b_1..b_n.
@@ -100,10 +122,12 @@ template <int M, int N> struct Kernels {
 // (group, coefficient)'s partials in chunks of 8192 slots; with more than one
 // chunk it needs merge_chunks(slots) fp64 chunk sums per (group,
 // coefficient) of scratch, after the partials in the workspace.
+// For narrow plans the merge skips the parts a group does not span (d_g,
+// cpb > 0); segment plans pass 0, 0.
 uint32_t merge_chunks(int64_t slots);
 hipError_t launch_merge(const float *partials, double *chunk_sums, int32_t n_groups, int32_t m,
-                        int32_t n, int64_t tiles, int64_t bundles, int32_t parts, float *dA,
-                        float *dB, hipStream_t s);
+                        int32_t n, int64_t tiles, int64_t bundles, int32_t parts, int32_t narrow_dg,
+                        int32_t narrow_cpb, float *dA, float *dB, hipStream_t s);
 hipError_t launch_zero(float *dA, float *dB, int64_t na, int64_t nb, hipStream_t s);
 
 // Per-element-atomic baseline, GR-KAN degrees only (grkan_naive.hip).

@@ -15,10 +15,10 @@ namespace {
 
 // Second stage of the deterministic backward: the partials of group g,
 // coefficient k -- one per (column part, row tile) -- are added in a fixed
-// order in fp64.  Workgroup (g, k, c) takes the c-th chunk of kMergeChunk
-// slots; each thread issues all of its loads before adding, so a chunk costs
-// about one memory round trip.  With one chunk per (g, k) (up to 8192 slots:
-// GR-KAN's 8 groups at KAT-B) the workgroup writes dA / dB directly;
+// order in fp64.  Workgroup (g, k, c) takes the c-th chunk of 8 slots per
+// thread; each thread issues all of its loads before adding, so a chunk
+// costs about one memory round trip.  With one chunk per (g, k) (up to 8192
+// slots: GR-KAN's 8 groups at KAT-B) the workgroup writes dA / dB directly;
 // otherwise (few groups, many tiles) it writes an fp64 chunk sum and
 // grkan_merge_chunks_kernel adds the chunk sums in order.  Slots are
 // [parts][8 * bundles]; within a part, slot r = (t mod 8) * bundles + t / 8
@@ -26,6 +26,10 @@ namespace {
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeLoads = 8;
 constexpr uint32_t kMergeChunk = (uint32_t)kMergeThreads * kMergeLoads;
+// Coefficients with at most this many slots (many groups, few tiles: one
+// function per channel) are merged by 256-thread workgroups.
+constexpr int kSmallThreads = 256;
+constexpr uint32_t kSmallChunk = (uint32_t)kSmallThreads * kMergeLoads;
 
 __device__ static inline void write_sum(int gk, int32_t na, int32_t nb, double total, float *dA,
                                         float *dB) {
@@ -49,26 +53,37 @@ __device__ static inline double block_sum(double s) {
     return total;
 }
 
-__global__ __launch_bounds__(kMergeThreads) void grkan_merge_kernel(
+// Parts of group g's slots that hold partials: all of them for segment
+// plans; for narrow plans the column blocks its channels span.
+__device__ static inline uint32_t parts_of(int g, uint32_t parts, int32_t dg, int32_t cpb) {
+    if (dg == 0) return parts;
+    const int64_t first = (int64_t)g * dg / cpb, last = ((int64_t)g * dg + dg - 1) / cpb;
+    return (uint32_t)(last - first + 1);
+}
+
+template <int T>
+__global__ __launch_bounds__(T) void grkan_merge_kernel(
     const float *__restrict__ partials, uint32_t tiles, uint32_t bundles, uint32_t slots,
-    int32_t na, int32_t nb, uint32_t chunks, double *__restrict__ chunk_sums,
+    int32_t na, int32_t nb, int32_t dg, int32_t cpb, uint32_t chunks, double *__restrict__ chunk_sums,
     float *__restrict__ dA, float *__restrict__ dB) {
+    constexpr uint32_t chunk = (uint32_t)T * kMergeLoads;
     const int gk = (int)blockIdx.x;
     const uint32_t c = blockIdx.y;
     const uint32_t per_part = 8u * bundles;
+    const uint32_t valid = parts_of(gk / (na + nb), slots / per_part, dg, cpb) * per_part;
     const float *p = partials + (int64_t)gk * slots;
     float v[kMergeLoads];
 #pragma unroll
     for (int i = 0; i < kMergeLoads; ++i) {
-        const uint32_t q = c * kMergeChunk + (uint32_t)i * kMergeThreads + threadIdx.x;
+        const uint32_t q = c * chunk + (uint32_t)i * T + threadIdx.x;
         const uint32_t r = q % per_part;
         const uint32_t tile = (r % bundles) * 8u + r / bundles;
-        v[i] = (q < slots && tile < tiles) ? p[q] : 0.0f;
+        v[i] = (q < valid && tile < tiles) ? p[q] : 0.0f;
     }
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < kMergeLoads; ++i) s += (double)v[i];
-    const double total = block_sum<kMergeThreads>(s);
+    const double total = block_sum<T>(s);
     if (threadIdx.x == 0) {
         if (chunks == 1) write_sum(gk, na, nb, total, dA, dB);
         else chunk_sums[(int64_t)gk * chunks + c] = total;
@@ -102,19 +117,26 @@ uint32_t merge_chunks(int64_t slots) {
 }
 
 hipError_t launch_merge(const float *partials, double *chunk_sums, int32_t n_groups, int32_t m,
-                        int32_t n, int64_t tiles, int64_t bundles, int32_t parts, float *dA,
-                        float *dB, hipStream_t s) {
+                        int32_t n, int64_t tiles, int64_t bundles, int32_t parts, int32_t narrow_dg,
+                        int32_t narrow_cpb, float *dA, float *dB, hipStream_t s) {
     const int32_t na = m + 1, nc = m + 1 + n;
     const int64_t slots = (int64_t)parts * 8 * bundles;
+    const dim3 grid_gk((unsigned)(n_groups * nc));
+    if (slots <= (int64_t)kSmallChunk) {
+        hipLaunchKernelGGL(grkan_merge_kernel<kSmallThreads>, grid_gk, dim3(kSmallThreads), 0, s, partials,
+                           (uint32_t)tiles, (uint32_t)bundles, (uint32_t)slots, na, n, narrow_dg, narrow_cpb,
+                           1u, chunk_sums, dA, dB);
+        return hipGetLastError();
+    }
     const uint32_t chunks = merge_chunks(slots);
-    hipLaunchKernelGGL(grkan_merge_kernel, dim3((unsigned)(n_groups * nc), chunks), dim3(kMergeThreads), 0,
-                       s, partials, (uint32_t)tiles, (uint32_t)bundles, (uint32_t)slots, na, n, chunks,
-                       chunk_sums, dA, dB);
+    hipLaunchKernelGGL(grkan_merge_kernel<kMergeThreads>, dim3(grid_gk.x, chunks), dim3(kMergeThreads), 0, s,
+                       partials, (uint32_t)tiles, (uint32_t)bundles, (uint32_t)slots, na, n, narrow_dg,
+                       narrow_cpb, chunks, chunk_sums, dA, dB);
     if (chunks == 1) return hipGetLastError();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(grkan_merge_chunks_kernel, dim3((unsigned)(n_groups * nc)), dim3(kChunkThreads), 0,
-                       s, chunk_sums, chunks, na, n, dA, dB);
+    hipLaunchKernelGGL(grkan_merge_chunks_kernel, grid_gk, dim3(kChunkThreads), 0, s, chunk_sums, chunks, na,
+                       n, dA, dB);
     return hipGetLastError();
 }
 

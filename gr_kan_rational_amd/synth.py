@@ -25,6 +25,7 @@ uses the same recipe with A [n_g, m+1] and B [n_g, n]:
     kat-b-r32       [1024, 197, 768]  fp32  n_g = 8,   (m, n) = (3, 2)  seed 7
     kat-b-r76       [1024, 197, 768]  fp32  n_g = 8,   (m, n) = (7, 6)  seed 8
     kat-b-poly5     [1024, 197, 768]  fp32  n_g = 8,   (m, n) = (5, 0)  seed 9
+    kat-b-perchan   [1024, 197, 768]  fp32  n_g = 768, (m, n) = (5, 4)  seed 10 (one PAU per channel)
 
 Recipe (reproducible, independent of the number of threads):
   * A then B from ``numpy.random.default_rng(seed)`` as float32 standard
@@ -97,12 +98,13 @@ WORKLOADS = {
         Workload("kat-b-r32", 1024, 197, 768, 8, "f32", 0.5, 1.0, 1e-2, 7, m=3, n=2),
         Workload("kat-b-r76", 1024, 197, 768, 8, "f32", 0.5, 1.0, 1e-2, 8, m=7, n=6),
         Workload("kat-b-poly5", 1024, 197, 768, 8, "f32", 0.5, 1.0, 1e-2, 9, m=5, n=0),
+        Workload("kat-b-perchan", 1024, 197, 768, 768, "f32", 0.5, 1.0, 1e-2, 10),
     )
 }
 
 # The GR-KAN workloads (degrees (5, 4), 8 groups) and the PAU-family ones.
 GRKAN_WORKLOADS = ("tiny", "kat-t", "kat-s-hid", "kat-b", "kat-b-hid-bf16")
-PAU_WORKLOADS = ("kat-b-pau", "kat-b-r32", "kat-b-r76", "kat-b-poly5")
+PAU_WORKLOADS = ("kat-b-pau", "kat-b-r32", "kat-b-r76", "kat-b-poly5", "kat-b-perchan")
 
 
 def custom(name: str, rows: int, d: int, n_groups: int, m: int = 5, n: int = 4, io: str = "f32",

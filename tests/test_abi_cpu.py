@@ -70,7 +70,11 @@ def test_workspace_size(lib):
     assert ws(lib, 201728, 768, 8, flags=BLOCK) == 0        # atomic modes need none
     assert ws(lib, 201728, 768, 8, flags=NAIVE) == 0
     assert ws(lib, 100, 770, 8) == 0                        # d % n_g != 0: rejected
-    assert ws(lib, 100, 40, 8) == 0                         # 5 channels * 4 B: not 16-byte vectors
+    # 5-channel groups (20 bytes, not whole 16-byte vectors): one channel per lane, 512-row tiles,
+    # 64 channels per column block; a group spans at most 2 blocks
+    assert ws(lib, 100, 40, 8) == 8 * 10 * 2 * 8 * 4
+    # one function per channel at KAT-B: 394 tiles of 512 rows -> 50 bundles -> 400 slots
+    assert ws(lib, 201728, 768, 768) == 768 * 10 * 400 * 4
     assert ws(lib, 0, 768, 8) == 0                          # no rows, no tiles
 
 
@@ -92,7 +96,6 @@ def bwd(lib, x=P, dy=P + 0x100000, A=P + 0x200000, B=P + 0x300000, dx=P + 0x4000
     (dict(rows=-1), INVALID), (dict(d=0), INVALID), (dict(n_g=0), INVALID), (dict(d=66), INVALID),
     (dict(io=7), INVALID),
     (dict(x=P + 4), UNSUPPORTED), (dict(y=P + 0x100008), UNSUPPORTED), (dict(A=P + 0x200002), UNSUPPORTED),
-    (dict(d=40), UNSUPPORTED),                       # d_g = 5 fp32 = 20 bytes per group row
     (dict(d=65536 * 4, n_g=65536), UNSUPPORTED),      # more groups than a grid dimension holds
     (dict(y=P + 16), INVALID),                       # partial overlap of y and x
     (dict(y=P + 0x200000 - 16), INVALID),             # y runs into A

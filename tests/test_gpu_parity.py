@@ -259,8 +259,9 @@ def test_errors_surface_as_exceptions(gk):
     with pytest.raises(gk.GRKANError) as e:
         gk.grkan_forward(flat, A, B, 8)
     assert e.value.status == gk.GRKAN_ERR_UNSUPPORTED
-    with pytest.raises(gk.GRKANError):
-        gk.grkan_forward(torch.randn(4, 40, device=DEV), A, B, 8)  # 20-byte group rows
+    with pytest.raises(gk.GRKANError) as e:
+        gk.grkan_forward(torch.randn(4, 42, device=DEV), A, B, 8)  # 42 channels in 8 groups
+    assert e.value.status == gk.GRKAN_ERR_INVALID_ARG
     with pytest.raises(gk.GRKANError) as e:
         gk.grkan_backward(torch.randn(4, 768, device=DEV), torch.randn(4, 768, device=DEV), A, B, 8,
                           workspace=torch.empty(8, dtype=torch.uint8, device=DEV))

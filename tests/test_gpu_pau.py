@@ -94,6 +94,43 @@ def test_pau_parity(gk, m, n, io, geom):
     run_and_check(gk, w, inp, "deterministic", f"({m},{n}) {io} {geom}")
 
 
+# Narrow groups (row segments that are not whole 16-byte vectors): one PAU per channel, 5-channel
+# groups, 3-channel groups, 125-channel groups spanning up to 3 column blocks of 64 channels,
+# and an odd channel count (bf16 rows that are not whole 4-byte words).
+NARROW = [(301, 768, 768), (203, 40, 8), (129, 300, 100), (97, 1000, 8), (67, 99, 33)]
+
+
+@pytest.mark.parametrize("m,n", [(5, 4), (3, 2), (7, 6), (5, 0), (2, 1)])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("geom", NARROW, ids=lambda g: f"{g[0]}x{g[1]}g{g[2]}")
+def test_pau_parity_narrow(gk, m, n, io, geom):
+    rows, d, n_g = geom
+    w = synth.custom(f"narrow{m}{n}", rows, d, n_g, m=m, n=n, io=io, seed=3000 + 10 * m + n)
+    log(f"[pau_narrow] (m,n)=({m},{n}) io={io} rows={rows} d={d} n_g={n_g}")
+    inp = synth.make_inputs(w)
+    run_and_check(gk, w, inp, "deterministic", f"narrow ({m},{n}) {io} {geom}")
+
+
+@pytest.mark.parametrize("geom", NARROW[:3], ids=lambda g: f"{g[0]}x{g[1]}g{g[2]}")
+def test_pau_parity_narrow_block_atomic(gk, geom):
+    rows, d, n_g = geom
+    w = synth.custom("narrow54a", rows, d, n_g, m=5, n=4, io="f32", seed=4000 + n_g)
+    log(f"[pau_narrow_block_atomic] rows={rows} d={d} n_g={n_g}")
+    run_and_check(gk, w, synth.make_inputs(w), "block_atomic", f"narrow block_atomic {geom}")
+
+
+def test_narrow_special_values(gk):
+    """One PAU per channel with exact zeros, b = 0 channels and x at a root of Q: the narrow
+    kernel's exact-sign path, element by element against the oracle."""
+    w = synth.custom("narrowspecial", 96, 64, 64, m=3, n=2, io="f32", seed=77)
+    inp = synth.make_inputs(w)
+    inp["x"][::3, :] = 0.0                    # exact zeros: s = 0
+    inp["B"][5] = 0.0                         # a channel with Q identically 0
+    inp["B"][7] = np.array([-0.75, 1.0], np.float32)   # Q = x (x - 0.75): root at 0.75
+    inp["x"][1::3, 7] = np.float32(0.75)
+    run_and_check(gk, w, inp, "deterministic", "narrow special values")
+
+
 @pytest.mark.parametrize("m,n", [(5, 4), (3, 2), (7, 6), (5, 0)])
 @pytest.mark.parametrize("geom", GEOMS, ids=lambda g: f"{g[0]}x{g[1]}g{g[2]}")
 def test_pau_parity_block_atomic(gk, m, n, geom):
