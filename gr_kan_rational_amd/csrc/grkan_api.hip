@@ -108,11 +108,14 @@ grkan_status_t plan_narrow(int64_t rows, int64_t d, int32_t n_groups, const Degr
     P->bundles = (P->tiles + 7) / 8;
     P->ncoef = deg.m + 1 + deg.n;
     if (plan_slots(*P) > (int64_t)65535 * 8192) return GRKAN_ERR_UNSUPPORTED;
-    int64_t tpl = (int64_t(1) << 31) / P->ncb;
-    const int64_t by_items = ((int64_t(1) << 32) - 1) / ((int64_t)P->ncb * P->block);
-    if (by_items < tpl) tpl = by_items;
-    if (tpl < 1) return GRKAN_ERR_UNSUPPORTED;
-    P->tiles_per_launch = tpl;
+    // Whole bundles of 8 tiles per launch: workgroup indices below 2^31 and
+    // work-items below 2^32.
+    const int64_t per_bundle = 8 * (int64_t)P->ncb;
+    int64_t bpl = (int64_t(1) << 31) / per_bundle;
+    const int64_t by_items = ((int64_t(1) << 32) - 1) / (per_bundle * P->block);
+    if (by_items < bpl) bpl = by_items;
+    if (bpl < 1) return GRKAN_ERR_UNSUPPORTED;
+    P->bundles_per_launch = bpl;
     P->div_ncb = make_fastdiv((uint32_t)P->ncb);
     P->div_dg = make_fastdiv((uint32_t)P->d_g);
     return GRKAN_OK;
@@ -208,16 +211,13 @@ int g_cus[kMaxDev];
 
 grkan_status_t from_hip(hipError_t e) { return e == hipSuccess ? GRKAN_OK : GRKAN_ERR_HIP; }
 
-// Launches cover whole bundles of 8 tiles (segment plans) or whole tiles
-// (narrow plans).
-int64_t launch_units(const Plan &P) { return P.kind == kNarrow ? P.tiles : P.bundles; }
-int64_t units_per_launch(const Plan &P) {
-    return P.kind == kNarrow ? P.tiles_per_launch : P.bundles_per_launch;
-}
+// Launches cover whole bundles of 8 tiles.
+int64_t launch_units(const Plan &P) { return P.bundles; }
+int64_t units_per_launch(const Plan &P) { return P.bundles_per_launch; }
 
-// Grid of one launch covering nz units.
+// Grid of one launch covering nz bundles.
 dim3 grid_of(const Plan &P, int64_t nz) {
-    if (P.kind == kNarrow) return dim3((unsigned)(P.ncb * nz));
+    if (P.kind == kNarrow) return dim3((unsigned)(8 * (int64_t)P.ncb * nz));
     return dim3((unsigned)(8 * (int64_t)P.parts * P.n_groups * nz));
 }
 
@@ -350,7 +350,7 @@ grkan_status_t query_impl(int64_t rows, int64_t d, int32_t n_groups, int32_t m, 
     out->rows_per_iter = P.rows_per_iter;
     out->unroll = P.unroll;
     out->tiles = P.tiles;
-    out->grid = P.kind == kNarrow ? P.tiles * P.ncb : plan_grid(P);
+    out->grid = P.kind == kNarrow ? 8 * P.bundles * P.ncb : plan_grid(P);
     out->cus = cus;
     out->blocks_per_cu = occ;
     out->parts = P.parts;

@@ -95,19 +95,25 @@ __device__ static inline Span make_span(const void *base, int64_t bytes) {
     return Span{static_cast<const char *>(base), (uint32_t)n};
 }
 
-// 16-byte accesses, non-temporal: the data is streamed once.
+// 16-byte accesses, non-temporal: the data is streamed once.  CHECK = false
+// is for workgroups whose every access is known to be inside the window
+// (full tiles, the vast majority): no compare, no branch.
+template <bool CHECK>
 __device__ static inline u32x4 win_load16(Span w, uint32_t off) {
-    return off < w.n ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w.p + off))
-                     : u32x4{0u, 0u, 0u, 0u};
+    if (CHECK && off >= w.n) return u32x4{0u, 0u, 0u, 0u};
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(w.p + off));
 }
+template <bool CHECK>
 __device__ static inline void win_store16(Span w, uint32_t off, u32x4 v) {
-    if (off < w.n) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(const_cast<char *>(w.p) + off));
+    if (CHECK && off >= w.n) return;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(const_cast<char *>(w.p) + off));
 }
 // A second read of data already loaded once, through a volatile access so
 // that the compiler issues it again instead of keeping the first load's
 // registers live until this point (the rare exact-sign path of the backward).
+template <bool CHECK>
 __device__ static inline u32x4 win_reload16(Span w, uint32_t off) {
-    if (off >= w.n) return u32x4{0u, 0u, 0u, 0u};
+    if (CHECK && off >= w.n) return u32x4{0u, 0u, 0u, 0u};
     return *reinterpret_cast<const volatile u32x4 *>(w.p + off);
 }
 
@@ -116,23 +122,29 @@ __device__ static inline u32x4 win_reload16(Span w, uint32_t off) {
 template <class T> struct Elem;
 template <> struct Elem<float> {
     static constexpr int kBytes = 4;
+    template <bool CHECK>
     __device__ static inline float load(Span w, uint32_t off) {
-        return off < w.n ? __builtin_nontemporal_load(reinterpret_cast<const float *>(w.p + off)) : 0.0f;
+        if (CHECK && off >= w.n) return 0.0f;
+        return __builtin_nontemporal_load(reinterpret_cast<const float *>(w.p + off));
     }
+    template <bool CHECK>
     __device__ static inline void store(Span w, uint32_t off, float v) {
-        if (off < w.n) __builtin_nontemporal_store(v, reinterpret_cast<float *>(const_cast<char *>(w.p) + off));
+        if (CHECK && off >= w.n) return;
+        __builtin_nontemporal_store(v, reinterpret_cast<float *>(const_cast<char *>(w.p) + off));
     }
 };
 template <> struct Elem<bf16io> {
     static constexpr int kBytes = 2;
     // bf16 -> fp32 is exact; fp32 -> bf16 rounds to nearest even.
+    template <bool CHECK>
     __device__ static inline float load(Span w, uint32_t off) {
-        if (off >= w.n) return 0.0f;
+        if (CHECK && off >= w.n) return 0.0f;
         const unsigned short h = __builtin_nontemporal_load(reinterpret_cast<const unsigned short *>(w.p + off));
         return __uint_as_float((uint32_t)h << 16);
     }
+    template <bool CHECK>
     __device__ static inline void store(Span w, uint32_t off, float v) {
-        if (off >= w.n) return;
+        if (CHECK && off >= w.n) return;
         const __bf16 h = (__bf16)v;
         __builtin_nontemporal_store(__builtin_bit_cast(unsigned short, h),
                                     reinterpret_cast<unsigned short *>(const_cast<char *>(w.p) + off));

@@ -102,6 +102,7 @@ struct Window {
     int64_t avail;    // bytes from base to the tensor end
     uint32_t lane;    // this lane's byte offset from base, pass 0
     uint32_t stride;  // bytes between passes (rows_per_iter rows)
+    bool full;        // every lane's every access is inside the tensor (uniform)
 };
 
 template <int U>
@@ -115,6 +116,7 @@ __device__ static inline Window window_of(const Plan &P, const Pos &p) {
     w.lane = (col < valid) ? (uint32_t)threadIdx.y * (uint32_t)P.row_bytes + (uint32_t)col * 16u
                            : kOffsetOutOfRange;
     w.stride = (uint32_t)P.rows_per_iter * (uint32_t)P.row_bytes;
+    w.full = valid >= P.part_vecs && row0 + U * P.rows_per_iter <= P.rows;
     return w;
 }
 
@@ -129,10 +131,25 @@ __device__ static inline const T *at(const T *p, int64_t bytes) {
 
 // ----------------------------------------------------------------- forward
 
-template <class IO, int M, int N, int U>
-__global__ __launch_bounds__(kMaxBlock) void grkan_fwd_kernel(FwdArgs a) {
+template <class IO, int M, int N, int U, bool CHECK>
+__device__ static inline void fwd_tile(Span rx, Span ry, const Window &w, const Coefs<M, N> &c) {
     using V = Io<IO>;
     constexpr int E = V::kElems;
+    u32x4 in[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) in[u] = win_load16<CHECK>(rx, w.lane + u * w.stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float f[E];
+        V::unpack(in[u], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] = rational<M, N>(f[e], c);
+        win_store16<CHECK>(ry, w.lane + u * w.stride, V::pack(f));
+    }
+}
+
+template <class IO, int M, int N, int U>
+__global__ __launch_bounds__(kMaxBlock) void grkan_fwd_kernel(FwdArgs a) {
     const Plan &P = a.plan;
     Pos p;
     if (!pos_of(P, a.bundle0, p)) return;
@@ -140,18 +157,7 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_fwd_kernel(FwdArgs a) {
     const Window w = window_of<U>(P, p);
     const Span rx = make_span(at(a.x, w.base), w.avail);
     const Span ry = make_span(at(a.y, w.base), w.avail);
-
-    u32x4 in[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) in[u] = win_load16(rx, w.lane + u * w.stride);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        float f[E];
-        V::unpack(in[u], f);
-#pragma unroll
-        for (int e = 0; e < E; ++e) f[e] = rational<M, N>(f[e], c);
-        win_store16(ry, w.lane + u * w.stride, V::pack(f));
-    }
+    fwd_tile<IO, M, N, U, true>(rx, ry, w, c);
 }
 
 // ---------------------------------------------------------------- backward
@@ -159,7 +165,7 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_fwd_kernel(FwdArgs a) {
 // One tile's elements: dX stored, this lane's gradient sums in acc.  The rare
 // exact-sign fix runs once per tile, before any dX is stored; it re-reads x
 // and dy, which is safe even when dx aliases x or dy.
-template <class IO, int M, int N, int U, bool QZERO>
+template <class IO, int M, int N, int U, bool QZERO, bool CHECK>
 __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window &w,
                                        const BwdCoefs<M, N> &k, float (&acc)[Deg<M, N>::kNumCoef]) {
     using V = Io<IO>;
@@ -169,8 +175,8 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
     u32x4 xin[U], din[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        xin[u] = win_load16(rx, w.lane + u * w.stride);
-        din[u] = win_load16(rdy, w.lane + u * w.stride);
+        xin[u] = win_load16<CHECK>(rx, w.lane + u * w.stride);
+        din[u] = win_load16<CHECK>(rdy, w.lane + u * w.stride);
     }
     float dxf[U][E];
     bool sure = true;
@@ -211,15 +217,15 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float xf[E], dyf[E];
-                V::unpack(win_reload16(rx, w.lane + u * w.stride), xf);
-                V::unpack(win_reload16(rdy, w.lane + u * w.stride), dyf);
+                V::unpack(win_reload16<CHECK>(rx, w.lane + u * w.stride), xf);
+                V::unpack(win_reload16<CHECK>(rdy, w.lane + u * w.stride), dyf);
 #pragma unroll
                 for (int e = 0; e < E; ++e) dxf[u][e] = exact_fix<M, N>(xf[e], dyf[e], k, acc);
             }
         }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) win_store16(rdx, w.lane + u * w.stride, V::pack(dxf[u]));
+    for (int u = 0; u < U; ++u) win_store16<CHECK>(rdx, w.lane + u * w.stride, V::pack(dxf[u]));
 }
 
 // Slot of a tile's partial within its part: tiles of one XCD side by side.
@@ -241,10 +247,12 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
     float acc[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) acc[i] = 0.0f;
+    // (A second, unchecked copy of the tile for full tiles spilled: the
+    // per-access checks cost < 1 VALU operation per element here.)
     if (k.q_zero) {
-        bwd_tile<IO, M, N, U, true>(rx, rdy, rdx, w, k, acc);
+        bwd_tile<IO, M, N, U, true, true>(rx, rdy, rdx, w, k, acc);
     } else {
-        if constexpr (N > 0) bwd_tile<IO, M, N, U, false>(rx, rdy, rdx, w, k, acc);
+        if constexpr (N > 0) bwd_tile<IO, M, N, U, false, true>(rx, rdy, rdx, w, k, acc);
     }
 
     // Workgroup sum of the NC terms, in a fixed order: transposed through LDS
@@ -295,50 +303,71 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
 // ------------------------------------------------------ narrow groups
 //
 // Groups whose row segment is not a whole number of 16-byte vectors (down to
-// one function per channel).  Lane (x, y) of a 64 x kNarrowRowLanes block owns
-// channel column c = 64 cb + x of the row tile, with that channel's
-// coefficients in its own registers, and walks rows y, y + kNarrowRowLanes,
-// ... of the tile in batches of U rows (loads issued together).  Each wave
-// reads 64 consecutive elements (256 or 128 bytes) per row.  The workgroup
-// then sums its lanes' terms over the row lanes and over the channels of
-// each group it touches, and writes one partial per (group, coefficient,
-// column block, tile).  Tiles are long (kNarrowRowLanes U iters rows) so
-// that these partials stay a small fraction of the traffic even with one
-// group per channel.
+// one function per channel).  Lane (x, y) of a 64-column block owns channel
+// column c = 64 cb + x of the row tile, with that channel's coefficients in
+// its own registers; each wave reads 64 consecutive elements per row.  The
+// forward loads all of a lane's rows (y, y + row lanes, ...) at once,
+// computes, stores and exits, like the wide kernels; the backward walks its
+// rows in batches (register limits, see below).  The backward workgroup then
+// sums its lanes' terms over the row lanes and over the channels of each
+// group it touches, and writes one partial per (group, coefficient, column
+// block, tile).  Workgroup b takes tile 8 (b / (8 ncb)) + (b mod 8) and
+// column block (b / 8) mod ncb, so that, as in the wide kernels, XCD (b mod 8)
+// takes whole row tiles.
+//
+// Measured on MI355X with copy probes of this layout at KAT-B: 128-row
+// one-shot tiles with that mapping streamed 6.1 TB/s, the same tiles dealt
+// column block first 5.6 TB/s, lanes looping over 4-row batches 5.2 TB/s
+// (128-row tiles) to 4.5 TB/s (512-row tiles).  Tiles are 128 rows: with one
+// group per channel the partials are then ~2.6% of the backward's traffic,
+// written once and read once by the merge.
 
 constexpr int kNarrowCols = 64;
-constexpr int kNarrowRowLanes = 4;
+constexpr int kNarrowRowLanes = 16;  // forward
 constexpr int kNarrowThreads = kNarrowCols * kNarrowRowLanes;
-constexpr int kNarrowUnroll = 4;
-// Tiles of 128 rows (forward) and 512 rows (backward: with one group per
-// channel the partials are then below 1% of the backward's traffic).
-constexpr int kNarrowFwdIters = 128 / (kNarrowRowLanes * kNarrowUnroll);
-constexpr int kNarrowBwdIters = 512 / (kNarrowRowLanes * kNarrowUnroll);
+// Backward: 4 row lanes, each walking 8 batches of 4 rows (128-row tiles).
+// The one-shot 128-row shape of the forward needs 1024-lane blocks, which
+// run one per CU at the backward's register count and stall the CU during
+// the workgroup reduction (measured 440-460 us against 397 us for this shape
+// with one function per channel at KAT-B).
+constexpr int kNarrowBwdRowLanes = 4;
+constexpr int kNarrowBwdThreads = kNarrowCols * kNarrowBwdRowLanes;
+constexpr int kNarrowBwdIters = 8;
+template <int M, int N> constexpr int narrow_bwd_unroll() { return 4; }
+// Forward rows per lane: 8 (128-row tiles); 4 for high degrees.
+template <int M, int N> constexpr int narrow_unroll() { return M + N <= 9 ? 8 : 4; }
 
 struct NarrowPos {
     int64_t tile;
     int cb;
 };
 
-__device__ static inline NarrowPos narrow_pos(const Plan &P, int64_t tile0) {
+__device__ static inline NarrowPos narrow_pos(const Plan &P, int64_t bundle0) {
     const uint32_t b = blockIdx.x;
-    const uint32_t t = fastdiv(b, P.div_ncb);
+    const uint32_t k = b >> 3;
+    const uint32_t bundle = fastdiv(k, P.div_ncb);
     NarrowPos p;
-    p.cb = (int)(b - t * (uint32_t)P.ncb);
-    p.tile = tile0 + t;
+    p.cb = (int)(k - bundle * (uint32_t)P.ncb);
+    p.tile = (bundle0 + (int64_t)bundle) * 8 + (b & 7);
     return p;
 }
 
-template <int U, int K>
+// The column block lies wholly inside the row.
+__device__ static inline bool c0_full(const Plan &P, const NarrowPos &p) {
+    return (int64_t)(p.cb + 1) * kNarrowCols <= P.d;
+}
+
+template <int RW, int U, int K>
 __device__ static inline Window narrow_window(const Plan &P, const NarrowPos &p, int64_t &ch) {
     Window w;
-    const int64_t row0 = p.tile * (int64_t)(kNarrowRowLanes * U * K);
+    const int64_t row0 = p.tile * (int64_t)(RW * U * K);
     w.base = row0 * P.row_bytes + (int64_t)p.cb * kNarrowCols * P.es;
     w.avail = P.rows * P.row_bytes - w.base;
     ch = (int64_t)p.cb * kNarrowCols + threadIdx.x;
     w.lane = (ch < P.d) ? (uint32_t)threadIdx.y * (uint32_t)P.row_bytes + (uint32_t)threadIdx.x * (uint32_t)P.es
                         : kOffsetOutOfRange;
-    w.stride = (uint32_t)kNarrowRowLanes * (uint32_t)P.row_bytes;
+    w.stride = (uint32_t)RW * (uint32_t)P.row_bytes;
+    w.full = c0_full(P, p) && row0 + RW * U * K <= P.rows;
     return w;
 }
 
@@ -348,94 +377,109 @@ __device__ static inline int narrow_group(const Plan &P, int64_t ch) {
     return ch < P.d ? (int)fastdiv((uint32_t)ch, P.div_dg) : 0;
 }
 
-template <class IO, int M, int N, int U, int K>
+template <class IO, int M, int N, int U, bool CHECK>
+__device__ static inline void narrow_fwd_rows(Span sx, Span sy, const Window &w, const Coefs<M, N> &c) {
+    using V = Elem<IO>;
+    float f[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) f[u] = V::template load<CHECK>(sx, w.lane + u * w.stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) V::template store<CHECK>(sy, w.lane + u * w.stride, rational<M, N>(f[u], c));
+}
+
+template <class IO, int M, int N>
 __global__ __launch_bounds__(kNarrowThreads) void grkan_fwd_narrow_kernel(FwdArgs a) {
     using V = Elem<IO>;
+    constexpr int U = narrow_unroll<M, N>();
     const Plan &P = a.plan;
     const NarrowPos p = narrow_pos(P, a.bundle0);
     if (p.tile >= P.tiles) return;
     int64_t ch;
-    const Window w = narrow_window<U, K>(P, p, ch);
+    const Window w = narrow_window<kNarrowRowLanes, U, 1>(P, p, ch);
     const Coefs<M, N> c = load_coefs<M, N>(a.A, a.B, narrow_group(P, ch));
     const Span sx = make_span(at(a.x, w.base), w.avail);
     const Span sy = make_span(at(a.y, w.base), w.avail);
-    for (int it = 0; it < K; ++it) {
-        float f[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) f[u] = V::load(sx, w.lane + (it * U + u) * w.stride);
-#pragma unroll
-        for (int u = 0; u < U; ++u) V::store(sy, w.lane + (it * U + u) * w.stride, rational<M, N>(f[u], c));
-    }
+    if (w.full) narrow_fwd_rows<IO, M, N, U, false>(sx, sy, w, c);
+    else narrow_fwd_rows<IO, M, N, U, true>(sx, sy, w, c);
 }
 
-template <class IO, int M, int N, int U, int K>
-__global__ __launch_bounds__(kNarrowThreads) void grkan_bwd_narrow_kernel(BwdArgs a) {
+// One lane's rows of a narrow tile: dX stored, the terms added to acc.
+template <class IO, int M, int N, int U, bool CHECK>
+__device__ static inline void narrow_bwd_rows(Span sx, Span sdy, Span sdx, const Window &w, int it,
+                                              const BwdCoefs<M, N> &k, float (&acc)[Deg<M, N>::kNumCoef]) {
     using V = Elem<IO>;
-    constexpr int NC = Deg<M, N>::kNumCoef;
     constexpr int KP = Deg<M, N>::kTop;
+    const uint32_t lane = w.lane + (uint32_t)(it * U) * w.stride;
+    float xf[U], dyf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        xf[u] = V::template load<CHECK>(sx, lane + u * w.stride);
+        dyf[u] = V::template load<CHECK>(sdy, lane + u * w.stride);
+        // keeps the two variants' arithmetic from being hoisted above the
+        // branch between them (see bwd_tile)
+        if constexpr (CHECK) asm volatile("" : "+v"(xf[u]), "+v"(dyf[u]));
+    }
+    float dxf[U];
+    bool sure = true;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const Pow<KP> X(xf[u]);
+        const ElemBwd eb = backward_element<M, N, KP>(X, dyf[u], k);
+        accumulate<M, N>(eb.w, eb.sv, X, acc);
+        dxf[u] = eb.dx;
+        sure = sure && eb.sure;
+    }
+    if constexpr (N > 0) {
+        // Rare: an element whose sign of Q the fp32 guard did not prove
+        // (x == 0, a root of Q, or b = 0 in its group): fix this lane's rows.
+        if (__builtin_expect(!sure, 0)) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) dxf[u] = exact_fix<M, N>(xf[u], dyf[u], k, acc);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) V::template store<CHECK>(sdx, lane + u * w.stride, dxf[u]);
+}
+
+template <class IO, int M, int N>
+__global__ __launch_bounds__(kNarrowBwdThreads) void grkan_bwd_narrow_kernel(BwdArgs a) {
+    using V = Elem<IO>;
+    constexpr int U = narrow_bwd_unroll<M, N>();
+    constexpr int K = kNarrowBwdIters;
+    constexpr int RW = kNarrowBwdRowLanes;
+    constexpr int NC = Deg<M, N>::kNumCoef;
     const Plan &P = a.plan;
     const NarrowPos p = narrow_pos(P, a.bundle0);
     if (p.tile >= P.tiles) return;
     int64_t ch;
-    const Window w = narrow_window<U, K>(P, p, ch);
+    const Window w = narrow_window<RW, U, K>(P, p, ch);
     const BwdCoefs<M, N> k = derive<M, N>(load_coefs<M, N>(a.A, a.B, narrow_group(P, ch)));
     const Span sx = make_span(at(a.x, w.base), w.avail);
     const Span sdy = make_span(at(a.dy, w.base), w.avail);
     const Span sdx = make_span(at(a.dx, w.base), w.avail);
 
-    // Sums per channel: fp32 over one batch (U terms), then fp32 across the
-    // batches (iters terms): no fp32 chain longer than 32.
     float acc[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) acc[i] = 0.0f;
     for (int it = 0; it < K; ++it) {
-        float xf[U], dyf[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            xf[u] = V::load(sx, w.lane + (it * U + u) * w.stride);
-            dyf[u] = V::load(sdy, w.lane + (it * U + u) * w.stride);
-        }
-        float part[NC];
-#pragma unroll
-        for (int i = 0; i < NC; ++i) part[i] = 0.0f;
-        float dxf[U];
-        bool sure = true;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const Pow<KP> X(xf[u]);
-            const ElemBwd eb = backward_element<M, N, KP>(X, dyf[u], k);
-            accumulate<M, N>(eb.w, eb.sv, X, part);
-            dxf[u] = eb.dx;
-            sure = sure && eb.sure;
-        }
-        if constexpr (N > 0) {
-            // Rare: an element whose sign of Q the fp32 guard did not prove
-            // (x == 0, a root of Q, or b = 0 in its group): fix the batch.
-            if (__builtin_expect(!sure, 0)) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) dxf[u] = exact_fix<M, N>(xf[u], dyf[u], k, part);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) V::store(sdx, w.lane + (it * U + u) * w.stride, dxf[u]);
-#pragma unroll
-        for (int i = 0; i < NC; ++i) acc[i] += part[i];
+        if (w.full) narrow_bwd_rows<IO, M, N, U, false>(sx, sdy, sdx, w, it, k, acc);
+        else narrow_bwd_rows<IO, M, N, U, true>(sx, sdy, sdx, w, it, k, acc);
     }
 
     // Workgroup sums in a fixed order: per channel over the row lanes, then
     // per group over its channels in this column block, in fp64.
-    __shared__ float red[NC * kNarrowRowLanes * kNarrowCols];
+    __shared__ float red[NC * RW * kNarrowCols];
     __shared__ double ct[NC * kNarrowCols];
     const int x = (int)threadIdx.x, y = (int)threadIdx.y;
     const int t = y * kNarrowCols + x;
 #pragma unroll
-    for (int i = 0; i < NC; ++i) red[(i * kNarrowRowLanes + y) * kNarrowCols + x] = acc[i];
+    for (int i = 0; i < NC; ++i) red[(i * RW + y) * kNarrowCols + x] = acc[i];
     __syncthreads();
-    for (int idx = t; idx < NC * kNarrowCols; idx += kNarrowThreads) {
+    for (int idx = t; idx < NC * kNarrowCols; idx += kNarrowBwdThreads) {
         const int i = idx / kNarrowCols, xx = idx % kNarrowCols;
         double s = 0.0;
 #pragma unroll
-        for (int yy = 0; yy < kNarrowRowLanes; ++yy) s += (double)red[(i * kNarrowRowLanes + yy) * kNarrowCols + xx];
+        for (int yy = 0; yy < RW; ++yy) s += (double)red[(i * RW + yy) * kNarrowCols + xx];
         ct[idx] = s;
     }
     __syncthreads();
@@ -443,7 +487,7 @@ __global__ __launch_bounds__(kNarrowThreads) void grkan_bwd_narrow_kernel(BwdArg
     const int64_t c1 = (c0 + kNarrowCols < P.d) ? c0 + kNarrowCols : P.d;
     const int64_t g_lo = c0 / P.d_g, g_hi = (c1 - 1) / P.d_g;
     const int nlg = (int)(g_hi - g_lo + 1);
-    for (int idx = t; idx < nlg * NC; idx += kNarrowThreads) {
+    for (int idx = t; idx < nlg * NC; idx += kNarrowBwdThreads) {
         const int64_t gg = g_lo + idx / NC;
         const int i = idx % NC;
         const int64_t lo = (gg * P.d_g > c0 ? gg * P.d_g : c0) - c0;
@@ -464,7 +508,7 @@ __global__ __launch_bounds__(kNarrowThreads) void grkan_bwd_narrow_kernel(BwdArg
 template <class IO, int M, int N>
 hipError_t fwd_impl(const FwdArgs &a, dim3 grid, hipStream_t s) {
     if (a.plan.kind == kNarrow) {
-        hipLaunchKernelGGL((grkan_fwd_narrow_kernel<IO, M, N, kNarrowUnroll, kNarrowFwdIters>), grid,
+        hipLaunchKernelGGL((grkan_fwd_narrow_kernel<IO, M, N>), grid,
                            dim3(kNarrowCols, kNarrowRowLanes), 0, s, a);
         return hipGetLastError();
     }
@@ -482,8 +526,8 @@ size_t bwd_lds_bytes(int block) {
 template <class IO, int M, int N>
 hipError_t bwd_impl(const BwdArgs &a, dim3 grid, hipStream_t s) {
     if (a.plan.kind == kNarrow) {
-        hipLaunchKernelGGL((grkan_bwd_narrow_kernel<IO, M, N, kNarrowUnroll, kNarrowBwdIters>), grid,
-                           dim3(kNarrowCols, kNarrowRowLanes), 0, s, a);
+        hipLaunchKernelGGL((grkan_bwd_narrow_kernel<IO, M, N>), grid,
+                           dim3(kNarrowCols, kNarrowBwdRowLanes), 0, s, a);
         return hipGetLastError();
     }
     const dim3 block((unsigned)a.plan.part_vecs, (unsigned)a.plan.rows_per_iter);
@@ -502,9 +546,9 @@ int Kernels<M, N>::unroll(grkan_dtype_t io, int pass) {
 
 template <int M, int N>
 void Kernels<M, N>::narrow_shape(grkan_dtype_t, int pass, int *row_lanes, int *unroll, int *iters) {
-    *row_lanes = kNarrowRowLanes;
-    *unroll = kNarrowUnroll;
-    *iters = pass ? kNarrowBwdIters : kNarrowFwdIters;
+    *row_lanes = pass ? kNarrowBwdRowLanes : kNarrowRowLanes;
+    *unroll = pass ? narrow_bwd_unroll<M, N>() : narrow_unroll<M, N>();
+    *iters = pass ? kNarrowBwdIters : 1;
 }
 
 template <int M, int N>
@@ -528,12 +572,13 @@ hipError_t Kernels<M, N>::occupancy(grkan_dtype_t io, int pass, int block, int *
     if (narrow) {
         const void *fn;
         if (io == GRKAN_BF16)
-            fn = pass ? (const void *)grkan_bwd_narrow_kernel<bf16io, M, N, kNarrowUnroll, kNarrowBwdIters>
-                      : (const void *)grkan_fwd_narrow_kernel<bf16io, M, N, kNarrowUnroll, kNarrowFwdIters>;
+            fn = pass ? (const void *)grkan_bwd_narrow_kernel<bf16io, M, N>
+                      : (const void *)grkan_fwd_narrow_kernel<bf16io, M, N>;
         else
-            fn = pass ? (const void *)grkan_bwd_narrow_kernel<float, M, N, kNarrowUnroll, kNarrowBwdIters>
-                      : (const void *)grkan_fwd_narrow_kernel<float, M, N, kNarrowUnroll, kNarrowFwdIters>;
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kNarrowThreads, 0);
+            fn = pass ? (const void *)grkan_bwd_narrow_kernel<float, M, N>
+                      : (const void *)grkan_fwd_narrow_kernel<float, M, N>;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn,
+                                                            pass ? kNarrowBwdThreads : kNarrowThreads, 0);
     }
     const void *fn;
     const size_t lds = pass ? bwd_lds_bytes<M, N>(block) : 0;

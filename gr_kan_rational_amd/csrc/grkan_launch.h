@@ -52,18 +52,17 @@ struct Plan {
     FastDiv div_parts;      // division by parts
     // Narrow groups (a group row segment that is not a whole number of
     // 16-byte vectors, e.g. one function per channel): each lane owns one
-    // channel column (with its own coefficients) over a long row tile; a
-    // workgroup is 64 channel columns x row_lanes rows.  `parts` is then the
-    // most column blocks one group spans, `unroll` the rows a lane loads at
-    // once and `iters` how many such batches it runs; a tile is
-    // row_lanes * unroll * iters rows.
+    // channel column (with its own coefficients); a workgroup is 64 channel
+    // columns x row_lanes rows, loading `unroll` rows per lane at once (a
+    // tile of row_lanes * unroll rows; iters = 1).  `parts` is then the most
+    // column blocks one group spans; workgroups per bundle of 8 tiles:
+    // 8 * ncb.
     int64_t row_words;      // channels per row
     int32_t ncb;            // column blocks of 64 channels
     int32_t cpb;            // channels per column block
     int32_t d_g;            // channels per group
     int32_t row_lanes;
     int32_t iters;
-    int64_t tiles_per_launch;
     FastDiv div_ncb;        // division by ncb
     FastDiv div_dg;         // channel -> group
 };
