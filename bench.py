@@ -7,6 +7,7 @@ Default workload: KAT-B shape, fp32 [1024, 197, 768], 8 groups.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload kat-b]
                     [--mode deterministic|atomic] [--no-cpu-baseline] [--no-naive]
+                    [--inflate 2,4,8|none]
 
 Prints one JSON line.  `value` is elements per second of the whole step
 (E / step time, K back-to-back steps between two HIP events); `roofline`
@@ -16,8 +17,10 @@ its average duration in a loop of K back-to-back backward calls, timed with
 HIP events on the stream it runs on.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
 workload.  `detail` adds the forward's figures, the atomic-mode and naive
-per-element-atomic backward times, and the rounding error of each backward
-reduction against the oracle's fp64 group sums (tests/golden).
+per-element-atomic backward times, the rounding error of each backward
+reduction against the oracle's fp64 group sums (tests/golden), and the
+FLOP-inflation probe: forward and backward times with each element's
+arithmetic repeated 2, 4 and 8 times (same outputs, same memory traffic).
 """
 from __future__ import annotations
 
@@ -95,6 +98,9 @@ def main() -> int:
     ap.add_argument("--mode", choices=["deterministic", "block_atomic"], default="deterministic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--inflate", default="2,4,8",
+                    help="repeat counts of the FLOP-inflation probe timed after the step (GR-KAN "
+                         "degrees only; 'none' to skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of one workload tensor (counter calibration)")
     args = ap.parse_args()
@@ -273,6 +279,26 @@ def main() -> int:
             errors["naive_per_element_atomic"] = grad_errors()
     if errors:
         detail["grad_error_vs_fp64_oracle"] = errors
+
+    repeats = [] if args.inflate == "none" or pau else [int(r) for r in args.inflate.split(",")]
+    if repeats and w.d % w.n_groups == 0 and (w.d // w.n_groups * es) % 16 == 0:
+        # The pages' Insight 2: the same calls with each element's arithmetic repeated R times
+        # (outputs unchanged).  Flat times mean the arithmetic is hidden under the memory
+        # stream; times growing with R mean the kernel is near or past the point where its
+        # arithmetic, not HBM, sets the pace.
+        log(f"FLOP-inflation probe, repeats {repeats}")
+        infl = {"repeats": [1], "fwd_ms": [fwd_ms], "bwd_ms": [bwd_ms]}
+        for r in repeats:
+            infl["repeats"].append(r)
+            infl["fwd_ms"].append(time_one(
+                lambda: gk.grkan_inflated_forward(x, A, B, w.n_groups, repeat=r, out=y, stream=stream),
+                args.steps))
+            infl["bwd_ms"].append(time_one(
+                lambda: gk.grkan_inflated_backward(x, dy, A, B, w.n_groups, repeat=r, dx=dx, dA=dA,
+                                                   dB=dB, workspace=ws, stream=stream), args.steps))
+        infl["fwd_vs_plain"] = [t / fwd_ms for t in infl["fwd_ms"]]
+        infl["bwd_vs_plain"] = [t / bwd_ms for t in infl["bwd_ms"]]
+        detail["flop_inflation"] = infl
 
     traffic = traffic_from_profiles(w.name, bwd_bytes)
     out = {

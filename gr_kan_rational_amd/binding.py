@@ -76,6 +76,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grkan_pau_query_launch.argtypes = [i64, i64, i32, i32, i32, ctypes.c_int, i32,
                                            ctypes.POINTER(grkan_launch_t)]
     lib.grkan_pau_query_launch.restype = ctypes.c_int
+    lib.grkan_inflated_forward.argtypes = [vp, vp, vp, vp, i64, i64, i32, ctypes.c_int, i32, vp]
+    lib.grkan_inflated_forward.restype = ctypes.c_int
+    lib.grkan_inflated_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, ctypes.c_int, u32,
+                                            i32, vp, sz, vp]
+    lib.grkan_inflated_backward.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -120,7 +125,7 @@ def _rows_d(x: torch.Tensor):
     return (x.numel() // d if d else 0), d
 
 
-def _forward(x, A, B, n_groups, m, n, out, stream, pau):
+def _forward(x, A, B, n_groups, m, n, out, stream, pau, repeat=None):
     lib = load_library()
     io = _io(x)
     _check_coefs(A, B, n_groups, x.device, m, n)
@@ -129,12 +134,18 @@ def _forward(x, A, B, n_groups, m, n, out, stream, pau):
     if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
         raise ValueError("out must match x")
     s = ctypes.c_void_p(_stream(stream))
-    if pau:
+    if repeat is not None:
+        name = "grkan_inflated_forward"
+        st = lib.grkan_inflated_forward(_ptr(x), _ptr(y), _ptr(A), _ptr(B), rows, d, n_groups, io,
+                                        int(repeat), s)
+    elif pau:
+        name = "grkan_pau_forward"
         st = lib.grkan_pau_forward(_ptr(x), _ptr(y), _ptr(A), _ptr(B), rows, d, n_groups, m, n, io, s)
     else:
+        name = "grkan_forward"
         st = lib.grkan_forward(_ptr(x), _ptr(y), _ptr(A), _ptr(B), rows, d, n_groups, io, s)
     if st != GRKAN_OK:
-        raise GRKANError(st, "grkan_pau_forward" if pau else "grkan_forward")
+        raise GRKANError(st, name)
     return y
 
 
@@ -151,6 +162,14 @@ def grkan_pau_forward(x: torch.Tensor, A: torch.Tensor, B, n_groups: int, m: int
     return _forward(x, A, B, n_groups, m, n, out, stream, pau=True)
 
 
+def grkan_inflated_forward(x: torch.Tensor, A: torch.Tensor, B: torch.Tensor, n_groups: int = 8,
+                           repeat: int = 8, out: torch.Tensor | None = None,
+                           stream=None) -> torch.Tensor:
+    """grkan_forward with each element's rational evaluated `repeat` times
+    (``grkan_inflated_forward``, the FLOP-inflation probe): same output, more arithmetic."""
+    return _forward(x, A, B, n_groups, GRKAN_M, GRKAN_N, out, stream, pau=False, repeat=repeat)
+
+
 def grkan_backward_workspace_size(rows: int, d: int, n_groups: int, io: int = GRKAN_F32,
                                   flags: int = 0) -> int:
     return int(load_library().grkan_backward_workspace_size(rows, d, n_groups, io, flags))
@@ -165,7 +184,7 @@ def grkan_pau_supported(m: int, n: int) -> bool:
     return bool(load_library().grkan_pau_supported(m, n))
 
 
-def _backward(x, dy, A, B, n_groups, m, n, mode, dx, dA, dB, workspace, stream, pau):
+def _backward(x, dy, A, B, n_groups, m, n, mode, dx, dA, dB, workspace, stream, pau, repeat=None):
     lib = load_library()
     io = _io(x)
     if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device or not dy.is_contiguous():
@@ -188,14 +207,20 @@ def _backward(x, dy, A, B, n_groups, m, n, mode, dx, dA, dB, workspace, stream, 
     wsp = _ptr(workspace) if workspace is not None else None
     wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
     s = ctypes.c_void_p(_stream(stream))
-    if pau:
+    if repeat is not None:
+        name = "grkan_inflated_backward"
+        st = lib.grkan_inflated_backward(_ptr(x), _ptr(dy), _ptr(A), _ptr(B), _ptr(dx), _ptr(dA),
+                                         _ptr(dB), rows, d, n_groups, io, flags, int(repeat), wsp, wsn, s)
+    elif pau:
+        name = "grkan_pau_backward"
         st = lib.grkan_pau_backward(_ptr(x), _ptr(dy), _ptr(A), _ptr(B), _ptr(dx), _ptr(dA), _ptr(dB),
                                     rows, d, n_groups, m, n, io, flags, wsp, wsn, s)
     else:
+        name = "grkan_backward"
         st = lib.grkan_backward(_ptr(x), _ptr(dy), _ptr(A), _ptr(B), _ptr(dx), _ptr(dA), _ptr(dB),
                                 rows, d, n_groups, io, flags, wsp, wsn, s)
     if st != GRKAN_OK:
-        raise GRKANError(st, "grkan_pau_backward" if pau else "grkan_backward")
+        raise GRKANError(st, name)
     return dx, dA, dB
 
 
@@ -221,6 +246,17 @@ def grkan_pau_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B, n_
                        stream=None):
     """(dx, dA, dB) for degrees (m, n) (``grkan_pau_backward``); dB is None when n == 0."""
     return _backward(x, dy, A, B, n_groups, m, n, mode, dx, dA, dB, workspace, stream, pau=True)
+
+
+def grkan_inflated_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                            n_groups: int = 8, repeat: int = 8, mode: str = "deterministic",
+                            dx: torch.Tensor | None = None, dA: torch.Tensor | None = None,
+                            dB: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                            stream=None):
+    """grkan_backward with each element evaluated `repeat` times
+    (``grkan_inflated_backward``, the FLOP-inflation probe): same outputs, more arithmetic."""
+    return _backward(x, dy, A, B, n_groups, GRKAN_M, GRKAN_N, mode, dx, dA, dB, workspace, stream,
+                     pau=False, repeat=repeat)
 
 
 def grkan_query_launch(rows: int, d: int, n_groups: int, io: int, pass_: int) -> dict:

@@ -31,8 +31,8 @@ struct DegreeOps {
     int m, n;
     int (*unroll)(grkan_dtype_t, int);
     int (*target_block)(grkan_dtype_t, int, bool);
-    hipError_t (*forward)(grkan_dtype_t, const FwdArgs &, dim3, hipStream_t);
-    hipError_t (*backward)(grkan_dtype_t, const BwdArgs &, dim3, hipStream_t);
+    hipError_t (*forward)(grkan_dtype_t, const FwdArgs &, int, dim3, hipStream_t);
+    hipError_t (*backward)(grkan_dtype_t, const BwdArgs &, int, dim3, hipStream_t);
     hipError_t (*occupancy)(grkan_dtype_t, int, int, int *, bool);
     void (*narrow_shape)(grkan_dtype_t, int, int *, int *, int *);
 };
@@ -221,14 +221,18 @@ dim3 grid_of(const Plan &P, int64_t nz) {
     return dim3((unsigned)(8 * (int64_t)P.parts * P.n_groups * nz));
 }
 
+bool valid_repeat(int32_t repeat) { return repeat == 1 || repeat == 2 || repeat == 4 || repeat == 8; }
+
 grkan_status_t forward_impl(const void *x, void *y, const float *A, const float *B, int64_t rows,
                             int64_t d, int32_t n_groups, int32_t m, int32_t n, grkan_dtype_t io,
-                            hipStream_t stream) {
+                            hipStream_t stream, int32_t repeat = 1) {
     const DegreeOps *deg = find_degree(m, n);
     if (!deg) return (m < 0 || n < 0) ? GRKAN_ERR_INVALID_ARG : GRKAN_ERR_UNSUPPORTED;
+    if (!valid_repeat(repeat)) return GRKAN_ERR_INVALID_ARG;
     Plan P;
     grkan_status_t st = plan_shape(rows, d, n_groups, *deg, io, 0, false, &P);
     if (st != GRKAN_OK) return st;
+    if (repeat != 1 && (P.kind == kNarrow || m != kGrkanM || n != kGrkanN)) return GRKAN_ERR_UNSUPPORTED;
     if (!A || (n > 0 && !B)) return GRKAN_ERR_INVALID_ARG;
     if (!aligned(A, 4) || !aligned(B, 4)) return GRKAN_ERR_UNSUPPORTED;
     if (rows == 0) return GRKAN_OK;
@@ -243,7 +247,7 @@ grkan_status_t forward_impl(const void *x, void *y, const float *A, const float 
     for (int64_t b0 = 0; b0 < launch_units(P); b0 += units_per_launch(P)) {
         const int64_t nz = (launch_units(P) - b0 < units_per_launch(P)) ? launch_units(P) - b0 : units_per_launch(P);
         FwdArgs a{x, y, A, B, P, b0};
-        st = from_hip(deg->forward(io, a, grid_of(P, nz), stream));
+        st = from_hip(deg->forward(io, a, repeat, grid_of(P, nz), stream));
         if (st != GRKAN_OK) return st;
     }
     return GRKAN_OK;
@@ -262,15 +266,19 @@ size_t workspace_impl(int64_t rows, int64_t d, int32_t n_groups, int32_t m, int3
 grkan_status_t backward_impl(const void *x, const void *dy, const float *A, const float *B, void *dx,
                              float *dA, float *dB, int64_t rows, int64_t d, int32_t n_groups,
                              int32_t m, int32_t n, grkan_dtype_t io, uint32_t flags,
-                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                             void *workspace, size_t workspace_bytes, hipStream_t stream,
+                             int32_t repeat = 1) {
     if (flags & ~(uint32_t)(GRKAN_BLOCK_ATOMIC | GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
     if ((flags & GRKAN_BLOCK_ATOMIC) && (flags & GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
     const DegreeOps *deg = find_degree(m, n);
     if (!deg) return (m < 0 || n < 0) ? GRKAN_ERR_INVALID_ARG : GRKAN_ERR_UNSUPPORTED;
+    if (!valid_repeat(repeat)) return GRKAN_ERR_INVALID_ARG;
     if ((flags & GRKAN_NAIVE_ATOMIC) && (m != kGrkanM || n != kGrkanN)) return GRKAN_ERR_UNSUPPORTED;
     Plan P;
     grkan_status_t st = plan_shape(rows, d, n_groups, *deg, io, 1, flags != 0, &P);
     if (st != GRKAN_OK) return st;
+    if (repeat != 1 && (P.kind == kNarrow || m != kGrkanM || n != kGrkanN || (flags & GRKAN_NAIVE_ATOMIC)))
+        return GRKAN_ERR_UNSUPPORTED;
     if (!A || !dA || (n > 0 && (!B || !dB))) return GRKAN_ERR_INVALID_ARG;
     if (!aligned(A, 4) || !aligned(B, 4) || !aligned(dA, 4) || !aligned(dB, 4))
         return GRKAN_ERR_UNSUPPORTED;
@@ -315,7 +323,7 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
     for (int64_t b0 = 0; b0 < launch_units(P); b0 += units_per_launch(P)) {
         const int64_t nz = (launch_units(P) - b0 < units_per_launch(P)) ? launch_units(P) - b0 : units_per_launch(P);
         BwdArgs a{x, dy, dx, A, B, dA, dB, partials, det ? kModePartials : kModeAtomic, P, b0};
-        st = from_hip(deg->backward(io, a, grid_of(P, nz), stream));
+        st = from_hip(deg->backward(io, a, repeat, grid_of(P, nz), stream));
         if (st != GRKAN_OK) return st;
     }
     if (!det) return GRKAN_OK;
@@ -428,4 +436,21 @@ extern "C" grkan_status_t grkan_pau_query_launch(int64_t rows, int64_t d, int32_
                                                  int32_t m, int32_t n, grkan_dtype_t io,
                                                  int32_t pass, grkan_launch_t *out) {
     return query_impl(rows, d, n_groups, m, n, io, pass, out);
+}
+
+extern "C" grkan_status_t grkan_inflated_forward(const void *x, void *y, const float *A,
+                                                 const float *B, int64_t rows, int64_t d,
+                                                 int32_t n_groups, grkan_dtype_t io, int32_t repeat,
+                                                 hipStream_t stream) {
+    return forward_impl(x, y, A, B, rows, d, n_groups, kGrkanM, kGrkanN, io, stream, repeat);
+}
+
+extern "C" grkan_status_t grkan_inflated_backward(const void *x, const void *dy, const float *A,
+                                                  const float *B, void *dx, float *dA, float *dB,
+                                                  int64_t rows, int64_t d, int32_t n_groups,
+                                                  grkan_dtype_t io, uint32_t flags, int32_t repeat,
+                                                  void *workspace, size_t workspace_bytes,
+                                                  hipStream_t stream) {
+    return backward_impl(x, dy, A, B, dx, dA, dB, rows, d, n_groups, kGrkanM, kGrkanN, io, flags,
+                         workspace, workspace_bytes, stream, repeat);
 }

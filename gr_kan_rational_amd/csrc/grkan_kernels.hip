@@ -129,9 +129,54 @@ __device__ static inline const T *at(const T *p, int64_t bytes) {
     return reinterpret_cast<const T *>(reinterpret_cast<const char *>(p) + bytes);
 }
 
+// ------------------------------------------------- FLOP-inflation probe
+//
+// [FlashKAT notes] (section "1. 性能瓶颈诊断", Insight 2) multiply the
+// rational's arithmetic by 8 with nested loops and find the run time
+// unchanged: the activation's FLOPs are not what limits it.  The same probe
+// here: with R > 1 every element is evaluated R - 1 extra times before the
+// evaluation whose results are used.  Each extra evaluation starts from a
+// copy of x passed through an empty asm statement, so the compiler can
+// neither share its arithmetic with the real evaluation nor fold it away, and
+// hands its results to another empty asm statement, so it is not dropped as
+// dead.  Outputs are those of R = 1 bit for bit; only the arithmetic per
+// element grows.  The gradient terms are accumulated once.
+
+template <class T> __device__ static inline T opaque(T v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+template <int M, int N, int R>
+__device__ static inline void burn_forward(float x, const Coefs<M, N> &c) {
+#pragma unroll
+    for (int r = 1; r < R; ++r) {
+        const float y = rational<M, N>(opaque(x), c);
+        asm volatile("" ::"v"(y));
+    }
+}
+
+template <int M, int N, int K, int R, bool QZERO>
+__device__ static inline void burn_backward(float x, float dy, const BwdCoefs<M, N> &k) {
+#pragma unroll
+    for (int r = 1; r < R; ++r) {
+        const Pow<K> X(opaque(x));
+        if constexpr (QZERO) {
+            float Pd = (M >= 1) ? k.da[0] : 0.0f;
+#pragma unroll
+            for (int i = 2; i <= M; ++i) Pd = fmaf(k.da[i - 1], X.p[i - 1], Pd);
+            asm volatile("" ::"v"(dy * Pd));
+        } else {
+            const ElemBwd e = backward_element<M, N, K>(X, dy, k);
+            asm volatile("" ::"v"(e.dx), "v"(e.w), "v"(e.sv), "v"(e.sure ? 1 : 0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // ----------------------------------------------------------------- forward
 
-template <class IO, int M, int N, int U, bool CHECK>
+template <class IO, int M, int N, int U, bool CHECK, int R = 1>
 __device__ static inline void fwd_tile(Span rx, Span ry, const Window &w, const Coefs<M, N> &c) {
     using V = Io<IO>;
     constexpr int E = V::kElems;
@@ -143,12 +188,16 @@ __device__ static inline void fwd_tile(Span rx, Span ry, const Window &w, const 
         float f[E];
         V::unpack(in[u], f);
 #pragma unroll
-        for (int e = 0; e < E; ++e) f[e] = rational<M, N>(f[e], c);
+        for (int e = 0; e < E; ++e) {
+            if constexpr (R > 1) burn_forward<M, N, R>(f[e], c);
+            f[e] = rational<M, N>(f[e], c);
+        }
         win_store16<CHECK>(ry, w.lane + u * w.stride, V::pack(f));
     }
 }
 
-template <class IO, int M, int N, int U>
+// R = 1: the plain forward; R = 2, 4, 8: the FLOP-inflation probe.
+template <class IO, int M, int N, int U, int R>
 __global__ __launch_bounds__(kMaxBlock) void grkan_fwd_kernel(FwdArgs a) {
     const Plan &P = a.plan;
     Pos p;
@@ -157,15 +206,16 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_fwd_kernel(FwdArgs a) {
     const Window w = window_of<U>(P, p);
     const Span rx = make_span(at(a.x, w.base), w.avail);
     const Span ry = make_span(at(a.y, w.base), w.avail);
-    fwd_tile<IO, M, N, U, true>(rx, ry, w, c);
+    fwd_tile<IO, M, N, U, true, R>(rx, ry, w, c);
 }
+
 
 // ---------------------------------------------------------------- backward
 
 // One tile's elements: dX stored, this lane's gradient sums in acc.  The rare
 // exact-sign fix runs once per tile, before any dX is stored; it re-reads x
 // and dy, which is safe even when dx aliases x or dy.
-template <class IO, int M, int N, int U, bool QZERO, bool CHECK>
+template <class IO, int M, int N, int U, bool QZERO, bool CHECK, int R = 1>
 __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window &w,
                                        const BwdCoefs<M, N> &k, float (&acc)[Deg<M, N>::kNumCoef]) {
     using V = Io<IO>;
@@ -192,6 +242,7 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
         V::unpack(din[u], dyf);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
+            if constexpr (R > 1) burn_backward<M, N, K, R, QZERO>(xf[e], dyf[e], k);
             const Pow<K> X(xf[e]);
             const float dy = dyf[e];
             if constexpr (QZERO) {
@@ -233,7 +284,8 @@ __device__ static inline int64_t slot_in_part(const Plan &P, int64_t tile) {
     return (tile & 7) * P.bundles + (tile >> 3);
 }
 
-template <class IO, int M, int N, int U>
+// R = 1: the plain backward; R = 2, 4, 8: the FLOP-inflation probe.
+template <class IO, int M, int N, int U, int R>
 __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
     constexpr int NC = Deg<M, N>::kNumCoef;
     const Plan &P = a.plan;
@@ -250,9 +302,9 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
     // (A second, unchecked copy of the tile for full tiles spilled: the
     // per-access checks cost < 1 VALU operation per element here.)
     if (k.q_zero) {
-        bwd_tile<IO, M, N, U, true, true>(rx, rdy, rdx, w, k, acc);
+        bwd_tile<IO, M, N, U, true, true, R>(rx, rdy, rdx, w, k, acc);
     } else {
-        if constexpr (N > 0) bwd_tile<IO, M, N, U, false, true>(rx, rdy, rdx, w, k, acc);
+        if constexpr (N > 0) bwd_tile<IO, M, N, U, false, true, R>(rx, rdy, rdx, w, k, acc);
     }
 
     // Workgroup sum of the NC terms, in a fixed order: transposed through LDS
@@ -506,14 +558,28 @@ __global__ __launch_bounds__(kNarrowBwdThreads) void grkan_bwd_narrow_kernel(Bwd
 }
 
 template <class IO, int M, int N>
-hipError_t fwd_impl(const FwdArgs &a, dim3 grid, hipStream_t s) {
+hipError_t fwd_impl(const FwdArgs &a, int repeat, dim3 grid, hipStream_t s) {
     if (a.plan.kind == kNarrow) {
+        if (repeat != 1) return hipErrorInvalidValue;
         hipLaunchKernelGGL((grkan_fwd_narrow_kernel<IO, M, N>), grid,
                            dim3(kNarrowCols, kNarrowRowLanes), 0, s, a);
         return hipGetLastError();
     }
     const dim3 block((unsigned)a.plan.part_vecs, (unsigned)a.plan.rows_per_iter);
-    hipLaunchKernelGGL((grkan_fwd_kernel<IO, M, N, fwd_unroll<IO, M, N>()>), grid, block, 0, s, a);
+    constexpr int U = fwd_unroll<IO, M, N>();
+    if (repeat != 1) {
+        if constexpr (M == 5 && N == 4) {
+            switch (repeat) {
+            case 2: hipLaunchKernelGGL((grkan_fwd_kernel<IO, M, N, U, 2>), grid, block, 0, s, a); break;
+            case 4: hipLaunchKernelGGL((grkan_fwd_kernel<IO, M, N, U, 4>), grid, block, 0, s, a); break;
+            case 8: hipLaunchKernelGGL((grkan_fwd_kernel<IO, M, N, U, 8>), grid, block, 0, s, a); break;
+            default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((grkan_fwd_kernel<IO, M, N, U, 1>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -524,15 +590,29 @@ size_t bwd_lds_bytes(int block) {
 }
 
 template <class IO, int M, int N>
-hipError_t bwd_impl(const BwdArgs &a, dim3 grid, hipStream_t s) {
+hipError_t bwd_impl(const BwdArgs &a, int repeat, dim3 grid, hipStream_t s) {
     if (a.plan.kind == kNarrow) {
+        if (repeat != 1) return hipErrorInvalidValue;
         hipLaunchKernelGGL((grkan_bwd_narrow_kernel<IO, M, N>), grid,
                            dim3(kNarrowCols, kNarrowBwdRowLanes), 0, s, a);
         return hipGetLastError();
     }
     const dim3 block((unsigned)a.plan.part_vecs, (unsigned)a.plan.rows_per_iter);
     const size_t lds = bwd_lds_bytes<M, N>(a.plan.block);
-    hipLaunchKernelGGL((grkan_bwd_kernel<IO, M, N, bwd_unroll<IO, M, N>()>), grid, block, lds, s, a);
+    constexpr int U = bwd_unroll<IO, M, N>();
+    if (repeat != 1) {
+        if constexpr (M == 5 && N == 4) {
+            switch (repeat) {
+            case 2: hipLaunchKernelGGL((grkan_bwd_kernel<IO, M, N, U, 2>), grid, block, lds, s, a); break;
+            case 4: hipLaunchKernelGGL((grkan_bwd_kernel<IO, M, N, U, 4>), grid, block, lds, s, a); break;
+            case 8: hipLaunchKernelGGL((grkan_bwd_kernel<IO, M, N, U, 8>), grid, block, lds, s, a); break;
+            default: return hipErrorInvalidValue;
+            }
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((grkan_bwd_kernel<IO, M, N, U, 1>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
@@ -558,13 +638,13 @@ int Kernels<M, N>::target_block(grkan_dtype_t, int pass, bool atomic_mode) {
 }
 
 template <int M, int N>
-hipError_t Kernels<M, N>::forward(grkan_dtype_t io, const FwdArgs &a, dim3 grid, hipStream_t s) {
-    return io == GRKAN_BF16 ? fwd_impl<bf16io, M, N>(a, grid, s) : fwd_impl<float, M, N>(a, grid, s);
+hipError_t Kernels<M, N>::forward(grkan_dtype_t io, const FwdArgs &a, int repeat, dim3 grid, hipStream_t s) {
+    return io == GRKAN_BF16 ? fwd_impl<bf16io, M, N>(a, repeat, grid, s) : fwd_impl<float, M, N>(a, repeat, grid, s);
 }
 
 template <int M, int N>
-hipError_t Kernels<M, N>::backward(grkan_dtype_t io, const BwdArgs &a, dim3 grid, hipStream_t s) {
-    return io == GRKAN_BF16 ? bwd_impl<bf16io, M, N>(a, grid, s) : bwd_impl<float, M, N>(a, grid, s);
+hipError_t Kernels<M, N>::backward(grkan_dtype_t io, const BwdArgs &a, int repeat, dim3 grid, hipStream_t s) {
+    return io == GRKAN_BF16 ? bwd_impl<bf16io, M, N>(a, repeat, grid, s) : bwd_impl<float, M, N>(a, repeat, grid, s);
 }
 
 template <int M, int N>
@@ -583,11 +663,11 @@ hipError_t Kernels<M, N>::occupancy(grkan_dtype_t io, int pass, int block, int *
     const void *fn;
     const size_t lds = pass ? bwd_lds_bytes<M, N>(block) : 0;
     if (io == GRKAN_BF16)
-        fn = pass ? (const void *)grkan_bwd_kernel<bf16io, M, N, bwd_unroll<bf16io, M, N>()>
-                  : (const void *)grkan_fwd_kernel<bf16io, M, N, fwd_unroll<bf16io, M, N>()>;
+        fn = pass ? (const void *)grkan_bwd_kernel<bf16io, M, N, bwd_unroll<bf16io, M, N>(), 1>
+                  : (const void *)grkan_fwd_kernel<bf16io, M, N, fwd_unroll<bf16io, M, N>(), 1>;
     else
-        fn = pass ? (const void *)grkan_bwd_kernel<float, M, N, bwd_unroll<float, M, N>()>
-                  : (const void *)grkan_fwd_kernel<float, M, N, fwd_unroll<float, M, N>()>;
+        fn = pass ? (const void *)grkan_bwd_kernel<float, M, N, bwd_unroll<float, M, N>(), 1>
+                  : (const void *)grkan_fwd_kernel<float, M, N, fwd_unroll<float, M, N>(), 1>;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, block, lds);
 }
 

@@ -101,12 +101,15 @@ struct BwdArgs {
 };
 
 // Kernels of one degree pair, defined in grkan_kernels.hip (compiled once per
-// supported pair).  pass 0 = forward, 1 = backward.
+// supported pair).  pass 0 = forward, 1 = backward.  `repeat` is the number
+// of evaluations per element: 1, or 2 / 4 / 8 for the FLOP-inflation probe,
+// whose kernels exist for GR-KAN's degrees (5, 4) and segment plans only
+// (forward / backward return hipErrorInvalidValue for anything else).
 template <int M, int N> struct Kernels {
     static int unroll(grkan_dtype_t io, int pass);
     static int target_block(grkan_dtype_t io, int pass, bool atomic_mode);
-    static hipError_t forward(grkan_dtype_t io, const FwdArgs &a, dim3 grid, hipStream_t s);
-    static hipError_t backward(grkan_dtype_t io, const BwdArgs &a, dim3 grid, hipStream_t s);
+    static hipError_t forward(grkan_dtype_t io, const FwdArgs &a, int repeat, dim3 grid, hipStream_t s);
+    static hipError_t backward(grkan_dtype_t io, const BwdArgs &a, int repeat, dim3 grid, hipStream_t s);
     static hipError_t occupancy(grkan_dtype_t io, int pass, int block, int *blocks_per_cu, bool narrow);
     // Narrow-group launch shape: row lanes per block, rows loaded together,
     // batches per tile.

@@ -189,6 +189,36 @@ GRKAN_API grkan_status_t grkan_pau_query_launch(int64_t rows, int64_t d, int32_t
                                       int32_t m, int32_t n, grkan_dtype_t io, int32_t pass,
                                       grkan_launch_t *out);
 
+/*
+ * FLOP-inflation probe ([FlashKAT notes], section "1. 性能瓶颈诊断",
+ * Insight 2: the rational's arithmetic multiplied by 8 through nested loops
+ * left the pages' run time unchanged).  grkan_forward / grkan_backward with
+ * every element evaluated `repeat` times instead of once -- the rational in
+ * the forward; P, P', Q, Q', 1 + |Q|, the sign guard and dx in the backward --
+ * and the results of the last evaluation used.  The outputs are bit for bit
+ * those of grkan_forward / grkan_backward with the same arguments; the
+ * memory traffic and launch geometry are the same too, so the run time
+ * against `repeat` shows how far the activation is from being bound by its
+ * arithmetic.  A measurement tool, not a faster path.
+ *   repeat    1, 2, 4 or 8 (1 runs the plain kernels); anything else is
+ *             GRKAN_ERR_INVALID_ARG.
+ *   Other arguments as in grkan_forward / grkan_backward, with two limits:
+ *   shapes whose group row segment (d / n_groups * bytes(io)) is not a
+ *   multiple of 16 bytes, and GRKAN_NAIVE_ATOMIC, are GRKAN_ERR_UNSUPPORTED
+ *   for repeat > 1.  The workspace is grkan_backward_workspace_size()'s.
+ */
+GRKAN_API grkan_status_t grkan_inflated_forward(const void *x, void *y, const float *A,
+                                      const float *B, int64_t rows, int64_t d,
+                                      int32_t n_groups, grkan_dtype_t io, int32_t repeat,
+                                      hipStream_t stream);
+
+GRKAN_API grkan_status_t grkan_inflated_backward(const void *x, const void *dy, const float *A,
+                                       const float *B, void *dx, float *dA, float *dB,
+                                       int64_t rows, int64_t d, int32_t n_groups,
+                                       grkan_dtype_t io, uint32_t flags, int32_t repeat,
+                                       void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

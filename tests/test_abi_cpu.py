@@ -39,7 +39,8 @@ def test_header_declares_the_abi():
         "grkan_forward", "grkan_backward", "grkan_backward_workspace_size",
         "grkan_status_string", "grkan_query_launch",
         "grkan_pau_supported", "grkan_pau_forward", "grkan_pau_backward",
-        "grkan_pau_backward_workspace_size", "grkan_pau_query_launch"])
+        "grkan_pau_backward_workspace_size", "grkan_pau_query_launch",
+        "grkan_inflated_forward", "grkan_inflated_backward"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -192,3 +193,45 @@ def test_pau_rejects_before_any_device_call(lib):
     assert pbwd(lib, 7, 6, dA=P + 0x600000 - 8 * 8 * 4 + 8) == INVALID  # dA [8][8] runs into dB
     # n = 0: B and dB may be NULL; rows == 0 returns before any HIP call
     assert pfwd(lib, 5, 0, x=None, y=None, B=None, rows=0) == OK
+
+
+# ------------------------------------------------------- FLOP-inflation probe
+
+def ifwd(lib, repeat, x=P, y=P + 0x100000, A=P + 0x200000, B=P + 0x300000, rows=4, d=64, n_g=8, io=F32):
+    return lib.grkan_inflated_forward(x, y, A, B, rows, d, n_g, io, repeat, None)
+
+
+def ibwd(lib, repeat, x=P, dy=P + 0x100000, A=P + 0x200000, B=P + 0x300000, dx=P + 0x400000,
+         dA=P + 0x500000, dB=P + 0x600000, rows=4, d=64, n_g=8, io=F32, flags=DEFAULT,
+         ws_ptr=P + 0x700000, ws_bytes=1 << 20):
+    return lib.grkan_inflated_backward(x, dy, A, B, dx, dA, dB, rows, d, n_g, io, flags, repeat,
+                                       ws_ptr, ws_bytes, None)
+
+
+@pytest.mark.parametrize("repeat", [0, 3, 5, 16, -1])
+def test_inflated_rejects_repeat(lib, repeat):
+    assert ifwd(lib, repeat) == INVALID
+    assert ibwd(lib, repeat) == INVALID
+
+
+@pytest.mark.parametrize("repeat", [1, 2, 4, 8])
+def test_inflated_validates_like_the_plain_calls(lib, repeat):
+    assert ifwd(lib, repeat, A=None) == INVALID
+    assert ifwd(lib, repeat, y=P + 16) == INVALID
+    assert ifwd(lib, repeat, x=P + 4) == UNSUPPORTED
+    assert ibwd(lib, repeat, ws_bytes=100) == INVALID
+    assert ibwd(lib, repeat, dA=P + 0x600000 + 8) == INVALID
+    assert ibwd(lib, repeat, flags=BLOCK | NAIVE) == INVALID
+    # rows == 0 returns before any HIP call
+    assert ifwd(lib, repeat, x=None, y=None, rows=0) == OK
+
+
+@pytest.mark.parametrize("repeat", [2, 4, 8])
+def test_inflated_limits(lib, repeat):
+    # 5-channel fp32 groups (20-byte row segments) take the one-channel-per-lane kernels, which
+    # have no inflated variant; nor has the naive per-element-atomic baseline.
+    assert ifwd(lib, repeat, d=40) == UNSUPPORTED
+    assert ibwd(lib, repeat, d=40) == UNSUPPORTED
+    assert ibwd(lib, repeat, flags=NAIVE) == UNSUPPORTED
+    # the plain kernels still take those (validation passes on to the device)
+    assert fwd(lib, d=40, rows=0, x=None, y=None) == OK
