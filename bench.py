@@ -89,6 +89,119 @@ def cpu_baseline(w, target_s: float = 10.0) -> dict:
                       f"(Y, dX, dA, dB) in fp64, {dt:.1f} s wall"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
+
+
+def cpu_baseline_layer(w, target_s: float = 10.0) -> dict:
+    """fp64 layer oracle (bf16(F(x)) W^T) on the first rows of the workload."""
+    from gr_kan_rational_amd import synth
+    from oracle import layer, oracle
+
+    Wb = synth.weight(w)
+    calib = 64
+    inp = synth.make_inputs(w, rows=calib, need_dy=False)
+    t0 = time.perf_counter()
+    layer.forward(inp["x"], inp["A"], inp["B"], Wb, w.n_groups)
+    dt = time.perf_counter() - t0
+    rows = int(min(w.rows, max(calib, calib * target_s / max(dt, 1e-3))))
+    inp = synth.make_inputs(w, rows=rows, need_dy=False)
+    t0 = time.perf_counter()
+    layer.forward(inp["x"], inp["A"], inp["B"], Wb, w.n_groups)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.d * w.d_out
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"first {rows} of {w.rows} rows of {w.name}: F in fp64, bf16 rounding, fp64 "
+                      f"matrix product, {dt:.1f} s wall"}
+
+
+def bench_layer(args, w, gk, synth, dev, log) -> int:
+    """The GR-KAN layer forward z = F(x) W^T (bf16): F fused into the matrix-core GEMM
+    (grkan_layer_forward), against the unfused composition on the same GEMM kernel
+    (grkan_forward -> grkan_linear_forward) and, for context, grkan_forward followed by
+    torch's library GEMM."""
+    import torch
+
+    log(f"layer workload {w.name}: x [{w.batch},{w.seq},{w.d}] -> {w.d_out}, bf16: generating inputs")
+    inp = synth.make_inputs(w, need_dy=False)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, W = bf(inp["x"]), bf(inp["W"])
+    A = torch.from_numpy(inp["A"]).to(dev)
+    B = torch.from_numpy(inp["B"]).to(dev)
+    del inp
+    z = torch.empty((w.rows, w.d_out), dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        gk.grkan_layer_forward(x, A, B, W, w.n_groups, out=z, stream=stream)
+
+    def unfused():
+        gk.grkan_forward(x, A, B, w.n_groups, out=y, stream=stream)
+        gk.grkan_linear_forward(y, W, out=z, stream=stream)
+
+    def timed(fn, reps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(reps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ms = timed(fused, args.steps)
+    flops = 2.0 * w.rows * w.d * w.d_out
+    tflops = flops / (ms * 1e-3) / 1e12
+    detail = {
+        "unfused_ms": timed(unfused, args.steps),
+        "activation_ms": timed(lambda: gk.grkan_forward(x, A, B, w.n_groups, out=y, stream=stream), args.steps),
+        "linear_ms": timed(lambda: gk.grkan_linear_forward(y, W, out=z, stream=stream), args.steps),
+        "torch_linear_ms": timed(lambda: torch.matmul(y, W.t(), out=z), args.steps),
+        "flops_per_step": flops,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    detail["torch_unfused_ms"] = detail["activation_ms"] + detail["torch_linear_ms"]
+    log(f"fused {ms:.4f} ms ({tflops:.1f} TFLOP/s); unfused {detail['unfused_ms']:.4f} ms; "
+        f"activation {detail['activation_ms']:.4f} + linear {detail['linear_ms']:.4f} ms; "
+        f"torch linear {detail['torch_linear_ms']:.4f} ms")
+    out = {
+        "metric": f"GR-KAN layer forward z = F(x) W^T (F fused into a bf16 matrix-core GEMM), workload {w.name}",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 (fp32 accumulation)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "shape": [w.batch, w.seq, w.d], "d_out": w.d_out,
+                   "n_groups": w.n_groups, "degrees": [w.m, w.n], "io": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "grkan_layer_forward (grkan_layer_gemm_kernel, fused)",
+                     "algorithmic_flops_per_launch": flops},
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 layer oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline_layer(w)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +248,8 @@ def main() -> int:
                           "copies": max(1, args.steps)}), flush=True)
         return 0
     gk.load_library()
+    if w.d_out > 0:
+        return bench_layer(args, w, gk, synth, dev, log)
     io = gk.GRKAN_BF16 if w.io == "bf16" else gk.GRKAN_F32
     log(f"workload {w.name} [{w.batch},{w.seq},{w.d}] {w.io}: generating inputs")
     inp = synth.make_inputs(w)

@@ -81,6 +81,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grkan_inflated_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, ctypes.c_int, u32,
                                             i32, vp, sz, vp]
     lib.grkan_inflated_backward.restype = ctypes.c_int
+    lib.grkan_layer_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.grkan_layer_forward.restype = ctypes.c_int
+    lib.grkan_linear_forward.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.grkan_linear_forward.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -257,6 +261,45 @@ def grkan_inflated_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, 
     (``grkan_inflated_backward``, the FLOP-inflation probe): same outputs, more arithmetic."""
     return _backward(x, dy, A, B, n_groups, GRKAN_M, GRKAN_N, mode, dx, dA, dB, workspace, stream,
                      pau=False, repeat=repeat)
+
+
+def _layer_out(x, W, out):
+    if x.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+        raise TypeError("the layer takes bfloat16 x and W")
+    if W.dim() != 2 or not W.is_contiguous() or W.device != x.device:
+        raise ValueError("W must be a contiguous [d_out, d_in] tensor on x's device")
+    rows, d_in = _rows_d(x)
+    if W.shape[1] != d_in:
+        raise ValueError("W's second dimension must be x's last")
+    d_out = W.shape[0]
+    z = torch.empty((*x.shape[:-1], d_out), dtype=torch.bfloat16, device=x.device) if out is None else out
+    if z.dtype != torch.bfloat16 or z.numel() != rows * d_out or not z.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor of rows x d_out elements")
+    return rows, d_in, d_out, z
+
+
+def grkan_layer_forward(x: torch.Tensor, A: torch.Tensor, B: torch.Tensor, W: torch.Tensor,
+                        n_groups: int = 8, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """z = F(x) W^T, the GR-KAN layer with F fused into the matrix product
+    (``grkan_layer_forward``); bf16 x [..., d_in], W [d_out, d_in]."""
+    _check_coefs(A, B, n_groups, x.device)
+    rows, d_in, d_out, z = _layer_out(x, W, out)
+    st = load_library().grkan_layer_forward(_ptr(x), _ptr(A), _ptr(B), _ptr(W), _ptr(z), rows, d_in,
+                                            d_out, n_groups, ctypes.c_void_p(_stream(stream)))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_layer_forward")
+    return z
+
+
+def grkan_linear_forward(y: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
+                         stream=None) -> torch.Tensor:
+    """z = y W^T on the same matrix-core kernel (``grkan_linear_forward``)."""
+    rows, d_in, d_out, z = _layer_out(y, W, out)
+    st = load_library().grkan_linear_forward(_ptr(y), _ptr(W), _ptr(z), rows, d_in, d_out,
+                                             ctypes.c_void_p(_stream(stream)))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_linear_forward")
+    return z
 
 
 def grkan_query_launch(rows: int, d: int, n_groups: int, io: int, pass_: int) -> dict:

@@ -438,6 +438,54 @@ extern "C" grkan_status_t grkan_pau_query_launch(int64_t rows, int64_t d, int32_
     return query_impl(rows, d, n_groups, m, n, io, pass, out);
 }
 
+// ------------------------------------------------------------ the layer
+
+namespace {
+
+grkan_status_t layer_shape(int64_t rows, int64_t d_in, int64_t d_out) {
+    if (rows < 0 || d_in <= 0 || d_out <= 0) return GRKAN_ERR_INVALID_ARG;
+    if (rows > INT32_MAX || d_in > INT32_MAX || d_out > INT32_MAX) return GRKAN_ERR_UNSUPPORTED;
+    if (d_in % layer_k_step() != 0) return GRKAN_ERR_UNSUPPORTED;
+    return GRKAN_OK;
+}
+
+}  // namespace
+
+extern "C" grkan_status_t grkan_layer_forward(const void *x, const float *A, const float *B,
+                                              const void *W, void *z, int64_t rows, int64_t d_in,
+                                              int64_t d_out, int32_t n_groups, hipStream_t stream) {
+    grkan_status_t st = layer_shape(rows, d_in, d_out);
+    if (st != GRKAN_OK) return st;
+    if (n_groups <= 0 || d_in % n_groups != 0) return GRKAN_ERR_INVALID_ARG;
+    if (n_groups > layer_max_groups() || (d_in / n_groups) % 8 != 0) return GRKAN_ERR_UNSUPPORTED;
+    if (!A || !B || !W) return GRKAN_ERR_INVALID_ARG;
+    if (!aligned(A, 4) || !aligned(B, 4) || !aligned(W, 16)) return GRKAN_ERR_UNSUPPORTED;
+    if (rows == 0) return GRKAN_OK;
+    if (!x || !z) return GRKAN_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(z, 2)) return GRKAN_ERR_UNSUPPORTED;
+    const size_t xb = (size_t)rows * d_in * 2, zb = (size_t)rows * d_out * 2, wb = (size_t)d_out * d_in * 2;
+    if (overlap(z, zb, x, xb) || overlap(z, zb, W, wb) || overlap(z, zb, A, (size_t)n_groups * 24) ||
+        overlap(z, zb, B, (size_t)n_groups * 16))
+        return GRKAN_ERR_INVALID_ARG;
+    // ---- validation done; HIP calls from here on
+    return from_hip(launch_layer_forward(x, A, B, W, z, rows, d_in, d_out, n_groups, stream));
+}
+
+extern "C" grkan_status_t grkan_linear_forward(const void *y, const void *W, void *z, int64_t rows,
+                                               int64_t d_in, int64_t d_out, hipStream_t stream) {
+    grkan_status_t st = layer_shape(rows, d_in, d_out);
+    if (st != GRKAN_OK) return st;
+    if (!W) return GRKAN_ERR_INVALID_ARG;
+    if (!aligned(W, 16)) return GRKAN_ERR_UNSUPPORTED;
+    if (rows == 0) return GRKAN_OK;
+    if (!y || !z) return GRKAN_ERR_INVALID_ARG;
+    if (!aligned(y, 16) || !aligned(z, 2)) return GRKAN_ERR_UNSUPPORTED;
+    const size_t yb = (size_t)rows * d_in * 2, zb = (size_t)rows * d_out * 2, wb = (size_t)d_out * d_in * 2;
+    if (overlap(z, zb, y, yb) || overlap(z, zb, W, wb)) return GRKAN_ERR_INVALID_ARG;
+    // ---- validation done; HIP calls from here on
+    return from_hip(launch_linear_forward(y, W, z, rows, d_in, d_out, stream));
+}
+
 extern "C" grkan_status_t grkan_inflated_forward(const void *x, void *y, const float *A,
                                                  const float *B, int64_t rows, int64_t d,
                                                  int32_t n_groups, grkan_dtype_t io, int32_t repeat,

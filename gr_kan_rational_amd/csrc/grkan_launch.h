@@ -132,6 +132,18 @@ hipError_t launch_merge(const float *partials, double *chunk_sums, int32_t n_gro
                         int32_t narrow_cpb, float *dA, float *dB, hipStream_t s);
 hipError_t launch_zero(float *dA, float *dB, int64_t na, int64_t nb, hipStream_t s);
 
+// The GR-KAN layer's linear map on MFMA (grkan_layer.hip), bf16 x / W / z:
+// z = F(x) W^T with F fused into the GEMM prologue (GR-KAN degrees), and the
+// plain z = y W^T.  Callers check: rows, d_out < 2^31, d_in a multiple of
+// layer_k_step(), d_in / n_groups a multiple of 8, n_groups at most
+// layer_max_groups(), 16-byte aligned x, y, W.
+int layer_max_groups();
+int layer_k_step();
+hipError_t launch_layer_forward(const void *x, const float *A, const float *B, const void *W, void *z,
+                                int64_t rows, int64_t d_in, int64_t d_out, int32_t n_groups, hipStream_t s);
+hipError_t launch_linear_forward(const void *y, const void *W, void *z, int64_t rows, int64_t d_in,
+                                 int64_t d_out, hipStream_t s);
+
 // Per-element-atomic baseline, GR-KAN degrees only (grkan_naive.hip).
 hipError_t launch_naive(grkan_dtype_t io, const void *x, const void *dy, void *dx, const float *A,
                         const float *B, float *dA, float *dB, int64_t rows, int64_t d,

@@ -1,0 +1,262 @@
+// grkan_layer.hip -- the GR-KAN layer's linear map on MFMA (gfx950): the
+// forward z = F(x) W^T with the group-rational activation F applied while the
+// A operand is staged (F fused into the GEMM prologue), and the plain GEMM
+// z = y W^T it replaces when F is applied by its own kernel.
+//
+// Pages cited
+//   [FlashKAT notes]  "FlashKAT: Understanding and Addressing Performance
+//                     Bottlenecks in the Kolmogorov-Arnold Transformer",
+//                     Paper-Notes page (AAAI 2026), arXiv 2505.13813.
+//
+// A GR-KAN layer applies the group-rational F to its d_in inputs and maps the
+// result linearly to d_out outputs: (2m + 2n + 3) d_in FLOPs of rational
+// against 2 d_in d_out of linear map per row ([FlashKAT notes], section
+// "1. 性能瓶颈诊断", Insight 2).  The pages print no bias; none is applied.
+// Precision: x, W and z are bf16, F is evaluated in fp32 exactly as the
+// activation kernels do and rounded to nearest-even bf16 as the MFMA operand,
+// products accumulate in fp32, z is rounded to nearest-even bf16.
+//
+// Kernel shape (both variants).  C[M][N] = A[M][K] B[N][K]^T with both
+// operands K-contiguous (x row-major [rows][d_in], W row-major
+// [d_out][d_in]).  Workgroup tile 256 x 256, 8 waves as 4 x 2, wave tile
+// 64 x 128 = 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators
+// per lane, 2 waves per SIMD).  K advances 64 at a time through two LDS
+// stages of [256 + 256][64 + 8] bf16 (rows padded by 16 bytes so that a
+// fragment read by 8 consecutive rows touches 8 distinct bank groups; 144 KB
+// in all).  The tiles of step k + 1 arrive in registers during step k - 1
+// (their loads are issued at the end of the previous step, so a whole step
+// of MFMAs covers their latency) and are written to the other stage one
+// 16-byte chunk per thread after each of step k's four MFMA sub-steps; each
+// lane's MFMA fragments (8 consecutive k of one row) are read one sub-step
+// ahead.  Fused variant: the activation runs on each staged x chunk between
+// the registers and the LDS write -- a thread's chunks lie in one channel
+// group (d_in / n_groups a multiple of 8), whose coefficients come from an
+// LDS table -- interleaved with the MFMAs.
+// Workgroup order: XCD (b mod 8) takes whole 256-row panels, N tiles of a
+// panel back to back, so a panel of x is fetched into one XCD's L2 once.
+//
+// Measured on MI355X (KAT-B MLP shapes, 201,728 rows, 951.9 GFLOP per
+// call): the plain GEMM runs at 900-1,040 TFLOP/s; the fused prologue costs
+// 0.45 ms (d_out = 3072) and 0.48 ms (d_out = 768) more than the plain GEMM,
+// because evaluating F costs ~15 VALU instructions per element and every
+// 256-wide N tile evaluates it again: at this tile width the activation's
+// vector work is as large as the tile's matrix work (a CU issues ~4,000 bf16
+// MFMA FLOPs but only 64 vector lanes per cycle), and the two overlap only in
+// part.  Wider N tiles need more accumulator registers than a SIMD holds at
+// 256 rows.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+
+#include "grkan_device.h"
+#include "grkan_launch.h"
+
+namespace grkan {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kWavesM = 4, kWavesN = 2;
+constexpr int kThreads = kWavesM * kWavesN * 64;
+constexpr int kLdk = kBK + 8;                         // padded LDS row, bf16 elements
+constexpr int kWTM = kBM / kWavesM, kWTN = kBN / kWavesN;
+constexpr int kTM = kWTM / 32, kTN = kWTN / 32;       // MFMA blocks per wave
+constexpr int kChunksPerRow = kBK / 8;                // 16-byte chunks per tile row
+constexpr int kCA = kBM * kChunksPerRow / kThreads;   // A chunks per thread per step
+constexpr int kCB = kBN * kChunksPerRow / kThreads;
+constexpr int kStage = (kBM + kBN) * kLdk;            // bf16 elements per LDS stage
+constexpr size_t kLdsBytes = 2 * (size_t)kStage * 2;
+constexpr int kKSteps = kBK / 16;
+constexpr int kInterleave = 14;                       // VALU instructions scheduled per MFMA (fused)
+static_assert(kBM * kChunksPerRow % kThreads == 0 && kBN * kChunksPerRow % kThreads == 0, "chunks");
+static_assert(kCA == kKSteps && kCB == kKSteps, "one chunk of each tile is staged per K sub-step");
+static_assert(kThreads % kChunksPerRow == 0, "a thread's chunks share one column");
+
+struct LayerArgs {
+    const uint16_t *x;  // [M][K] bf16 (activation input, or y for the plain GEMM)
+    const uint16_t *w;  // [N][K] bf16
+    uint16_t *z;        // [M][N] bf16
+    const float *A;     // [n_groups][6] (fused variant)
+    const float *B;     // [n_groups][4]
+    int32_t M, N, K, d_g, n_groups;
+};
+
+// The coefficient table: group g at [g * 12]: a_0..a_5, b_1..b_4.
+constexpr int kMaxLayerGroups = 64;
+
+__device__ static inline u32x4 activate8(u32x4 v, const Coefs<5, 4> &c) {
+    float f[8];
+    Io<bf16io>::unpack(v, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = rational<5, 4>(f[e], c);
+    return Io<bf16io>::pack(f);
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    __shared__ float coef[kMaxLayerGroups * 12];
+    const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int wm = wv / kWavesN, wn = wv % kWavesN;
+    const int nb_count = (a.N + kBN - 1) / kBN;
+    const int b = (int)blockIdx.x, xcd = b & 7, idx = b >> 3;
+    const int m0 = ((idx / nb_count) * 8 + xcd) * kBM, n0 = (idx % nb_count) * kBN;
+    if (m0 >= a.M) return;
+    if (FUSED) {
+        for (int i = t; i < a.n_groups * 12; i += kThreads) {
+            const int g = i / 12, k = i % 12;
+            coef[i] = k < 6 ? a.A[g * 6 + k] : (k < 10 ? a.B[g * 4 + k - 6] : 0.0f);
+        }
+    }
+
+    // Source rows of this thread's chunks.  Rows past the end are clamped to
+    // the last row: they only feed outputs that are never stored.
+    const int cc = t % kChunksPerRow;
+    const uint16_t *pa[kCA];
+    const uint16_t *pb[kCB];
+#pragma unroll
+    for (int j = 0; j < kCA; ++j) {
+        const int r = (t + kThreads * j) / kChunksPerRow;
+        pa[j] = a.x + (size_t)min(m0 + r, a.M - 1) * a.K + cc * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < kCB; ++j) {
+        const int r = (t + kThreads * j) / kChunksPerRow;
+        pb[j] = a.w + (size_t)min(n0 + r, a.N - 1) * a.K + cc * 8;
+    }
+    u32x4 ra[kCA], rb[kCB];
+    auto load_tiles = [&](int kt) {
+#pragma unroll
+        for (int j = 0; j < kCA; ++j) ra[j] = *reinterpret_cast<const u32x4 *>(pa[j] + kt * kBK);
+#pragma unroll
+        for (int j = 0; j < kCB; ++j) rb[j] = *reinterpret_cast<const u32x4 *>(pb[j] + kt * kBK);
+    };
+    Coefs<5, 4> c;
+    auto load_coefs_of = [&](int kt) {
+        const int g = (kt * kBK + cc * 8) / a.d_g;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) c.a[i] = coef[g * 12 + i];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c.b[i] = coef[g * 12 + 6 + i];
+    };
+    // Chunk j of this thread's share of both tiles -> LDS stage buf.
+    auto stage_chunk = [&](int buf, int j) {
+        if (FUSED) ra[j] = activate8(ra[j], c);
+        uint16_t *s = lds + buf * kStage;
+        const int r = (t + kThreads * j) / kChunksPerRow;
+        *reinterpret_cast<u32x4 *>(s + r * kLdk + cc * 8) = ra[j];
+        *reinterpret_cast<u32x4 *>(s + (kBM + r) * kLdk + cc * 8) = rb[j];
+    };
+
+    f32x16 acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) acc[i][j] = f32x16{};
+    bf16x8 fa[2][kTM], fb[2][kTN];
+    auto load_fragments = [&](int buf, int ks, int set) {
+        const uint16_t *s = lds + buf * kStage;
+        const int ko = ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+            fa[set][i] = *reinterpret_cast<const bf16x8 *>(s + (wm * kWTM + i * 32 + (lane & 31)) * kLdk + ko);
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+            fb[set][j] = *reinterpret_cast<const bf16x8 *>(s + (kBM + wn * kWTN + j * 32 + (lane & 31)) * kLdk + ko);
+    };
+
+    const int nk = a.K / kBK;
+    load_tiles(0);
+    __syncthreads();  // coefficient table
+    if (FUSED) load_coefs_of(0);
+#pragma unroll
+    for (int j = 0; j < kKSteps; ++j) stage_chunk(0, j);
+    if (nk > 1) load_tiles(1);
+    __syncthreads();
+    load_fragments(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (FUSED && more) load_coefs_of(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+            const int set = ks & 1;
+            if (ks + 1 < kKSteps) load_fragments(cur, ks + 1, set ^ 1);
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+            if (more) stage_chunk(cur ^ 1, ks);
+            if (FUSED) {
+#pragma unroll
+                for (int q = 0; q < kTM * kTN; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, kInterleave, 0);  // then VALU
+                }
+            }
+        }
+        if (kt + 2 < nk) load_tiles(kt + 2);
+        __syncthreads();
+        if (more) load_fragments(cur ^ 1, 0, 0);
+    }
+
+    // bf16 results; full tiles skip the range checks.
+    const bool full = m0 + kBM <= a.M && n0 + kBN <= a.N;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int col = n0 + wn * kWTN + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + wm * kWTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (full || (row < a.M && col < a.N)) {
+                    const __bf16 h = (__bf16)acc[i][j][v];
+                    a.z[(size_t)row * a.N + col] = __builtin_bit_cast(uint16_t, h);
+                }
+            }
+        }
+}
+
+std::once_flag g_attr_once[2];
+hipError_t g_attr_err[2];
+
+template <bool FUSED>
+hipError_t launch(const LayerArgs &a, hipStream_t s) {
+    auto kern = grkan_layer_gemm_kernel<FUSED>;
+    std::call_once(g_attr_once[FUSED], [&] {
+        g_attr_err[FUSED] = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    });
+    if (g_attr_err[FUSED] != hipSuccess) return g_attr_err[FUSED];
+    const int64_t mb = (a.M + kBM - 1) / kBM, nb = (a.N + kBN - 1) / kBN;
+    const int64_t grid = (mb + 7) / 8 * 8 * nb;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int layer_max_groups() { return kMaxLayerGroups; }
+int layer_k_step() { return kBK; }
+
+hipError_t launch_layer_forward(const void *x, const float *A, const float *B, const void *W, void *z,
+                                int64_t rows, int64_t d_in, int64_t d_out, int32_t n_groups, hipStream_t s) {
+    LayerArgs a{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(W), static_cast<uint16_t *>(z),
+                A, B, (int32_t)rows, (int32_t)d_out, (int32_t)d_in, (int32_t)(d_in / n_groups), n_groups};
+    return launch<true>(a, s);
+}
+
+hipError_t launch_linear_forward(const void *y, const void *W, void *z, int64_t rows, int64_t d_in,
+                                 int64_t d_out, hipStream_t s) {
+    LayerArgs a{static_cast<const uint16_t *>(y), static_cast<const uint16_t *>(W), static_cast<uint16_t *>(z),
+                nullptr, nullptr, (int32_t)rows, (int32_t)d_out, (int32_t)d_in, 1, 1};
+    return launch<false>(a, s);
+}
+
+}  // namespace grkan

@@ -27,9 +27,18 @@ uses the same recipe with A [n_g, m+1] and B [n_g, n]:
     kat-b-poly5     [1024, 197, 768]  fp32  n_g = 8,   (m, n) = (5, 0)  seed 9
     kat-b-perchan   [1024, 197, 768]  fp32  n_g = 768, (m, n) = (5, 4)  seed 10 (one PAU per channel)
 
+A GR-KAN layer (the activation followed by its linear map, bf16) adds the
+weight W [d_out, d] ~ N(0, 1/sqrt(d)) (a fan-in scaled normal; the pages give
+no initialisation for it), rounded to bf16:
+
+    kat-b-layer1-bf16  X [1024, 197, 768]  -> 3072 outputs, n_g = 8  seed 11
+    kat-b-layer2-bf16  X [1024, 197, 3072] -> 768 outputs,  n_g = 8  seed 12
+
+(the two GR-KAN layers of a KAT-B MLP block).
+
 Recipe (reproducible, independent of the number of threads):
-  * A then B from ``numpy.random.default_rng(seed)`` as float32 standard
-    normals, multiplied by the std in float32;
+  * A then B (then W, for a layer) from ``numpy.random.default_rng(seed)``
+    as float32 standard normals, multiplied by the std in float32;
   * X and dY in fixed chunks of 2**22 elements of the row-major tensor;
     chunk k of tensor t (t = 1 for X, 2 for dY) comes from
     ``PCG64(SeedSequence(seed, spawn_key=(t, k)))`` as float32 standard
@@ -64,6 +73,7 @@ class Workload:
     identity_group0: bool = False
     m: int = 5         # numerator degree (a_0..a_m)
     n: int = 4         # denominator degree (b_1..b_n)
+    d_out: int = 0     # outputs of the layer's linear map (0: the activation alone)
 
     @property
     def rows(self) -> int:
@@ -99,18 +109,21 @@ WORKLOADS = {
         Workload("kat-b-r76", 1024, 197, 768, 8, "f32", 0.5, 1.0, 1e-2, 8, m=7, n=6),
         Workload("kat-b-poly5", 1024, 197, 768, 8, "f32", 0.5, 1.0, 1e-2, 9, m=5, n=0),
         Workload("kat-b-perchan", 1024, 197, 768, 768, "f32", 0.5, 1.0, 1e-2, 10),
+        Workload("kat-b-layer1-bf16", 1024, 197, 768, 8, "bf16", 0.5, 1.0, 1e-2, 11, d_out=3072),
+        Workload("kat-b-layer2-bf16", 1024, 197, 3072, 8, "bf16", 0.5, 1.0, 1e-2, 12, d_out=768),
     )
 }
 
 # The GR-KAN workloads (degrees (5, 4), 8 groups) and the PAU-family ones.
 GRKAN_WORKLOADS = ("tiny", "kat-t", "kat-s-hid", "kat-b", "kat-b-hid-bf16")
 PAU_WORKLOADS = ("kat-b-pau", "kat-b-r32", "kat-b-r76", "kat-b-poly5", "kat-b-perchan")
+LAYER_WORKLOADS = ("kat-b-layer1-bf16", "kat-b-layer2-bf16")
 
 
 def custom(name: str, rows: int, d: int, n_groups: int, m: int = 5, n: int = 4, io: str = "f32",
-           seed: int = 100, coef_std: float = 0.5, dy_std: float = 1e-2) -> Workload:
+           seed: int = 100, coef_std: float = 0.5, dy_std: float = 1e-2, d_out: int = 0) -> Workload:
     """A workload of the same recipe with any shape, group count and degrees."""
-    return Workload(name, rows, 1, d, n_groups, io, coef_std, 1.0, dy_std, seed, m=m, n=n)
+    return Workload(name, rows, 1, d, n_groups, io, coef_std, 1.0, dy_std, seed, m=m, n=n, d_out=d_out)
 
 
 def _threads() -> int:
@@ -133,7 +146,7 @@ def bf16_to_f32(h: np.ndarray) -> np.ndarray:
     return (h.astype(np.uint32) << 16).view(np.float32)
 
 
-def coefficients(w: Workload) -> tuple[np.ndarray, np.ndarray]:
+def _draws(w: Workload):
     rng = np.random.default_rng(w.seed)
     std = np.float32(w.coef_std)
     A = rng.standard_normal((w.n_groups, w.m + 1), dtype=np.float32) * std
@@ -141,7 +154,22 @@ def coefficients(w: Workload) -> tuple[np.ndarray, np.ndarray]:
     if w.identity_group0:
         A[0] = 0
         A[0, 1] = 1
-    return A.astype(np.float32), B.astype(np.float32)
+    return rng, A.astype(np.float32), B.astype(np.float32)
+
+
+def coefficients(w: Workload) -> tuple[np.ndarray, np.ndarray]:
+    _, A, B = _draws(w)
+    return A, B
+
+
+def weight(w: Workload) -> np.ndarray:
+    """The layer's W [d_out, d] as bf16 bit patterns (uint16)."""
+    if w.d_out <= 0:
+        raise ValueError("not a layer workload")
+    rng, _, _ = _draws(w)
+    W = rng.standard_normal((w.d_out, w.d), dtype=np.float32)
+    W *= np.float32(1.0 / np.sqrt(w.d))
+    return bf16_bits(W).reshape(w.d_out, w.d)
 
 
 def _tensor(w: Workload, which: int, std: float, out: np.ndarray) -> None:
@@ -176,7 +204,8 @@ def make_inputs(w: Workload | str, rows: int | None = None, need_dy: bool = True
     """Inputs of workload `w` (optionally only its first `rows` rows).
 
     Returns ``{"A", "B", "x", "dy", "workload"}`` with x/dy shaped [rows, d]
-    (float32, or uint16 bf16 bit patterns when ``w.io == "bf16"``).
+    (float32, or uint16 bf16 bit patterns when ``w.io == "bf16"``), plus
+    ``"W"`` for a layer workload.
     """
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -193,4 +222,7 @@ def make_inputs(w: Workload | str, rows: int | None = None, need_dy: bool = True
         dy = np.empty(w.elements, dtype=dt)
         _tensor(w, 2, w.dy_std, dy)
         dy = dy.reshape(w.rows, w.d)
-    return {"A": A, "B": B, "x": x.reshape(w.rows, w.d), "dy": dy, "workload": w}
+    out = {"A": A, "B": B, "x": x.reshape(w.rows, w.d), "dy": dy, "workload": w}
+    if w.d_out > 0:
+        out["W"] = weight(w)
+    return out

@@ -219,6 +219,36 @@ GRKAN_API grkan_status_t grkan_inflated_backward(const void *x, const void *dy, 
                                        void *workspace, size_t workspace_bytes,
                                        hipStream_t stream);
 
+/*
+ * The GR-KAN layer ([FlashKAT notes], section "1. 性能瓶颈诊断", Insight 2:
+ * the activation's (2m+2n+3) d_in FLOPs feed a linear map of 2 d_in d_out):
+ * z = F(x) W^T, GR-KAN degrees (5, 4), no bias (the pages print none).
+ * bf16 throughout: F is evaluated in fp32 as grkan_forward does, rounded to
+ * nearest-even bf16 and multiplied on the matrix cores with fp32
+ * accumulation; z is rounded to nearest-even bf16.  F is applied while x is
+ * staged for the matrix product, so F(x) never goes to memory.
+ *   x         bf16 [rows][d_in], 16-byte aligned (may be NULL when rows == 0).
+ *   A, B      fp32 [n_groups][6], [n_groups][4], 4-byte aligned.
+ *   W         bf16 [d_out][d_in] (row o holds output o's weights), 16-byte aligned.
+ *   z         bf16 [rows][d_out], 2-byte aligned; must not overlap x, W, A, B.
+ *   rows >= 0 (0 is a no-op); d_in, d_out >= 1; d_in % n_groups == 0.
+ *   GRKAN_ERR_UNSUPPORTED: d_in not a multiple of 64, d_in / n_groups not a
+ *   multiple of 8, more than 64 groups, rows / d_in / d_out >= 2^31, or a
+ *   misaligned pointer.
+ */
+GRKAN_API grkan_status_t grkan_layer_forward(const void *x, const float *A, const float *B,
+                                   const void *W, void *z, int64_t rows, int64_t d_in,
+                                   int64_t d_out, int32_t n_groups, hipStream_t stream);
+
+/*
+ * The same linear map without the activation: z = y W^T, bf16 y [rows][d_in]
+ * (16-byte aligned), W and z as above, the same matrix-core kernel and
+ * limits.  With y = grkan_forward(x) (bf16) it is the unfused form of
+ * grkan_layer_forward and gives the same bits.
+ */
+GRKAN_API grkan_status_t grkan_linear_forward(const void *y, const void *W, void *z, int64_t rows,
+                                    int64_t d_in, int64_t d_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,12 @@ Tolerances (fixed here, used by every parity test):
   running sum wanders on the scale of ||t||_2 leaves an error of about
   2^-24 * sqrt(n / 2) * ||t||_2; this scheme does not meet the default
   scheme's bound at large n, which is the pages' point about atomics.
+* The bf16 GR-KAN layer z = bf16(F(x)) W^T (oracle/layer.py):
+  |gpu - ref| <= amb + gamma * mag + ulp_bf16(|ref| + amb + gamma * mag),
+  gamma = K * 2^-24.  amb covers elements whose bf16 rounding of F is not
+  unique at fp32 accuracy (either neighbour is a correct operand), gamma *
+  mag bounds fp32 accumulation of K exact bf16 products (mag = sum of their
+  absolute values), and one bf16 unit covers the rounding of z.
 """
 from __future__ import annotations
 
@@ -101,3 +107,20 @@ def check_sums(name: str, gpu: np.ndarray, ref: np.ndarray, norm: np.ndarray,
                              f"gpu={gpu[bad][:8].tolist()} ref={ref[bad][:8].tolist()} "
                              f"tol={tol[bad][:8].tolist()}")
     return stats
+
+
+def check_layer(name: str, gpu: np.ndarray, ref: dict, k: int) -> dict:
+    """Elementwise layer check; returns statistics, raises on a failure."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    z, amb, mag = ref["z"], ref["amb"], ref["mag"]
+    slack = amb + k * 2.0 ** -24 * mag
+    tol = slack + ulp_bf16(np.abs(z) + slack)
+    err = np.abs(gpu - z)
+    bad = err > tol
+    st = {"n": int(gpu.size), "fail": int(np.count_nonzero(bad)),
+          "max_err_over_tol": float(np.max(err / np.maximum(tol, 1e-300))) if gpu.size else 0.0}
+    if st["fail"]:
+        i = int(np.flatnonzero(bad.ravel())[0])
+        raise AssertionError(f"{name}: {st['fail']} of {st['n']} outside tolerance; first at {i}: "
+                             f"gpu {gpu.ravel()[i]!r} ref {z.ravel()[i]!r} tol {tol.ravel()[i]!r}")
+    return st

@@ -40,7 +40,8 @@ def test_header_declares_the_abi():
         "grkan_status_string", "grkan_query_launch",
         "grkan_pau_supported", "grkan_pau_forward", "grkan_pau_backward",
         "grkan_pau_backward_workspace_size", "grkan_pau_query_launch",
-        "grkan_inflated_forward", "grkan_inflated_backward"])
+        "grkan_inflated_forward", "grkan_inflated_backward",
+        "grkan_layer_forward", "grkan_linear_forward"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -235,3 +236,44 @@ def test_inflated_limits(lib, repeat):
     assert ibwd(lib, repeat, flags=NAIVE) == UNSUPPORTED
     # the plain kernels still take those (validation passes on to the device)
     assert fwd(lib, d=40, rows=0, x=None, y=None) == OK
+
+
+# ------------------------------------------------------------------ the layer
+
+def lfwd(lib, x=P, A=P + 0x200000, B=P + 0x300000, W=P + 0x400000, z=P + 0x800000, rows=4, d_in=256,
+         d_out=32, n_g=8):
+    return lib.grkan_layer_forward(x, A, B, W, z, rows, d_in, d_out, n_g, None)
+
+
+def linfwd(lib, y=P, W=P + 0x400000, z=P + 0x800000, rows=4, d_in=256, d_out=32):
+    return lib.grkan_linear_forward(y, W, z, rows, d_in, d_out, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), INVALID), (dict(B=None), INVALID), (dict(W=None), INVALID), (dict(x=None), INVALID),
+    (dict(z=None), INVALID), (dict(rows=-1), INVALID), (dict(d_in=0), INVALID), (dict(d_out=0), INVALID),
+    (dict(n_g=0), INVALID), (dict(n_g=3), INVALID),            # 256 % 3 != 0
+    (dict(d_in=96, n_g=8), UNSUPPORTED),                       # d_in not a multiple of 64
+    (dict(n_g=64, d_in=256), UNSUPPORTED),                     # 4-channel groups: not a multiple of 8
+    (dict(n_g=128, d_in=8192), UNSUPPORTED),                   # more than 64 groups
+    (dict(rows=1 << 31), UNSUPPORTED), (dict(d_out=1 << 31), UNSUPPORTED),
+    (dict(x=P + 8), UNSUPPORTED), (dict(W=P + 0x400008), UNSUPPORTED), (dict(z=P + 0x800001), UNSUPPORTED),
+    (dict(A=P + 0x200002), UNSUPPORTED),
+    (dict(z=P + 64), INVALID),                                 # z inside x
+    (dict(z=P + 0x400000 - 64), INVALID),                      # z runs into W
+])
+def test_layer_rejects(lib, kw, code):
+    assert lfwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), INVALID), (dict(y=None), INVALID), (dict(z=None), INVALID), (dict(rows=-1), INVALID),
+    (dict(d_in=96), UNSUPPORTED), (dict(y=P + 8), UNSUPPORTED), (dict(z=P + 64), INVALID),
+])
+def test_linear_rejects(lib, kw, code):
+    assert linfwd(lib, **kw) == code
+
+
+def test_layer_empty_is_ok_without_device(lib):
+    assert lfwd(lib, x=None, z=None, rows=0) == OK
+    assert linfwd(lib, y=None, z=None, rows=0) == OK

@@ -1,0 +1,138 @@
+"""GPU parity of the GR-KAN layer z = F(x) W^T (grkan_layer_forward: F fused
+into the matrix-core GEMM) and of the plain GEMM (grkan_linear_forward)
+against the fp64 layer oracle (oracle/layer.py), tolerances in
+tests/parity.py.  Shapes span several 256 x 256 tiles with ragged row and
+column tails, 8 to 64 groups, and the two KAT-B MLP layers at full size
+(sampled rows).  The fused layer must equal the unfused composition
+grkan_forward -> grkan_linear_forward bit for bit: both round the same fp32
+F to bf16 and run the same matrix kernel.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gr_kan_rational_amd import synth
+from oracle import layer
+from oracle import oracle as orc
+import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+# (rows, d_in, n_groups, d_out)
+SHAPES = [(301, 256, 8, 272), (257, 768, 8, 3072), (300, 3072, 8, 768), (513, 512, 64, 256),
+          (64, 128, 16, 48), (1, 64, 8, 1), (700, 1536, 24, 520)]
+
+
+@pytest.fixture(scope="module")
+def gk():
+    import gr_kan_rational_amd.binding as b
+
+    b.load_library()
+    return b
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def inputs(rows, d_in, n_g, d_out, seed):
+    w = synth.custom("layer", rows, d_in, n_g, io="bf16", seed=seed, d_out=d_out)
+    return synth.make_inputs(w, need_dy=False)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_layer_parity(gk, shape):
+    rows, d_in, n_g, d_out = shape
+    log(f"[layer] rows={rows} d_in={d_in} n_g={n_g} d_out={d_out}")
+    inp = inputs(rows, d_in, n_g, d_out, 6000 + rows)
+    x, W = bf(inp["x"]), bf(inp["W"])
+    A, B = torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV)
+    z = gk.grkan_layer_forward(x, A, B, W, n_g)
+    y = gk.grkan_forward(x, A, B, n_g)
+    z2 = gk.grkan_linear_forward(y, W)
+    torch.cuda.synchronize()
+    ref = layer.forward(inp["x"], inp["A"], inp["B"], inp["W"], n_g)
+    parity.check_layer(f"layer {shape}", host(z), ref, d_in)
+    assert torch.equal(z.view(torch.int16), z2.view(torch.int16)), "fused and unfused differ"
+
+
+@pytest.mark.parametrize("shape", [(301, 256, 272), (300, 3072, 768), (64, 64, 33)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_linear_parity(gk, shape):
+    rows, d_in, d_out = shape
+    log(f"[linear] rows={rows} d_in={d_in} d_out={d_out}")
+    inp = inputs(rows, d_in, 8, d_out, 6100 + rows)
+    z = gk.grkan_linear_forward(bf(inp["x"]), bf(inp["W"]))
+    torch.cuda.synchronize()
+    yv = orc.to_f64(inp["x"], "bf16")
+    wv = orc.to_f64(inp["W"], "bf16")
+    ref = {"z": yv @ wv.T, "amb": np.zeros((rows, d_out)), "mag": np.abs(yv) @ np.abs(wv).T}
+    parity.check_layer(f"linear {shape}", host(z), ref, d_in)
+
+
+def test_layer_special_values(gk):
+    """Identity numerators with b = 0 (F = x, so z = x W^T exactly up to accumulation), exact
+    zeros, a group at a root of Q, and an identity weight (z = bf16(F(x)))."""
+    rows, d_in, n_g = 96, 128, 8
+    inp = inputs(rows, d_in, n_g, d_in, 6200)
+    inp["x"][::4, :] = 0
+    inp["A"][1] = [0, 1, 0, 0, 0, 0]
+    inp["B"][1] = 0
+    inp["B"][2] = [-0.75, 1.0, 0.0, 0.0]
+    inp["x"][1::4, 32:48] = synth.bf16_bits(np.float32([0.75]))[0]
+    inp["W"] = synth.bf16_bits(np.eye(d_in, dtype=np.float32))
+    x, W = bf(inp["x"]), bf(inp["W"])
+    A, B = torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV)
+    z = gk.grkan_layer_forward(x, A, B, W, n_g)
+    y = gk.grkan_forward(x, A, B, n_g)
+    torch.cuda.synchronize()
+    ref = layer.forward(inp["x"], inp["A"], inp["B"], inp["W"], n_g)
+    parity.check_layer("layer special", host(z), ref, d_in)
+    # identity weight: z is the activation's own bf16 output
+    assert torch.equal(z.view(torch.int16), y.view(torch.int16))
+
+
+def test_layer_empty(gk):
+    inp = inputs(4, 64, 8, 16, 6300)
+    x = bf(inp["x"])[:0]
+    A, B = torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV)
+    z = gk.grkan_layer_forward(x, A, B, bf(inp["W"]), 8)
+    assert z.shape == (0, 16)
+
+
+def test_layer_rejects_unsupported(gk):
+    inp = inputs(4, 96, 8, 16, 6400)
+    A, B = torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV)
+    with pytest.raises(gk.GRKANError) as e:
+        gk.grkan_layer_forward(bf(inp["x"]), A, B, bf(inp["W"]), 8)   # d_in = 96
+    assert e.value.status == gk.GRKAN_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", list(synth.LAYER_WORKLOADS))
+def test_layer_full_size_sampled(gk, name):
+    """The KAT-B MLP layers at full size, in the benchmark's launch configuration: 48 sampled
+    rows (first, last, and spread over every row tile) against the oracle."""
+    w = synth.WORKLOADS[name]
+    log(f"[layer_full] {name}")
+    inp = synth.make_inputs(w, need_dy=False)
+    x, W = bf(inp["x"]), bf(inp["W"])
+    A, B = torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV)
+    z = gk.grkan_layer_forward(x, A, B, W, w.n_groups)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, w.rows - 1], rng.integers(0, w.rows, 46)]))
+    zs = host(z[torch.from_numpy(rows).to(DEV)])
+    ref = layer.forward(inp["x"][rows], inp["A"], inp["B"], inp["W"], w.n_groups)
+    parity.check_layer(f"{name} sampled rows", zs, ref, w.d)
