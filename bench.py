@@ -93,50 +93,68 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 
 
 def cpu_baseline_layer(w, target_s: float = 10.0) -> dict:
-    """fp64 layer oracle (bf16(F(x)) W^T) on the first rows of the workload."""
+    """fp64 layer oracle, forward (bf16(F(x)) W^T) and backward (dW, dx, dA, dB), on the
+    first rows of the workload."""
     from gr_kan_rational_amd import synth
     from oracle import layer, oracle
 
     Wb = synth.weight(w)
+
+    def run(rows):
+        inp = synth.make_inputs(w, rows=rows)
+        t0 = time.perf_counter()
+        layer.forward(inp["x"], inp["A"], inp["B"], Wb, w.n_groups)
+        layer.backward(inp["x"], inp["dz"], inp["A"], inp["B"], Wb, w.n_groups)
+        return time.perf_counter() - t0
+
     calib = 64
-    inp = synth.make_inputs(w, rows=calib, need_dy=False)
-    t0 = time.perf_counter()
-    layer.forward(inp["x"], inp["A"], inp["B"], Wb, w.n_groups)
-    dt = time.perf_counter() - t0
+    dt = run(calib)
     rows = int(min(w.rows, max(calib, calib * target_s / max(dt, 1e-3))))
-    inp = synth.make_inputs(w, rows=rows, need_dy=False)
-    t0 = time.perf_counter()
-    layer.forward(inp["x"], inp["A"], inp["B"], Wb, w.n_groups)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * w.d * w.d_out
+    dt = run(rows)
+    flops = 3 * 2.0 * rows * w.d * w.d_out
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"first {rows} of {w.rows} rows of {w.name}: F in fp64, bf16 rounding, fp64 "
-                      f"matrix product, {dt:.1f} s wall"}
+            "sample": f"first {rows} of {w.rows} rows of {w.name}: forward and backward, F in fp64 with bf16 "
+                      f"rounding, fp64 matrix products, {dt:.1f} s wall"}
 
 
 def bench_layer(args, w, gk, synth, dev, log) -> int:
-    """The GR-KAN layer forward z = F(x) W^T (bf16): F fused into the matrix-core GEMM
-    (grkan_layer_forward), against the unfused composition on the same GEMM kernel
-    (grkan_forward -> grkan_linear_forward) and, for context, grkan_forward followed by
-    torch's library GEMM."""
+    """The GR-KAN layer (bf16): a step is the forward z = F(x) W^T (grkan_layer_forward, F
+    fused into the matrix-core GEMM) and the backward (grkan_layer_backward: dW, dx, dA, dB);
+    three GEMMs of 2 rows d_in d_out FLOPs each.  `detail` compares the forward with its
+    unfused composition on the same GEMM kernel (grkan_forward -> grkan_linear_forward) and,
+    for context, with grkan_forward followed by torch's library GEMM."""
     import torch
 
     log(f"layer workload {w.name}: x [{w.batch},{w.seq},{w.d}] -> {w.d_out}, bf16: generating inputs")
-    inp = synth.make_inputs(w, need_dy=False)
+    inp = synth.make_inputs(w)
 
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    x, W = bf(inp["x"]), bf(inp["W"])
+    x, W, dz = bf(inp["x"]), bf(inp["W"]), bf(inp["dz"])
     A = torch.from_numpy(inp["A"]).to(dev)
     B = torch.from_numpy(inp["B"]).to(dev)
     del inp
     z = torch.empty((w.rows, w.d_out), dtype=torch.bfloat16, device=dev)
     y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    dA = torch.empty((w.n_groups, 6), dtype=torch.float32, device=dev)
+    dB = torch.empty((w.n_groups, 4), dtype=torch.float32, device=dev)
+    dW = torch.empty((w.d_out, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(gk.grkan_layer_backward_workspace_size(w.rows, w.d, w.d_out, w.n_groups),
+                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def fused():
         gk.grkan_layer_forward(x, A, B, W, w.n_groups, out=z, stream=stream)
+
+    def backward():
+        gk.grkan_layer_backward(x, dz, A, B, W, w.n_groups, dx=dx, dA=dA, dB=dB, dW=dW, workspace=ws,
+                                stream=stream)
+
+    def step():
+        fused()
+        backward()
 
     def unfused():
         gk.grkan_forward(x, A, B, w.n_groups, out=y, stream=stream)
@@ -156,13 +174,19 @@ def bench_layer(args, w, gk, synth, dev, log) -> int:
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
-        fused()
+        step()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    ms = timed(fused, args.steps)
-    flops = 2.0 * w.rows * w.d * w.d_out
+    ms = timed(step, args.steps)
+    gemm_flops = 2.0 * w.rows * w.d * w.d_out
+    flops = 3 * gemm_flops
     tflops = flops / (ms * 1e-3) / 1e12
+    fwd_ms = timed(fused, args.steps)
+    bwd_ms = timed(backward, args.steps)
     detail = {
+        "forward_ms": fwd_ms, "backward_ms": bwd_ms,
+        "forward_TFLOPs": gemm_flops / (fwd_ms * 1e-3) / 1e12,
+        "backward_TFLOPs": 2 * gemm_flops / (bwd_ms * 1e-3) / 1e12,
         "unfused_ms": timed(unfused, args.steps),
         "activation_ms": timed(lambda: gk.grkan_forward(x, A, B, w.n_groups, out=y, stream=stream), args.steps),
         "linear_ms": timed(lambda: gk.grkan_linear_forward(y, W, out=z, stream=stream), args.steps),
@@ -171,11 +195,13 @@ def bench_layer(args, w, gk, synth, dev, log) -> int:
         "device": torch.cuda.get_device_name(dev),
     }
     detail["torch_unfused_ms"] = detail["activation_ms"] + detail["torch_linear_ms"]
-    log(f"fused {ms:.4f} ms ({tflops:.1f} TFLOP/s); unfused {detail['unfused_ms']:.4f} ms; "
+    log(f"step {ms:.4f} ms ({tflops:.1f} TFLOP/s); forward (fused) {fwd_ms:.4f} ms, backward {bwd_ms:.4f} ms; "
+        f"unfused forward {detail['unfused_ms']:.4f} ms; "
         f"activation {detail['activation_ms']:.4f} + linear {detail['linear_ms']:.4f} ms; "
         f"torch linear {detail['torch_linear_ms']:.4f} ms")
     out = {
-        "metric": f"GR-KAN layer forward z = F(x) W^T (F fused into a bf16 matrix-core GEMM), workload {w.name}",
+        "metric": f"GR-KAN layer forward + backward TFLOP/s (bf16 matrix cores, F fused into the forward GEMM), "
+                  f"workload {w.name}",
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -189,10 +215,10 @@ def bench_layer(args, w, gk, synth, dev, log) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "shape": [w.batch, w.seq, w.d], "d_out": w.d_out,
                    "n_groups": w.n_groups, "degrees": [w.m, w.n], "io": "bf16"},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+        "roofline": {"bound": "mfma", "achieved": detail["forward_TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": detail["forward_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
                      "kernel": "grkan_layer_forward (grkan_layer_gemm_kernel, fused)",
-                     "algorithmic_flops_per_launch": flops},
+                     "algorithmic_flops_per_launch": gemm_flops},
         "detail": detail,
     }
     if not args.no_cpu_baseline:

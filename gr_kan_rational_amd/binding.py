@@ -85,6 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grkan_layer_forward.restype = ctypes.c_int
     lib.grkan_linear_forward.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.grkan_linear_forward.restype = ctypes.c_int
+    lib.grkan_layer_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+    lib.grkan_layer_backward.restype = ctypes.c_int
+    lib.grkan_layer_backward_workspace_size.argtypes = [i64, i64, i64, i32]
+    lib.grkan_layer_backward_workspace_size.restype = sz
     _lib = lib
     return lib
 
@@ -263,7 +267,7 @@ def grkan_inflated_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, 
                      pau=False, repeat=repeat)
 
 
-def _layer_out(x, W, out):
+def _layer_dims(x, W):
     if x.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
         raise TypeError("the layer takes bfloat16 x and W")
     if W.dim() != 2 or not W.is_contiguous() or W.device != x.device:
@@ -271,7 +275,11 @@ def _layer_out(x, W, out):
     rows, d_in = _rows_d(x)
     if W.shape[1] != d_in:
         raise ValueError("W's second dimension must be x's last")
-    d_out = W.shape[0]
+    return rows, d_in, W.shape[0]
+
+
+def _layer_out(x, W, out):
+    rows, d_in, d_out = _layer_dims(x, W)
     z = torch.empty((*x.shape[:-1], d_out), dtype=torch.bfloat16, device=x.device) if out is None else out
     if z.dtype != torch.bfloat16 or z.numel() != rows * d_out or not z.is_contiguous():
         raise ValueError("out must be a contiguous bfloat16 tensor of rows x d_out elements")
@@ -300,6 +308,39 @@ def grkan_linear_forward(y: torch.Tensor, W: torch.Tensor, out: torch.Tensor | N
     if st != GRKAN_OK:
         raise GRKANError(st, "grkan_linear_forward")
     return z
+
+
+def grkan_layer_backward_workspace_size(rows: int, d_in: int, d_out: int, n_groups: int = 8) -> int:
+    return int(load_library().grkan_layer_backward_workspace_size(rows, d_in, d_out, n_groups))
+
+
+def grkan_layer_backward(x: torch.Tensor, dz: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                         W: torch.Tensor, n_groups: int = 8, dx: torch.Tensor | None = None,
+                         dA: torch.Tensor | None = None, dB: torch.Tensor | None = None,
+                         dW: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         stream=None):
+    """(dx, dA, dB, dW) of the GR-KAN layer (``grkan_layer_backward``): bf16 x [..., d_in],
+    dz [..., d_out], W [d_out, d_in]; dx bf16, dA / dB / dW fp32."""
+    _check_coefs(A, B, n_groups, x.device)
+    rows, d_in, d_out = _layer_dims(x, W)
+    if dz.dtype != torch.bfloat16 or dz.numel() != rows * d_out or not dz.is_contiguous():
+        raise ValueError("dz must be a contiguous bfloat16 tensor of rows x d_out elements")
+    dx = torch.empty_like(x) if dx is None else dx
+    dA = torch.empty((n_groups, 6), dtype=torch.float32, device=x.device) if dA is None else dA
+    dB = torch.empty((n_groups, 4), dtype=torch.float32, device=x.device) if dB is None else dB
+    dW = torch.empty((d_out, d_in), dtype=torch.float32, device=x.device) if dW is None else dW
+    lib = load_library()
+    need = lib.grkan_layer_backward_workspace_size(rows, d_in, d_out, n_groups)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsp = _ptr(workspace) if workspace is not None else None
+    wsn = workspace.numel() if workspace is not None else 0
+    st = lib.grkan_layer_backward(_ptr(x), _ptr(dz), _ptr(A), _ptr(B), _ptr(W), _ptr(dx), _ptr(dA), _ptr(dB),
+                                  _ptr(dW), rows, d_in, d_out, n_groups, wsp, wsn,
+                                  ctypes.c_void_p(_stream(stream)))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_layer_backward")
+    return dx, dA, dB, dW
 
 
 def grkan_query_launch(rows: int, d: int, n_groups: int, io: int, pass_: int) -> dict:

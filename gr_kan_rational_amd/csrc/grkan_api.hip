@@ -486,6 +486,108 @@ extern "C" grkan_status_t grkan_linear_forward(const void *y, const void *W, voi
     return from_hip(launch_linear_forward(y, W, z, rows, d_in, d_out, stream));
 }
 
+// Layer backward workspace: W^T, one bf16 [rows][d_in] buffer (Y = F(x),
+// then dY), the activation backward's partials, the weight gradient's split
+// partials; each 256-byte aligned.
+namespace {
+
+struct LayerBwdPlan {
+    Plan act;
+    size_t off_wt, off_buf, off_act, off_wg, total;
+};
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+grkan_status_t layer_bwd_plan(int64_t rows, int64_t d_in, int64_t d_out, int32_t n_groups, LayerBwdPlan *lp) {
+    grkan_status_t st = layer_shape(rows, d_in, d_out);
+    if (st != GRKAN_OK) return st;
+    if (n_groups <= 0 || d_in % n_groups != 0) return GRKAN_ERR_INVALID_ARG;
+    if (n_groups > layer_max_groups() || (d_in / n_groups) % 8 != 0) return GRKAN_ERR_UNSUPPORTED;
+    if (d_out % layer_k_step() != 0) return GRKAN_ERR_UNSUPPORTED;
+    const DegreeOps *deg = find_degree(kGrkanM, kGrkanN);
+    st = plan_shape(rows > 0 ? rows : 1, d_in, n_groups, *deg, GRKAN_BF16, 1, false, &lp->act);
+    if (st != GRKAN_OK) return st;
+    lp->off_wt = 0;
+    lp->off_buf = align256((size_t)d_in * d_out * 2);
+    lp->off_act = lp->off_buf + align256((size_t)rows * d_in * 2);
+    lp->off_wg = lp->off_act + align256(workspace_need(lp->act));
+    lp->total = lp->off_wg + align256(wgrad_partials_bytes(rows, d_out, d_in));
+    return GRKAN_OK;
+}
+
+}  // namespace
+
+extern "C" size_t grkan_layer_backward_workspace_size(int64_t rows, int64_t d_in, int64_t d_out,
+                                                      int32_t n_groups) {
+    LayerBwdPlan lp;
+    if (rows <= 0 || layer_bwd_plan(rows, d_in, d_out, n_groups, &lp) != GRKAN_OK) return 0;
+    return lp.total;
+}
+
+extern "C" grkan_status_t grkan_layer_backward(const void *x, const void *dz, const float *A, const float *B,
+                                               const void *W, void *dx, float *dA, float *dB, float *dW,
+                                               int64_t rows, int64_t d_in, int64_t d_out, int32_t n_groups,
+                                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    LayerBwdPlan lp;
+    grkan_status_t st = layer_bwd_plan(rows, d_in, d_out, n_groups, &lp);
+    if (st != GRKAN_OK) return st;
+    if (!A || !B || !W || !dA || !dB || !dW) return GRKAN_ERR_INVALID_ARG;
+    if (!aligned(A, 4) || !aligned(B, 4) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(dW, 4) ||
+        !aligned(W, 16))
+        return GRKAN_ERR_UNSUPPORTED;
+    const size_t ab = (size_t)n_groups * 24, bb = (size_t)n_groups * 16, wb = (size_t)d_out * d_in * 2;
+    const size_t wgb = (size_t)d_out * d_in * 4;
+    const size_t xb = rows > 0 ? (size_t)rows * d_in * 2 : 0, zb = rows > 0 ? (size_t)rows * d_out * 2 : 0;
+    if (rows > 0) {
+        if (!x || !dz || !dx) return GRKAN_ERR_INVALID_ARG;
+        if (!aligned(x, 16) || !aligned(dz, 16) || !aligned(dx, 16)) return GRKAN_ERR_UNSUPPORTED;
+        // dx may be x itself (x is last read by the step that writes dx)
+        if (bad_alias(dx, x, xb) || overlap(dx, xb, dz, zb) || overlap(dx, xb, W, wb) ||
+            overlap(dx, xb, A, ab) || overlap(dx, xb, B, bb))
+            return GRKAN_ERR_INVALID_ARG;
+    }
+    const void *ins[] = {x, dz, W, A, B, dx};
+    const size_t insz[] = {xb, zb, wb, ab, bb, xb};
+    const void *outs[] = {dA, dB, dW};
+    const size_t outsz[] = {ab, bb, wgb};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (overlap(outs[o], outsz[o], ins[i], insz[i])) return GRKAN_ERR_INVALID_ARG;
+        for (int q = o + 1; q < 3; ++q)
+            if (overlap(outs[o], outsz[o], outs[q], outsz[q])) return GRKAN_ERR_INVALID_ARG;
+    }
+    if (rows > 0) {
+        if (!workspace || workspace_bytes < lp.total) return GRKAN_ERR_INVALID_ARG;
+        if (!aligned(workspace, 256)) return GRKAN_ERR_UNSUPPORTED;
+        for (int i = 0; i < 6; ++i)
+            if (overlap(workspace, lp.total, ins[i], insz[i])) return GRKAN_ERR_INVALID_ARG;
+        for (int o = 0; o < 3; ++o)
+            if (overlap(workspace, lp.total, outs[o], outsz[o])) return GRKAN_ERR_INVALID_ARG;
+    }
+
+    // ---- validation done; HIP calls from here on
+    if (rows == 0) {
+        st = from_hip(launch_zero(dA, dB, (int64_t)n_groups * 6, (int64_t)n_groups * 4, stream));
+        if (st != GRKAN_OK) return st;
+        return from_hip(launch_zero(dW, dW, (int64_t)d_out * d_in, 0, stream));
+    }
+    char *ws = static_cast<char *>(workspace);
+    void *wt = ws + lp.off_wt, *buf = ws + lp.off_buf;
+    // Y = F(x) (bf16), then dW = dz^T Y
+    st = forward_impl(x, buf, A, B, rows, d_in, n_groups, kGrkanM, kGrkanN, GRKAN_BF16, stream);
+    if (st != GRKAN_OK) return st;
+    st = from_hip(launch_wgrad(dz, buf, reinterpret_cast<float *>(ws + lp.off_wg), dW, rows, d_out, d_in, stream));
+    if (st != GRKAN_OK) return st;
+    // dY = dz W (bf16, over W^T so that both operands are K-contiguous), into the same buffer
+    st = from_hip(launch_transpose16(W, wt, d_out, d_in, stream));
+    if (st != GRKAN_OK) return st;
+    st = from_hip(launch_linear_forward(dz, wt, buf, rows, d_out, d_in, stream));
+    if (st != GRKAN_OK) return st;
+    // dx, dA, dB: the activation's backward on (x, dY), deterministic scheme
+    return backward_impl(x, buf, A, B, dx, dA, dB, rows, d_in, n_groups, kGrkanM, kGrkanN, GRKAN_BF16, 0,
+                         ws + lp.off_act, workspace_need(lp.act), stream);
+}
+
 extern "C" grkan_status_t grkan_inflated_forward(const void *x, void *y, const float *A,
                                                  const float *B, int64_t rows, int64_t d,
                                                  int32_t n_groups, grkan_dtype_t io, int32_t repeat,

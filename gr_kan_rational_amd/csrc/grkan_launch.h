@@ -143,6 +143,15 @@ hipError_t launch_layer_forward(const void *x, const float *A, const float *B, c
                                 int64_t rows, int64_t d_in, int64_t d_out, int32_t n_groups, hipStream_t s);
 hipError_t launch_linear_forward(const void *y, const void *W, void *z, int64_t rows, int64_t d_in,
                                  int64_t d_out, hipStream_t s);
+// Weight gradient dW [M][N] (fp32) = dz^T y for bf16 dz [rows][M], y [rows][N]
+// (M, N multiples of 8, 16-byte aligned rows), through fp32 split partials
+// [wgrad_splits][M][N] (wgrad_partials_bytes of scratch) and a fixed-order sum.
+int wgrad_splits(int64_t rows, int64_t M, int64_t N);
+size_t wgrad_partials_bytes(int64_t rows, int64_t M, int64_t N);
+hipError_t launch_wgrad(const void *dz, const void *y, float *partials, float *dW, int64_t rows, int64_t M,
+                        int64_t N, hipStream_t s);
+// out [C][R] = in [R][C]^T, bf16.
+hipError_t launch_transpose16(const void *in, void *out, int64_t R, int64_t C, hipStream_t s);
 
 // Per-element-atomic baseline, GR-KAN degrees only (grkan_naive.hip).
 hipError_t launch_naive(grkan_dtype_t io, const void *x, const void *dy, void *dx, const float *A,

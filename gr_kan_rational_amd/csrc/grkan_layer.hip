@@ -223,8 +223,174 @@ __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a)
         }
 }
 
-std::once_flag g_attr_once[2];
-hipError_t g_attr_err[2];
+// ------------------------------------------------------------ backward
+//
+// Weight gradient dW = dZ^T Y: P[s][m][n] = sum over the rows r of split s of
+// A[r][m] B[r][n] (A = dZ [rows][d_out], B = Y [rows][d_in], bf16), then a
+// fixed-order sum over the splits.  Here K = rows runs down the columns of
+// both operands, while an MFMA fragment wants 8 consecutive k of one m (or
+// n): each thread loads one 16-byte chunk (8 consecutive m) from each of 4
+// consecutive rows and writes it transposed -- for each of its 8 m, the 4
+// rows as one 8-byte LDS write -- into the same padded [m][k] layout the
+// forward kernel reads, so the MFMA loop is the forward's.  The rows are cut
+// into splits so that the few output tiles (36 at the KAT-B shapes) still
+// fill the GPU; each workgroup writes its fp32 tile of partial sums, and
+// grkan_wgrad_reduce_kernel adds the splits in order (bitwise reproducible).
+constexpr int kWgSplitsTarget = 1024;  // workgroups to aim for
+
+struct WgradArgs {
+    const uint16_t *a;   // [rows][M] bf16 (dZ)
+    const uint16_t *b;   // [rows][N] bf16 (Y = F(x))
+    float *partials;     // [splits][M][N]
+    int32_t rows, M, N, splits, rows_per_split;
+};
+
+__device__ static inline uint32_t pack2(uint32_t lo, uint32_t hi, int odd) {
+    // the bf16 at position odd (0 = low half) of lo and of hi, as (lo's, hi's)
+    return odd ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+}
+
+__global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int wm = wv / kWavesN, wn = wv % kWavesN;
+    const int mb_count = (a.M + kBM - 1) / kBM, nb_count = (a.N + kBN - 1) / kBN;
+    const int tiles = mb_count * nb_count;
+    const int b = (int)blockIdx.x;
+    const int split = b / tiles, tile = b % tiles;
+    const int m0 = (tile / nb_count) * kBM, n0 = (tile % nb_count) * kBN;
+    const int r_begin = split * a.rows_per_split;
+    const int r_end = min(a.rows, r_begin + a.rows_per_split);
+
+    // This thread's chunks: 8 consecutive columns (cc), rows 4 rg .. 4 rg + 3
+    // of each 64-row step.  A wave covers all 16 row groups of 4 column
+    // chunks: its transposed LDS writes then fall on distinct bank pairs
+    // except for a 2-way overlap (a wave spanning 32 column chunks instead
+    // would put them all on the same banks).  Columns past the end are
+    // clamped (their outputs are not stored); rows past the split's end read
+    // as zero.
+    constexpr int kRowGroups = kBK / 4;                 // 16
+    static_assert(kThreads / kRowGroups * 8 == kBM && kBM == kBN, "one 64-row step per thread set");
+    const int rg = t % kRowGroups, cc = t / kRowGroups;
+    const uint16_t *pa = a.a + min(m0 + cc * 8, a.M - 8);
+    const uint16_t *pb = a.b + min(n0 + cc * 8, a.N - 8);
+    u32x4 ra[4], rb[4];
+    auto load_tiles = [&](int kt) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = r_begin + kt * kBK + rg * 4 + q;
+            const bool in = r < r_end;
+            const size_t rr = (size_t)(in ? r : r_begin);
+            const u32x4 va = *reinterpret_cast<const u32x4 *>(pa + rr * a.M);
+            const u32x4 vb = *reinterpret_cast<const u32x4 *>(pb + rr * a.N);
+            ra[q] = in ? va : u32x4{0u, 0u, 0u, 0u};
+            rb[q] = in ? vb : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    // Columns 2h and 2h + 1 of the chunks -> LDS rows cc*8 + 2h, + 1, k = 4 rg .. 4 rg + 3.
+    auto stage_pair = [&](int buf, int h) {
+        uint16_t *s = lds + buf * kStage;
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+            const int col = cc * 8 + 2 * h + odd;
+            uint2 va, vb;
+            va.x = pack2(ra[0][h], ra[1][h], odd);
+            va.y = pack2(ra[2][h], ra[3][h], odd);
+            vb.x = pack2(rb[0][h], rb[1][h], odd);
+            vb.y = pack2(rb[2][h], rb[3][h], odd);
+            *reinterpret_cast<uint2 *>(s + col * kLdk + rg * 4) = va;
+            *reinterpret_cast<uint2 *>(s + (kBM + col) * kLdk + rg * 4) = vb;
+        }
+    };
+
+    f32x16 acc[kTM][kTN];
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) acc[i][j] = f32x16{};
+    bf16x8 fa[2][kTM], fb[2][kTN];
+    auto load_fragments = [&](int buf, int ks, int set) {
+        const uint16_t *s = lds + buf * kStage;
+        const int ko = ks * 16 + 8 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+            fa[set][i] = *reinterpret_cast<const bf16x8 *>(s + (wm * kWTM + i * 32 + (lane & 31)) * kLdk + ko);
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+            fb[set][j] = *reinterpret_cast<const bf16x8 *>(s + (kBM + wn * kWTN + j * 32 + (lane & 31)) * kLdk + ko);
+    };
+
+    const int nk = (r_end - r_begin + kBK - 1) / kBK;
+    if (nk > 0) {
+        load_tiles(0);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) stage_pair(0, h);
+        if (nk > 1) load_tiles(1);
+        __syncthreads();
+        load_fragments(0, 0, 0);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks) {
+            const int set = ks & 1;
+            if (ks + 1 < kKSteps) load_fragments(cur, ks + 1, set ^ 1);
+#pragma unroll
+            for (int i = 0; i < kTM; ++i)
+#pragma unroll
+                for (int j = 0; j < kTN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+            if (more) stage_pair(cur ^ 1, ks);
+        }
+        if (kt + 2 < nk) load_tiles(kt + 2);
+        __syncthreads();
+        if (more) load_fragments(cur ^ 1, 0, 0);
+    }
+
+    float *out = a.partials + (size_t)split * a.M * a.N;
+#pragma unroll
+    for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j) {
+            const int col = n0 + wn * kWTN + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = m0 + wm * kWTM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                if (row < a.M && col < a.N) out[(size_t)row * a.N + col] = acc[i][j][v];
+            }
+        }
+}
+
+// dW[i] = sum over s of partials[s][i], in split order, in fp64.
+__global__ __launch_bounds__(256) void grkan_wgrad_reduce_kernel(const float *__restrict__ partials,
+                                                                 float *__restrict__ dW, int64_t n, int splits) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    double s = 0.0;
+    for (int k = 0; k < splits; ++k) s += (double)partials[(size_t)k * n + i];
+    dW[i] = (float)s;
+}
+
+// out[c][r] = in[r][c] for a [R][C] bf16 matrix, 32 x 32 tiles through LDS.
+__global__ __launch_bounds__(256) void grkan_transpose16_kernel(const uint16_t *__restrict__ in,
+                                                                uint16_t *__restrict__ out, int R, int C) {
+    __shared__ uint16_t tile[32][33];
+    const int c0 = blockIdx.x * 32, r0 = blockIdx.y * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+    for (int k = ty; k < 32; k += 8) {
+        const int r = r0 + k, c = c0 + tx;
+        if (r < R && c < C) tile[k][tx] = in[(size_t)r * C + c];
+    }
+    __syncthreads();
+    for (int k = ty; k < 32; k += 8) {
+        const int c = c0 + k, r = r0 + tx;
+        if (r < R && c < C) out[(size_t)c * R + r] = tile[tx][k];
+    }
+}
+
+std::once_flag g_attr_once[3];
+hipError_t g_attr_err[3];
 
 template <bool FUSED>
 hipError_t launch(const LayerArgs &a, hipStream_t s) {
@@ -250,6 +416,48 @@ hipError_t launch_layer_forward(const void *x, const float *A, const float *B, c
     LayerArgs a{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(W), static_cast<uint16_t *>(z),
                 A, B, (int32_t)rows, (int32_t)d_out, (int32_t)d_in, (int32_t)(d_in / n_groups), n_groups};
     return launch<true>(a, s);
+}
+
+int wgrad_splits(int64_t rows, int64_t M, int64_t N) {
+    const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    const int64_t steps = (rows + kBK - 1) / kBK;
+    int64_t splits = (kWgSplitsTarget + tiles - 1) / tiles;
+    if (splits > steps) splits = steps;
+    return (int)(splits < 1 ? 1 : splits);
+}
+
+size_t wgrad_partials_bytes(int64_t rows, int64_t M, int64_t N) {
+    return (size_t)wgrad_splits(rows, M, N) * (size_t)M * (size_t)N * sizeof(float);
+}
+
+hipError_t launch_wgrad(const void *dz, const void *y, float *partials, float *dW, int64_t rows, int64_t M,
+                        int64_t N, hipStream_t s) {
+    auto kern = grkan_wgrad_kernel;
+    std::call_once(g_attr_once[2], [&] {
+        g_attr_err[2] = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    });
+    if (g_attr_err[2] != hipSuccess) return g_attr_err[2];
+    const int splits = wgrad_splits(rows, M, N);
+    const int64_t steps = (rows + kBK - 1) / kBK;
+    const int rps = (int)((steps + splits - 1) / splits) * kBK;
+    WgradArgs a{static_cast<const uint16_t *>(dz), static_cast<const uint16_t *>(y), partials, (int32_t)rows,
+                (int32_t)M, (int32_t)N, splits, rps};
+    const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * splits)), dim3(kThreads), kLdsBytes, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t n = M * N;
+    hipLaunchKernelGGL(grkan_wgrad_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, partials, dW,
+                       n, splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose16(const void *in, void *out, int64_t R, int64_t C, hipStream_t s) {
+    hipLaunchKernelGGL(grkan_transpose16_kernel, dim3((unsigned)((C + 31) / 32), (unsigned)((R + 31) / 32)),
+                       dim3(256), 0, s, static_cast<const uint16_t *>(in), static_cast<uint16_t *>(out), (int)R,
+                       (int)C);
+    return hipGetLastError();
 }
 
 hipError_t launch_linear_forward(const void *y, const void *W, void *z, int64_t rows, int64_t d_in,

@@ -34,13 +34,15 @@ no initialisation for it), rounded to bf16:
     kat-b-layer1-bf16  X [1024, 197, 768]  -> 3072 outputs, n_g = 8  seed 11
     kat-b-layer2-bf16  X [1024, 197, 3072] -> 768 outputs,  n_g = 8  seed 12
 
-(the two GR-KAN layers of a KAT-B MLP block).
+(the two GR-KAN layers of a KAT-B MLP block).  Their backward takes the
+upstream gradient dZ [rows, d_out] ~ N(0, 1e-2) (tensor 3 below) in place of
+dY.
 
 Recipe (reproducible, independent of the number of threads):
   * A then B (then W, for a layer) from ``numpy.random.default_rng(seed)``
     as float32 standard normals, multiplied by the std in float32;
   * X and dY in fixed chunks of 2**22 elements of the row-major tensor;
-    chunk k of tensor t (t = 1 for X, 2 for dY) comes from
+    chunk k of tensor t (t = 1 for X, 2 for dY, 3 for a layer's dZ) comes from
     ``PCG64(SeedSequence(seed, spawn_key=(t, k)))`` as float32 standard
     normals times the std in float32;
   * bf16 tensors are those float32 draws rounded to nearest-even bf16 and
@@ -204,8 +206,8 @@ def make_inputs(w: Workload | str, rows: int | None = None, need_dy: bool = True
     """Inputs of workload `w` (optionally only its first `rows` rows).
 
     Returns ``{"A", "B", "x", "dy", "workload"}`` with x/dy shaped [rows, d]
-    (float32, or uint16 bf16 bit patterns when ``w.io == "bf16"``), plus
-    ``"W"`` for a layer workload.
+    (float32, or uint16 bf16 bit patterns when ``w.io == "bf16"``); a layer
+    workload has ``"W"`` [d_out, d] and, in place of dy, ``"dz"`` [rows, d_out].
     """
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -218,11 +220,15 @@ def make_inputs(w: Workload | str, rows: int | None = None, need_dy: bool = True
     x = np.empty(w.elements, dtype=dt)
     _tensor(w, 1, w.x_std, x)
     dy = None
-    if need_dy:
+    if need_dy and w.d_out == 0:
         dy = np.empty(w.elements, dtype=dt)
         _tensor(w, 2, w.dy_std, dy)
         dy = dy.reshape(w.rows, w.d)
     out = {"A": A, "B": B, "x": x.reshape(w.rows, w.d), "dy": dy, "workload": w}
     if w.d_out > 0:
         out["W"] = weight(w)
+        if need_dy:
+            dz = np.empty(w.rows * w.d_out, dtype=dt)
+            _tensor(w, 3, w.dy_std, dz)
+            out["dz"] = dz.reshape(w.rows, w.d_out)
     return out

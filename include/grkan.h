@@ -249,6 +249,32 @@ GRKAN_API grkan_status_t grkan_layer_forward(const void *x, const float *A, cons
 GRKAN_API grkan_status_t grkan_linear_forward(const void *y, const void *W, void *z, int64_t rows,
                                     int64_t d_in, int64_t d_out, hipStream_t stream);
 
+/*
+ * Backward of grkan_layer_forward: given dz = dL/dz (bf16 [rows][d_out]),
+ *   dW = dz^T bf16(F(x))       fp32 [d_out][d_in]
+ *   dy = bf16(dz W)            (bf16, internal)
+ *   dx, dA, dB                 the activation's backward on (x, dy), as
+ *                              grkan_backward computes them (bf16 dx,
+ *                              deterministic two-stage sums for dA, dB)
+ * all on the matrix cores except the activation's own kernels.  dW sums over
+ * all rows: fixed-size row splits are summed in fp32 on the matrix cores and
+ * the splits in a fixed order in fp64, so the result is bitwise reproducible.
+ *   dx may be x itself; every other output must overlap nothing.
+ *   workspace: grkan_layer_backward_workspace_size() bytes, 256-byte aligned.
+ *   Limits as grkan_layer_forward, and d_out a multiple of 64.
+ *   rows == 0 writes zeros to dA, dB, dW.
+ */
+GRKAN_API grkan_status_t grkan_layer_backward(const void *x, const void *dz, const float *A,
+                                    const float *B, const void *W, void *dx, float *dA,
+                                    float *dB, float *dW, int64_t rows, int64_t d_in,
+                                    int64_t d_out, int32_t n_groups, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace grkan_layer_backward needs (0 for rows <= 0 or
+ * arguments it would reject).  Host-only. */
+GRKAN_API size_t grkan_layer_backward_workspace_size(int64_t rows, int64_t d_in, int64_t d_out,
+                                           int32_t n_groups);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,16 @@ between two bf16 values, both neighbours are correct roundings.  Such
 elements are flagged, and ``amb`` bounds what choosing the other neighbour
 can change in z.  ``mag`` = sum |bf16(F)| |W| scales the fp32 accumulation
 error.
+
+Backward.  With dz = dL/dz (bf16), the chain rule through z = bf16(F) W^T
+gives the weight gradient dW = dz^T bf16(F(x)) and dL/dF = dz W.  The GPU
+rounds dz W (accumulated in fp32) to bf16 before the activation's backward,
+as a bf16 layer does; the oracle does the same from the fp64 product and
+flags the elements whose fp64 product lies within fp32 accumulation error
+(d_out 2^-24 sum |dz||W|) of a bf16 rounding boundary.  dx, dA, dB are then
+the activation oracle's backward at dy = bf16(dz W); for the flagged elements
+``dx_amb``, ``dA_amb``, ``dB_amb`` bound what the other admissible rounding
+changes (dx and the terms are linear in dy).
 """
 from __future__ import annotations
 
@@ -74,3 +84,60 @@ def forward(x_bits: np.ndarray, A, B, W_bits: np.ndarray, n_groups: int) -> dict
     aw = np.abs(W)
     return {"z": fb @ W.T, "amb": width @ aw.T, "mag": np.abs(fb) @ aw.T,
             "n_ambiguous": int(np.count_nonzero(width))}
+
+
+def bf16_bits(values: np.ndarray) -> np.ndarray:
+    """uint16 bit patterns of values that are exactly representable in bf16."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    f = v.astype(np.float32)
+    if not np.array_equal(f.astype(np.float64), v):
+        raise ValueError("not bf16 values")
+    b = f.view(np.uint32)
+    if np.any(b & 0xFFFF):
+        raise ValueError("not bf16 values")
+    return (b >> 16).astype(np.uint16)
+
+
+def upstream(dz_bits: np.ndarray, W_bits: np.ndarray):
+    """(bf16(dz W), ambiguity width) for bf16 dz [rows, d_out], W [d_out, d_in]."""
+    dz = bf16_value(dz_bits)
+    W = bf16_value(W_bits)
+    k = W.shape[0]
+    dy = dz @ W
+    err = k * 2.0 ** -24 * (np.abs(dz) @ np.abs(W))
+    lo, hi = bf16_round(dy - err), bf16_round(dy + err)
+    return bf16_round(dy), np.where(lo != hi, hi - lo, 0.0)
+
+
+def backward(x_bits: np.ndarray, dz_bits: np.ndarray, A, B, W_bits: np.ndarray, n_groups: int) -> dict:
+    """Layer backward: dW [d_out, d_in] with its terms' L2 norms ``dW_norm`` and allowance
+    ``dW_amb``; dx [rows, d_in] with ``dxmag`` and ``dx_amb``; dA, dB with the activation
+    oracle's norms (nA, nB, mA, mB) and allowances ``dA_amb``, ``dB_amb``."""
+    x_bits = np.asarray(x_bits)
+    rows, d_in = x_bits.shape
+    dz = bf16_value(dz_bits).reshape(rows, -1)
+    fb, wf = activation_operand(x_bits, A, B, n_groups)
+    out = {"dW": dz.T @ fb, "dW_amb": np.abs(dz).T @ wf, "dW_norm": np.sqrt((dz * dz).T @ (fb * fb))}
+    dyb, wy = upstream(dz_bits, W_bits)
+    act = oracle.run(x_bits, A, B, n_groups, dy=bf16_bits(dyb), io="bf16")
+    for k in ("dx", "dxmag", "dA", "dB", "nA", "nB", "mA", "mB"):
+        out[k] = act[k]
+    out["dx_amb"] = np.zeros_like(act["dx"])
+    out["dA_amb"] = np.zeros_like(act["dA"])
+    out["dB_amb"] = np.zeros_like(act["dB"])
+    flagged = np.flatnonzero(wy.ravel())
+    out["n_ambiguous_dy"] = int(flagged.size)
+    if flagged.size:
+        ones = np.full(flagged.size, 0x3F80, dtype=np.uint16)   # dy = 1: the derivatives in dy
+        dyone = np.zeros(rows * d_in, dtype=np.uint16)
+        dyone[flagged] = ones
+        rec = oracle.points(x_bits, A, B, n_groups, flagged, dy=dyone.reshape(rows, d_in), io="bf16")
+        w = wy.ravel()[flagged]
+        out["dx_amb"].ravel()[flagged] = w * np.abs(rec[:, oracle.DX])
+        g = (flagged % d_in) // (d_in // n_groups)
+        na = out["dA"].shape[1]
+        for i in range(na):
+            np.add.at(out["dA_amb"][:, i], g, w * np.abs(rec[:, oracle.TA + i]))
+        for j in range(out["dB"].shape[1]):
+            np.add.at(out["dB_amb"][:, j], g, w * np.abs(rec[:, oracle.TB + j]))
+    return out

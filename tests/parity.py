@@ -29,6 +29,10 @@ Tolerances (fixed here, used by every parity test):
   running sum wanders on the scale of ||t||_2 leaves an error of about
   2^-24 * sqrt(n / 2) * ||t||_2; this scheme does not meet the default
   scheme's bound at large n, which is the pages' point about atomics.
+* The layer backward (oracle/layer.py): dx, dA, dB by the activation's
+  rules above plus the allowances for elements whose upstream bf16 rounding
+  of dz W is not unique (dx_amb, dA_amb, dB_amb); dW by the dA / dB rule
+  (its terms dz bf16(F) are exact in fp32) plus dW_amb.
 * The bf16 GR-KAN layer z = bf16(F(x)) W^T (oracle/layer.py):
   |gpu - ref| <= amb + gamma * mag + ulp_bf16(|ref| + amb + gamma * mag),
   gamma = K * 2^-24.  amb covers elements whose bf16 rounding of F is not
@@ -89,11 +93,13 @@ def sum_tol(ref: np.ndarray, norm: np.ndarray, mag=None) -> np.ndarray:
 
 
 def check_sums(name: str, gpu: np.ndarray, ref: np.ndarray, norm: np.ndarray,
-               atomic_adds: int = 0, mag=None) -> dict:
+               atomic_adds: int = 0, mag=None, extra=None) -> dict:
     """``mag``: L2 norm of the terms' rounding scales (oracle ``mA`` / ``mB``)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     err = np.abs(gpu - ref)
     tol = sum_tol(ref, norm, mag)
+    if extra is not None:
+        tol = tol + extra
     if atomic_adds:
         tol = tol + 8 * 2.0 ** -24 * np.sqrt(atomic_adds) * norm
     bad = ~(err <= tol)
@@ -124,3 +130,18 @@ def check_layer(name: str, gpu: np.ndarray, ref: dict, k: int) -> dict:
         raise AssertionError(f"{name}: {st['fail']} of {st['n']} outside tolerance; first at {i}: "
                              f"gpu {gpu.ravel()[i]!r} ref {z.ravel()[i]!r} tol {tol.ravel()[i]!r}")
     return st
+
+
+def check_elem_extra(name: str, gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, extra: np.ndarray,
+                     io: str = "f32") -> dict:
+    """check_elem with an extra allowance per element."""
+    gpu = np.asarray(gpu, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    tol = elem_tol(ref, np.asarray(mag, dtype=np.float64).ravel(), gpu, io) + np.asarray(extra).ravel()
+    err = np.abs(gpu - ref)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"{name}: {int(bad.sum())} of {gpu.size} outside tolerance; first at {i}: "
+                             f"gpu {gpu[i]!r} ref {ref[i]!r} tol {tol[i]!r}")
+    return {"n": int(gpu.size)}

@@ -41,7 +41,8 @@ def test_header_declares_the_abi():
         "grkan_pau_supported", "grkan_pau_forward", "grkan_pau_backward",
         "grkan_pau_backward_workspace_size", "grkan_pau_query_launch",
         "grkan_inflated_forward", "grkan_inflated_backward",
-        "grkan_layer_forward", "grkan_linear_forward"])
+        "grkan_layer_forward", "grkan_linear_forward", "grkan_layer_backward",
+        "grkan_layer_backward_workspace_size"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -277,3 +278,37 @@ def test_linear_rejects(lib, kw, code):
 def test_layer_empty_is_ok_without_device(lib):
     assert lfwd(lib, x=None, z=None, rows=0) == OK
     assert linfwd(lib, y=None, z=None, rows=0) == OK
+
+
+def lbwd(lib, x=P, dz=P + 0x100000, A=P + 0x200000, B=P + 0x300000, W=P + 0x400000, dx=P + 0x800000,
+         dA=P + 0x900000, dB=P + 0x910000, dW=P + 0xA00000, rows=4, d_in=256, d_out=64, n_g=8,
+         ws=P + 0x1000000, ws_bytes=1 << 30):
+    return lib.grkan_layer_backward(x, dz, A, B, W, dx, dA, dB, dW, rows, d_in, d_out, n_g, ws, ws_bytes, None)
+
+
+def test_layer_backward_workspace_size(lib):
+    f = lib.grkan_layer_backward_workspace_size
+    # KAT-B layer 2: W^T (768 x 3072 bf16), one [rows][3072] bf16 buffer, the bf16 activation
+    # backward's partials (as grkan_backward_workspace_size), 29 row splits of fp32 dW partials
+    # (ceil(1024 / 36 output tiles)), each piece 256-byte aligned
+    a256 = lambda v: (v + 255) // 256 * 256
+    act = lib.grkan_backward_workspace_size(201728, 3072, 8, BF16, 0)
+    assert f(201728, 3072, 768, 8) == (a256(768 * 3072 * 2) + a256(201728 * 3072 * 2) + a256(act)
+                                      + a256(29 * 768 * 3072 * 4))
+    assert f(0, 256, 64, 8) == 0
+    assert f(100, 256, 96, 8) == 0      # d_out not a multiple of 64
+    assert f(100, 96, 64, 8) == 0       # d_in not a multiple of 64
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), INVALID), (dict(dW=None), INVALID), (dict(dx=None), INVALID), (dict(dz=None), INVALID),
+    (dict(ws=None), INVALID), (dict(ws_bytes=1000), INVALID), (dict(d_out=96), UNSUPPORTED),
+    (dict(d_in=96), UNSUPPORTED), (dict(n_g=3), INVALID), (dict(ws=P + 0x1000010), UNSUPPORTED),
+    (dict(dx=P + 64), INVALID),                        # dx partly overlaps x
+    (dict(dx=P + 0x100000), INVALID),                  # dx overlaps dz
+    (dict(dW=P + 0x900000 + 8), INVALID),              # dW overlaps dA
+    (dict(ws=P + 0x400000), INVALID),                  # workspace overlaps W
+    (dict(dW=P + 0x3), UNSUPPORTED),
+])
+def test_layer_backward_rejects(lib, kw, code):
+    assert lbwd(lib, **kw) == code

@@ -7,6 +7,7 @@ column tails, 8 to 64 groups, and the two KAT-B MLP layers at full size
 grkan_forward -> grkan_linear_forward bit for bit: both round the same fp32
 F to bf16 and run the same matrix kernel.
 """
+import math
 import sys
 
 import numpy as np
@@ -136,3 +137,95 @@ def test_layer_full_size_sampled(gk, name):
     zs = host(z[torch.from_numpy(rows).to(DEV)])
     ref = layer.forward(inp["x"][rows], inp["A"], inp["B"], inp["W"], w.n_groups)
     parity.check_layer(f"{name} sampled rows", zs, ref, w.d)
+
+
+# ---------------------------------------------------------------- backward
+
+def backward_inputs(rows, d_in, n_g, d_out, seed):
+    w = synth.custom("layer-bwd", rows, d_in, n_g, io="bf16", seed=seed, d_out=d_out)
+    return synth.make_inputs(w)
+
+
+def check_backward(name, got, ref, sampled_rows=None):
+    dx, dA, dB, dW = got
+    parity.check_elem_extra(f"{name} dx", host(dx), ref["dx"], ref["dxmag"], ref["dx_amb"], "bf16")
+    parity.check_sums(f"{name} dA", dA.cpu().numpy(), ref["dA"], ref["nA"], mag=ref["mA"], extra=ref["dA_amb"])
+    parity.check_sums(f"{name} dB", dB.cpu().numpy(), ref["dB"], ref["nB"], mag=ref["mB"], extra=ref["dB_amb"])
+    parity.check_sums(f"{name} dW", dW.cpu().numpy(), ref["dW"], ref["dW_norm"], extra=ref["dW_amb"])
+
+
+# (rows, d_in, n_groups, d_out): several 256 x 256 tiles, ragged rows and columns, row splits
+BWD_SHAPES = [(301, 256, 8, 320), (700, 768, 8, 256), (257, 512, 64, 640), (64, 128, 16, 64), (1, 64, 8, 64),
+              (3000, 256, 8, 256)]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_layer_backward_parity(gk, shape):
+    rows, d_in, n_g, d_out = shape
+    log(f"[layer_bwd] rows={rows} d_in={d_in} n_g={n_g} d_out={d_out}")
+    inp = backward_inputs(rows, d_in, n_g, d_out, 7000 + rows)
+    x, dz, W = bf(inp["x"]), bf(inp["dz"]), bf(inp["W"])
+    A, B = torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV)
+    got = gk.grkan_layer_backward(x, dz, A, B, W, n_g)
+    torch.cuda.synchronize()
+    ref = layer.backward(inp["x"], inp["dz"], inp["A"], inp["B"], inp["W"], n_g)
+    check_backward(f"layer bwd {shape}", got, ref)
+    # bitwise reproducible, and dx may be x itself
+    got2 = gk.grkan_layer_backward(x, dz, A, B, W, n_g)
+    xc = x.clone()
+    got3 = gk.grkan_layer_backward(xc, dz, A, B, W, n_g, dx=xc)
+    torch.cuda.synchronize()
+    for a, b, c in zip(got, got2, got3):
+        it = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(a.view(it), b.view(it)) and torch.equal(a.view(it), c.view(it))
+
+
+def test_layer_backward_empty(gk):
+    inp = backward_inputs(4, 64, 8, 64, 7100)
+    A, B = torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV)
+    dA = torch.full((8, 6), 5.0, device=DEV)
+    dB = torch.full((8, 4), 5.0, device=DEV)
+    dW = torch.full((64, 64), 5.0, device=DEV)
+    gk.grkan_layer_backward(bf(inp["x"])[:0], bf(inp["dz"])[:0], A, B, bf(inp["W"]), 8, dA=dA, dB=dB, dW=dW)
+    torch.cuda.synchronize()
+    assert not dA.any() and not dB.any() and not dW.any()
+
+
+@pytest.mark.parametrize("name", list(synth.LAYER_WORKLOADS))
+def test_layer_backward_full_size(gk, name):
+    """The KAT-B MLP layers' backward at full size, in the benchmark's configuration: dx on
+    sampled rows and dW on sampled entries against the oracle one by one; dA, dB equal, bit
+    for bit, to the activation's own backward (grkan_backward, whose full-size group sums are
+    checked against the oracle elsewhere) on dY from the same matrix kernel."""
+    w = synth.WORKLOADS[name]
+    log(f"[layer_bwd_full] {name}")
+    inp = synth.make_inputs(w)
+    x, dz, W = bf(inp["x"]), bf(inp["dz"]), bf(inp["W"])
+    A, B = torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV)
+    dx, dA, dB, dW = gk.grkan_layer_backward(x, dz, A, B, W, w.n_groups)
+    dy = gk.grkan_linear_forward(dz, W.t().contiguous())
+    _, dA2, dB2 = gk.grkan_backward(x, dy, A, B, w.n_groups)
+    torch.cuda.synchronize()
+    assert torch.equal(dA, dA2) and torch.equal(dB, dB2)
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, w.rows - 1], rng.integers(0, w.rows, 30)]))
+    ref = layer.backward(inp["x"][rows], inp["dz"][rows], inp["A"], inp["B"], inp["W"], w.n_groups)
+    parity.check_elem_extra(f"{name} dx rows", host(dx[torch.from_numpy(rows).to(DEV)]), ref["dx"],
+                            ref["dxmag"], ref["dx_amb"], "bf16")
+    # dW on 24 sampled entries: column c of bf16(F(x)) over all rows, dotted with column o of dz
+    d_g = w.d // w.n_groups
+    dzv = orc.to_f64(inp["dz"], "bf16")
+    dWh = dW.cpu().numpy()
+    for o, c in zip(rng.integers(0, w.d_out, 24), rng.integers(0, w.d, 24)):
+        idx = np.arange(w.rows, dtype=np.int64) * w.d + c
+        rec = orc.points(inp["x"], inp["A"], inp["B"], w.n_groups, idx, io="bf16")
+        f = rec[:, orc.F]
+        err = 16.0 * 2.0 ** -24 * rec[:, orc.FMAG]
+        fb = layer.bf16_round(f)
+        lo, hi = layer.bf16_round(f - err), layer.bf16_round(f + err)
+        terms = dzv[:, o] * fb
+        refv = math.fsum(terms)
+        amb = float(np.sum(np.abs(dzv[:, o]) * np.where(lo != hi, hi - lo, 0.0)))
+        norm = float(np.sqrt(np.sum(terms * terms)))
+        parity.check_sums(f"{name} dW[{o},{c}]", np.array([dWh[o, c]]), np.array([refv]), np.array([norm]),
+                          extra=np.array([amb]))

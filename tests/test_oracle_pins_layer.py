@@ -116,3 +116,75 @@ def test_ambiguity_flags_exact_midpoints_only():
     alt[:, :8] = 1.0 + 2.0 ** -7          # the other neighbour of the midpoint
     z_alt = alt @ orc.to_f64(W, "bf16").T
     assert np.all(np.abs(z_alt - res["z"]) <= res["amb"])
+
+
+# ---------------------------------------------------------------- backward
+
+def small_bwd(rows=3, d_in=16, n_g=2, d_out=4, seed=31):
+    w = synth.custom("layer-bwd-pin", rows, d_in, n_g, io="bf16", seed=seed, d_out=d_out)
+    return synth.make_inputs(w)
+
+
+def test_backward_brute_force():
+    inp = small_bwd()
+    x, dz, A, B, W = inp["x"], inp["dz"], inp["A"], inp["B"], inp["W"]
+    rows, d_in = x.shape
+    d_out = W.shape[0]
+    d_g = d_in // 2
+    res = layer.backward(x, dz, A, B, W, 2)
+    xv, dzv, wv = orc.to_f64(x, "bf16"), orc.to_f64(dz, "bf16"), orc.to_f64(W, "bf16")
+    dA = np.zeros((2, 6))
+    dB = np.zeros((2, 4))
+    for r in range(rows):
+        for c in range(d_in):
+            g = c // d_g
+            dy = float(layer.bf16_round(np.float64(math.fsum(dzv[r, o] * wv[o, c] for o in range(d_out)))))
+            rec = orc.point(xv[r, c], dy, A[g], B[g])
+            assert abs(res["dx"][r, c] - rec[orc.DX]) <= 1e-13 * (abs(rec[orc.DX]) + 1e-30)
+            dA[g] += rec[orc.TA:orc.TA + 6]
+            dB[g] += rec[orc.TB:orc.TB + 4]
+    assert np.allclose(res["dA"], dA, rtol=1e-12, atol=1e-15)
+    assert np.allclose(res["dB"], dB, rtol=1e-12, atol=1e-15)
+    for o in range(d_out):
+        for c in range(d_in):
+            g = c // d_g
+            ref = math.fsum(dzv[r, o] * layer.bf16_round(np.float64(orc.point(xv[r, c], 0.0, A[g], B[g])[orc.F]))
+                            for r in range(rows))
+            assert abs(res["dW"][o, c] - ref) <= 1e-12 * (abs(ref) + 1e-30) + 1e-15
+
+
+def test_weight_gradient_is_the_derivative_of_the_loss():
+    # L(W) = sum dz * z(W) is linear in W: doubling W[o, c] changes L by W[o, c] dW[o, c]
+    inp = small_bwd(rows=5, d_in=32, n_g=4, d_out=6, seed=32)
+    x, dz, A, B, W = inp["x"], inp["dz"], inp["A"], inp["B"], inp["W"]
+    dzv = orc.to_f64(dz, "bf16")
+    res = layer.backward(x, dz, A, B, W, 4)
+
+    def loss(Wb):
+        return math.fsum((dzv * layer.forward(x, A, B, Wb, 4)["z"]).ravel())
+
+    base = loss(W)
+    wv = orc.to_f64(W, "bf16")
+    for o, c in [(0, 0), (3, 17), (5, 31), (2, 9)]:
+        W2 = W.copy()
+        W2[o, c] = synth.bf16_bits(np.float32([2.0 * wv[o, c]]))[0]
+        dl = loss(W2) - base
+        assert abs(dl - wv[o, c] * res["dW"][o, c]) <= 1e-10 * (abs(dl) + 1e-12)
+
+
+def test_upstream_ambiguity_at_a_midpoint():
+    # dy = 1 * 1 + 2^-8 * 1 = 1 + 2^-8: exactly halfway between bf16 1 and 1 + 2^-7
+    dz = synth.bf16_bits(np.float32([[1.0, 2.0 ** -8]]))
+    W = synth.bf16_bits(np.ones((2, 8), np.float32))
+    dyb, width = layer.upstream(dz, W)
+    assert np.all(dyb == 1.0) and np.all(width == 2.0 ** -7)
+    A = np.tile(np.float32([0.1, 0.9, -0.2, 0.05, 0.01, -0.02]), (1, 1))
+    B = np.tile(np.float32([0.3, -0.1, 0.2, 0.05]), (1, 1))
+    x = synth.bf16_bits(np.float32([[0.5, -1.25, 2.0, 0.75, -0.375, 1.5, -2.5, 0.25]]))
+    res = layer.backward(x, dz, A, B, W, 1)
+    assert res["n_ambiguous_dy"] == 8
+    other = orc.run(x, A, B, 1, dy=layer.bf16_bits(np.full((1, 8), 1.0 + 2.0 ** -7)), io="bf16")
+    assert np.all(np.abs(other["dx"] - res["dx"]) <= res["dx_amb"] * (1 + 1e-12))
+    assert np.all(np.abs(other["dA"] - res["dA"]) <= res["dA_amb"] * (1 + 1e-12))
+    assert np.all(np.abs(other["dB"] - res["dB"]) <= res["dB_amb"] * (1 + 1e-12))
+    assert np.all(res["dx_amb"] > 0)
