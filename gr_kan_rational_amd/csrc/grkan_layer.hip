@@ -229,14 +229,20 @@ __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a)
 // A[r][m] B[r][n] (A = dZ [rows][d_out], B = Y [rows][d_in], bf16), then a
 // fixed-order sum over the splits.  Here K = rows runs down the columns of
 // both operands, while an MFMA fragment wants 8 consecutive k of one m (or
-// n): each thread loads one 16-byte chunk (8 consecutive m) from each of 4
-// consecutive rows and writes it transposed -- for each of its 8 m, the 4
-// rows as one 8-byte LDS write -- into the same padded [m][k] layout the
-// forward kernel reads, so the MFMA loop is the forward's.  The rows are cut
+// n).  Each thread loads one 16-byte chunk (8 consecutive m) from each of 4
+// consecutive rows -- a wave reads 2 rows x 512 contiguous bytes per
+// instruction -- and writes it transposed: for each of its 8 m, the 4 rows
+// as one 8-byte LDS write.  LDS rows are [m][64 k] without padding, their
+// eight 16-byte chunks permuted by chunk ^ ((m + m / 8) mod 8): fragment
+// reads (8 consecutive m, one chunk) and the transposed writes (m = 8 cc + i
+// for 32 chunk columns cc) both spread over the banks.  The rows are cut
 // into splits so that the few output tiles (36 at the KAT-B shapes) still
 // fill the GPU; each workgroup writes its fp32 tile of partial sums, and
 // grkan_wgrad_reduce_kernel adds the splits in order (bitwise reproducible).
 constexpr int kWgSplitsTarget = 1024;  // workgroups to aim for
+constexpr int kWgRow = kBK;            // bf16 per LDS row (unpadded)
+constexpr int kWgStage = (kBM + kBN) * kWgRow;
+constexpr size_t kWgLdsBytes = 2 * (size_t)kWgStage * 2;
 
 struct WgradArgs {
     const uint16_t *a;   // [rows][M] bf16 (dZ)
@@ -248,6 +254,11 @@ struct WgradArgs {
 __device__ static inline uint32_t pack2(uint32_t lo, uint32_t hi, int odd) {
     // the bf16 at position odd (0 = low half) of lo and of hi, as (lo's, hi's)
     return odd ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+}
+
+// bf16 offset of 16-byte chunk `chunk` of LDS row m.
+__device__ static inline int wg_chunk(int m, int chunk) {
+    return m * kWgRow + ((chunk ^ ((m + (m >> 3)) & 7)) << 3);
 }
 
 __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
@@ -263,15 +274,11 @@ __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
     const int r_end = min(a.rows, r_begin + a.rows_per_split);
 
     // This thread's chunks: 8 consecutive columns (cc), rows 4 rg .. 4 rg + 3
-    // of each 64-row step.  A wave covers all 16 row groups of 4 column
-    // chunks: its transposed LDS writes then fall on distinct bank pairs
-    // except for a 2-way overlap (a wave spanning 32 column chunks instead
-    // would put them all on the same banks).  Columns past the end are
-    // clamped (their outputs are not stored); rows past the split's end read
-    // as zero.
-    constexpr int kRowGroups = kBK / 4;                 // 16
-    static_assert(kThreads / kRowGroups * 8 == kBM && kBM == kBN, "one 64-row step per thread set");
-    const int rg = t % kRowGroups, cc = t / kRowGroups;
+    // of each 64-row step.  Columns past the end are clamped (their outputs
+    // are not stored); rows past the split's end read as zero.
+    constexpr int kColChunks = kBM / 8;                 // 32
+    static_assert(kThreads / kColChunks * 4 == kBK && kBM == kBN, "one 64-row step per thread set");
+    const int cc = t % kColChunks, rg = t / kColChunks;
     const uint16_t *pa = a.a + min(m0 + cc * 8, a.M - 8);
     const uint16_t *pb = a.b + min(n0 + cc * 8, a.N - 8);
     u32x4 ra[4], rb[4];
@@ -287,9 +294,10 @@ __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
             rb[q] = in ? vb : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    // Columns 2h and 2h + 1 of the chunks -> LDS rows cc*8 + 2h, + 1, k = 4 rg .. 4 rg + 3.
+    // Columns 2h and 2h + 1 of the chunks -> LDS rows cc*8 + 2h (+ 1), k = 4 rg .. 4 rg + 3.
     auto stage_pair = [&](int buf, int h) {
-        uint16_t *s = lds + buf * kStage;
+        uint16_t *s = lds + buf * kWgStage;
+        const int sub = (rg & 1) * 4;
 #pragma unroll
         for (int odd = 0; odd < 2; ++odd) {
             const int col = cc * 8 + 2 * h + odd;
@@ -298,8 +306,8 @@ __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
             va.y = pack2(ra[2][h], ra[3][h], odd);
             vb.x = pack2(rb[0][h], rb[1][h], odd);
             vb.y = pack2(rb[2][h], rb[3][h], odd);
-            *reinterpret_cast<uint2 *>(s + col * kLdk + rg * 4) = va;
-            *reinterpret_cast<uint2 *>(s + (kBM + col) * kLdk + rg * 4) = vb;
+            *reinterpret_cast<uint2 *>(s + wg_chunk(col, rg >> 1) + sub) = va;
+            *reinterpret_cast<uint2 *>(s + wg_chunk(kBM + col, rg >> 1) + sub) = vb;
         }
     };
 
@@ -310,14 +318,14 @@ __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
         for (int j = 0; j < kTN; ++j) acc[i][j] = f32x16{};
     bf16x8 fa[2][kTM], fb[2][kTN];
     auto load_fragments = [&](int buf, int ks, int set) {
-        const uint16_t *s = lds + buf * kStage;
-        const int ko = ks * 16 + 8 * (lane >> 5);
+        const uint16_t *s = lds + buf * kWgStage;
+        const int chunk = 2 * ks + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
-            fa[set][i] = *reinterpret_cast<const bf16x8 *>(s + (wm * kWTM + i * 32 + (lane & 31)) * kLdk + ko);
+            fa[set][i] = *reinterpret_cast<const bf16x8 *>(s + wg_chunk(wm * kWTM + i * 32 + (lane & 31), chunk));
 #pragma unroll
         for (int j = 0; j < kTN; ++j)
-            fb[set][j] = *reinterpret_cast<const bf16x8 *>(s + (kBM + wn * kWTN + j * 32 + (lane & 31)) * kLdk + ko);
+            fb[set][j] = *reinterpret_cast<const bf16x8 *>(s + wg_chunk(kBM + wn * kWTN + j * 32 + (lane & 31), chunk));
     };
 
     const int nk = (r_end - r_begin + kBK - 1) / kBK;
@@ -435,7 +443,7 @@ hipError_t launch_wgrad(const void *dz, const void *y, float *partials, float *d
     auto kern = grkan_wgrad_kernel;
     std::call_once(g_attr_once[2], [&] {
         g_attr_err[2] = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWgLdsBytes);
     });
     if (g_attr_err[2] != hipSuccess) return g_attr_err[2];
     const int splits = wgrad_splits(rows, M, N);
@@ -444,7 +452,7 @@ hipError_t launch_wgrad(const void *dz, const void *y, float *partials, float *d
     WgradArgs a{static_cast<const uint16_t *>(dz), static_cast<const uint16_t *>(y), partials, (int32_t)rows,
                 (int32_t)M, (int32_t)N, splits, rps};
     const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * splits)), dim3(kThreads), kLdsBytes, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * splits)), dim3(kThreads), kWgLdsBytes, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = M * N;
