@@ -228,6 +228,122 @@ def bench_layer(args, w, gk, synth, dev, log) -> int:
     return 0
 
 
+def cpu_baseline_cheby(w, target_s: float = 10.0) -> dict:
+    """fp64 Chebyshev-KAN oracle, forward and backward, on the first rows of the workload."""
+    from gr_kan_rational_amd import synth
+    from oracle import chebykan, oracle
+
+    C = synth.weight(w)
+
+    def run(rows):
+        inp = synth.make_inputs(w, rows=rows)
+        t0 = time.perf_counter()
+        chebykan.forward(inp["x"], C, w.cheby)
+        chebykan.backward(inp["x"], inp["dz"], C, w.cheby)
+        return time.perf_counter() - t0
+
+    calib = 64
+    dt = run(calib)
+    rows = int(min(w.rows, max(calib, calib * target_s / max(dt, 1e-3))))
+    dt = run(rows)
+    flops = 3 * 2.0 * rows * w.d * (w.cheby + 1) * w.d_out
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"first {rows} of {w.rows} rows of {w.name}: forward and backward in fp64 (basis rounded "
+                      f"to bf16), {dt:.1f} s wall"}
+
+
+def bench_cheby(args, w, gk, synth, dev, log) -> int:
+    """The Chebyshev-KAN layer (bf16, degree 7): a step is the forward (basis built while
+    staging the GEMM's A operand) and the backward (dC on the matrix cores with the basis built
+    while staging, G = dy C, dx); three GEMMs of 2 rows 8 d_in d_out FLOPs each.  `detail`
+    adds, for context, the same forward in eager torch ops (tanh, the recurrence in bf16 tensors,
+    a library GEMM)."""
+    import torch
+
+    log(f"Chebyshev-KAN workload {w.name}: x [{w.batch},{w.seq},{w.d}] -> {w.d_out}, degree {w.cheby}")
+    inp = synth.make_inputs(w)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, C, dy = bf(inp["x"]), bf(inp["W"]), bf(inp["dz"])
+    del inp
+    y = torch.empty((w.rows, w.d_out), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty_like(x)
+    dC = torch.empty(C.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(gk.grkan_chebykan_backward_workspace_size(w.rows, w.d, w.d_out, w.cheby),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def forward():
+        gk.grkan_chebykan_forward(x, C, w.cheby, out=y, stream=stream)
+
+    def backward():
+        gk.grkan_chebykan_backward(x, dy, C, w.cheby, dx=dx, dC=dC, workspace=ws, stream=stream)
+
+    def step():
+        forward()
+        backward()
+
+    def timed(fn, reps):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        fn()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(reps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ms = timed(step, args.steps)
+    gemm_flops = 2.0 * w.rows * w.d * (w.cheby + 1) * w.d_out
+    tflops = 3 * gemm_flops / (ms * 1e-3) / 1e12
+    fwd_ms = timed(forward, args.steps)
+    bwd_ms = timed(backward, args.steps)
+    Cm = C.view(w.d_out, -1)
+
+    def torch_forward():
+        t = torch.tanh(x)
+        T = [torch.ones_like(t), t]
+        for _ in range(w.cheby - 1):
+            T.append(2 * t * T[-1] - T[-2])
+        return torch.matmul(torch.stack(T, dim=-1).view(w.rows, -1), Cm.t())
+
+    detail = {"forward_ms": fwd_ms, "backward_ms": bwd_ms,
+              "forward_TFLOPs": gemm_flops / (fwd_ms * 1e-3) / 1e12,
+              "backward_TFLOPs": 2 * gemm_flops / (bwd_ms * 1e-3) / 1e12,
+              "torch_eager_forward_ms": timed(torch_forward, max(3, args.steps // 5)),
+              "flops_per_step": 3 * gemm_flops, "device": torch.cuda.get_device_name(dev)}
+    log(f"step {ms:.4f} ms ({tflops:.1f} TFLOP/s); forward {fwd_ms:.4f} ms, backward {bwd_ms:.4f} ms; "
+        f"torch eager forward {detail['torch_eager_forward_ms']:.4f} ms")
+    out = {
+        "metric": f"Chebyshev-KAN layer forward + backward TFLOP/s (bf16 matrix cores, basis built in the GEMM "
+                  f"staging), workload {w.name}",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (fp32 accumulation)", "data": "synthetic",
+        "config": {"workload": w.name, "shape": [w.batch, w.seq, w.d], "d_out": w.d_out, "degree": w.cheby,
+                   "io": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": detail["forward_TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": detail["forward_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "grkan_chebykan_forward (grkan_layer_gemm_kernel, Chebyshev prologue)",
+                     "algorithmic_flops_per_launch": gemm_flops},
+        "detail": detail,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: fp64 Chebyshev-KAN oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline_cheby(w)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +390,8 @@ def main() -> int:
                           "copies": max(1, args.steps)}), flush=True)
         return 0
     gk.load_library()
+    if w.cheby:
+        return bench_cheby(args, w, gk, synth, dev, log)
     if w.d_out > 0:
         return bench_layer(args, w, gk, synth, dev, log)
     io = gk.GRKAN_BF16 if w.io == "bf16" else gk.GRKAN_F32

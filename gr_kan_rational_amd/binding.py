@@ -89,6 +89,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grkan_layer_backward.restype = ctypes.c_int
     lib.grkan_layer_backward_workspace_size.argtypes = [i64, i64, i64, i32]
     lib.grkan_layer_backward_workspace_size.restype = sz
+    lib.grkan_chebykan_forward.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.grkan_chebykan_forward.restype = ctypes.c_int
+    lib.grkan_chebykan_backward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+    lib.grkan_chebykan_backward.restype = ctypes.c_int
+    lib.grkan_chebykan_backward_workspace_size.argtypes = [i64, i64, i64, i32]
+    lib.grkan_chebykan_backward_workspace_size.restype = sz
     _lib = lib
     return lib
 
@@ -341,6 +347,59 @@ def grkan_layer_backward(x: torch.Tensor, dz: torch.Tensor, A: torch.Tensor, B: 
     if st != GRKAN_OK:
         raise GRKANError(st, "grkan_layer_backward")
     return dx, dA, dB, dW
+
+
+CHEBY_DEGREE = 7
+
+
+def _cheby_dims(x, C, degree):
+    if x.dtype != torch.bfloat16 or C.dtype != torch.bfloat16:
+        raise TypeError("the Chebyshev-KAN layer takes bfloat16 x and C")
+    rows, d_in = _rows_d(x)
+    if C.dim() != 3 or C.shape[1] != d_in or C.shape[2] != degree + 1 or not C.is_contiguous() \
+            or C.device != x.device:
+        raise ValueError("C must be a contiguous [d_out, d_in, degree + 1] tensor on x's device")
+    return rows, d_in, C.shape[0]
+
+
+def grkan_chebykan_forward(x: torch.Tensor, C: torch.Tensor, degree: int = CHEBY_DEGREE,
+                           out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = sum_i sum_k C[o, i, k] T_k(tanh x_i) (``grkan_chebykan_forward``), bf16."""
+    rows, d_in, d_out = _cheby_dims(x, C, degree)
+    y = torch.empty((*x.shape[:-1], d_out), dtype=torch.bfloat16, device=x.device) if out is None else out
+    if y.dtype != torch.bfloat16 or y.numel() != rows * d_out or not y.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor of rows x d_out elements")
+    st = load_library().grkan_chebykan_forward(_ptr(x), _ptr(C), _ptr(y), rows, d_in, d_out, degree,
+                                               ctypes.c_void_p(_stream(stream)))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_chebykan_forward")
+    return y
+
+
+def grkan_chebykan_backward_workspace_size(rows: int, d_in: int, d_out: int, degree: int = CHEBY_DEGREE) -> int:
+    return int(load_library().grkan_chebykan_backward_workspace_size(rows, d_in, d_out, degree))
+
+
+def grkan_chebykan_backward(x: torch.Tensor, dy: torch.Tensor, C: torch.Tensor, degree: int = CHEBY_DEGREE,
+                            dx: torch.Tensor | None = None, dC: torch.Tensor | None = None,
+                            workspace: torch.Tensor | None = None, stream=None):
+    """(dx, dC) of the Chebyshev-KAN layer (``grkan_chebykan_backward``): dx bf16, dC fp32."""
+    rows, d_in, d_out = _cheby_dims(x, C, degree)
+    if dy.dtype != torch.bfloat16 or dy.numel() != rows * d_out or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous bfloat16 tensor of rows x d_out elements")
+    dx = torch.empty_like(x) if dx is None else dx
+    dC = torch.empty(C.shape, dtype=torch.float32, device=x.device) if dC is None else dC
+    lib = load_library()
+    need = lib.grkan_chebykan_backward_workspace_size(rows, d_in, d_out, degree)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsp = _ptr(workspace) if workspace is not None else None
+    wsn = workspace.numel() if workspace is not None else 0
+    st = lib.grkan_chebykan_backward(_ptr(x), _ptr(dy), _ptr(C), _ptr(dx), _ptr(dC), rows, d_in, d_out, degree,
+                                     wsp, wsn, ctypes.c_void_p(_stream(stream)))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_chebykan_backward")
+    return dx, dC
 
 
 def grkan_query_launch(rows: int, d: int, n_groups: int, io: int, pass_: int) -> dict:

@@ -588,6 +588,107 @@ extern "C" grkan_status_t grkan_layer_backward(const void *x, const void *dz, co
                          ws + lp.off_act, workspace_need(lp.act), stream);
 }
 
+// ------------------------------------------------------- Chebyshev KAN
+
+namespace {
+
+constexpr int32_t kChebyDegree = 7;
+
+grkan_status_t cheby_shape(int64_t rows, int64_t d_in, int64_t d_out, int32_t degree) {
+    if (rows < 0 || d_in <= 0 || d_out <= 0 || degree < 0) return GRKAN_ERR_INVALID_ARG;
+    if (degree != kChebyDegree) return GRKAN_ERR_UNSUPPORTED;
+    if (rows > INT32_MAX || d_out > INT32_MAX || d_in > INT32_MAX / 8) return GRKAN_ERR_UNSUPPORTED;
+    if ((d_in * 8) % layer_k_step() != 0) return GRKAN_ERR_UNSUPPORTED;
+    return GRKAN_OK;
+}
+
+struct ChebyBwdPlan {
+    size_t off_ct, off_g, off_wg, total;
+};
+
+grkan_status_t cheby_bwd_plan(int64_t rows, int64_t d_in, int64_t d_out, int32_t degree, ChebyBwdPlan *cp) {
+    grkan_status_t st = cheby_shape(rows, d_in, d_out, degree);
+    if (st != GRKAN_OK) return st;
+    if (d_out % layer_k_step() != 0) return GRKAN_ERR_UNSUPPORTED;
+    const int64_t kb = d_in * 8;
+    cp->off_ct = 0;
+    cp->off_g = align256((size_t)kb * d_out * 2);
+    cp->off_wg = cp->off_g + align256((size_t)rows * kb * 2);
+    cp->total = cp->off_wg + align256(wgrad_partials_bytes(rows, d_out, kb));
+    return GRKAN_OK;
+}
+
+}  // namespace
+
+extern "C" grkan_status_t grkan_chebykan_forward(const void *x, const void *C, void *y, int64_t rows,
+                                                 int64_t d_in, int64_t d_out, int32_t degree,
+                                                 hipStream_t stream) {
+    grkan_status_t st = cheby_shape(rows, d_in, d_out, degree);
+    if (st != GRKAN_OK) return st;
+    if (!C) return GRKAN_ERR_INVALID_ARG;
+    if (!aligned(C, 16)) return GRKAN_ERR_UNSUPPORTED;
+    if (rows == 0) return GRKAN_OK;
+    if (!x || !y) return GRKAN_ERR_INVALID_ARG;
+    if (!aligned(x, 2) || !aligned(y, 2)) return GRKAN_ERR_UNSUPPORTED;
+    const size_t xb = (size_t)rows * d_in * 2, yb = (size_t)rows * d_out * 2, cb = (size_t)d_out * d_in * 16;
+    if (overlap(y, yb, x, xb) || overlap(y, yb, C, cb)) return GRKAN_ERR_INVALID_ARG;
+    // ---- validation done; HIP calls from here on
+    return from_hip(launch_cheby_forward(x, C, y, rows, d_in, d_out, stream));
+}
+
+extern "C" size_t grkan_chebykan_backward_workspace_size(int64_t rows, int64_t d_in, int64_t d_out,
+                                                         int32_t degree) {
+    ChebyBwdPlan cp;
+    if (rows <= 0 || cheby_bwd_plan(rows, d_in, d_out, degree, &cp) != GRKAN_OK) return 0;
+    return cp.total;
+}
+
+extern "C" grkan_status_t grkan_chebykan_backward(const void *x, const void *dy, const void *C, void *dx,
+                                                  float *dC, int64_t rows, int64_t d_in, int64_t d_out,
+                                                  int32_t degree, void *workspace, size_t workspace_bytes,
+                                                  hipStream_t stream) {
+    ChebyBwdPlan cp;
+    grkan_status_t st = cheby_bwd_plan(rows, d_in, d_out, degree, &cp);
+    if (st != GRKAN_OK) return st;
+    if (d_in % 8 != 0) return GRKAN_ERR_UNSUPPORTED;
+    if (!C || !dC) return GRKAN_ERR_INVALID_ARG;
+    if (!aligned(C, 16) || !aligned(dC, 4)) return GRKAN_ERR_UNSUPPORTED;
+    const size_t xb = rows > 0 ? (size_t)rows * d_in * 2 : 0, yb = rows > 0 ? (size_t)rows * d_out * 2 : 0;
+    const size_t cb = (size_t)d_out * d_in * 16, dcb = (size_t)d_out * d_in * 32;
+    if (rows > 0) {
+        if (!x || !dy || !dx) return GRKAN_ERR_INVALID_ARG;
+        if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16)) return GRKAN_ERR_UNSUPPORTED;
+        // dx may be x itself (each thread reads its x before writing the same bytes of dx,
+        // and x is read by the dC step before dx is written)
+        if (bad_alias(dx, x, xb) || overlap(dx, xb, dy, yb) || overlap(dx, xb, C, cb)) return GRKAN_ERR_INVALID_ARG;
+    }
+    const void *ins[] = {x, dy, C, dx};
+    const size_t insz[] = {xb, yb, cb, xb};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(dC, dcb, ins[i], insz[i])) return GRKAN_ERR_INVALID_ARG;
+    if (rows > 0) {
+        if (!workspace || workspace_bytes < cp.total) return GRKAN_ERR_INVALID_ARG;
+        if (!aligned(workspace, 256)) return GRKAN_ERR_UNSUPPORTED;
+        for (int i = 0; i < 4; ++i)
+            if (overlap(workspace, cp.total, ins[i], insz[i])) return GRKAN_ERR_INVALID_ARG;
+        if (overlap(workspace, cp.total, dC, dcb)) return GRKAN_ERR_INVALID_ARG;
+    }
+    // ---- validation done; HIP calls from here on
+    if (rows == 0) return from_hip(launch_zero(dC, dC, d_out * d_in * 8, 0, stream));
+    char *ws = static_cast<char *>(workspace);
+    const int64_t kb = d_in * 8;
+    // dC = dy^T basis(x), the basis built while staging
+    st = from_hip(launch_cheby_wgrad(dy, x, reinterpret_cast<float *>(ws + cp.off_wg), dC, rows, d_out, d_in,
+                                     stream));
+    if (st != GRKAN_OK) return st;
+    // G = dy C (bf16), over C^T so that both operands are K-contiguous; then dx
+    st = from_hip(launch_transpose16(C, ws + cp.off_ct, d_out, kb, stream));
+    if (st != GRKAN_OK) return st;
+    st = from_hip(launch_linear_forward(dy, ws + cp.off_ct, ws + cp.off_g, rows, d_out, kb, stream));
+    if (st != GRKAN_OK) return st;
+    return from_hip(launch_cheby_dx(x, ws + cp.off_g, dx, rows, d_in, stream));
+}
+
 extern "C" grkan_status_t grkan_inflated_forward(const void *x, void *y, const float *A,
                                                  const float *B, int64_t rows, int64_t d,
                                                  int32_t n_groups, grkan_dtype_t io, int32_t repeat,

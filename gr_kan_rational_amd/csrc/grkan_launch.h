@@ -150,6 +150,16 @@ int wgrad_splits(int64_t rows, int64_t M, int64_t N);
 size_t wgrad_partials_bytes(int64_t rows, int64_t M, int64_t N);
 hipError_t launch_wgrad(const void *dz, const void *y, float *partials, float *dW, int64_t rows, int64_t M,
                         int64_t N, hipStream_t s);
+// Chebyshev-KAN layer (degree 7, 8 basis functions per input): forward
+// y = bf16(basis(x)) C^T with the basis built while staging (x bf16
+// [rows][d_in], C bf16 [d_out][8 d_in]); dC = dy^T basis(x) through the
+// weight-gradient kernel (fp32 partials as launch_wgrad with M = d_out,
+// N = 8 d_in); dx from G = dy C (bf16 [rows][8 d_in], d_in a multiple of 8).
+hipError_t launch_cheby_forward(const void *x, const void *C, void *y, int64_t rows, int64_t d_in, int64_t d_out,
+                                hipStream_t s);
+hipError_t launch_cheby_wgrad(const void *dy, const void *x, float *partials, float *dC, int64_t rows,
+                              int64_t d_out, int64_t d_in, hipStream_t s);
+hipError_t launch_cheby_dx(const void *x, const void *G, void *dx, int64_t rows, int64_t d_in, hipStream_t s);
 // out [C][R] = in [R][C]^T, bf16.
 hipError_t launch_transpose16(const void *in, void *out, int64_t R, int64_t C, hipStream_t s);
 

@@ -76,11 +76,18 @@ static_assert(kBM * kChunksPerRow % kThreads == 0 && kBN * kChunksPerRow % kThre
 static_assert(kCA == kKSteps && kCB == kKSteps, "one chunk of each tile is staged per K sub-step");
 static_assert(kThreads % kChunksPerRow == 0, "a thread's chunks share one column");
 
+// What the A operand is made of.
+enum Prologue : int {
+    kPlain = 0,     // A = x itself (bf16 [M][K])
+    kRational = 1,  // A = bf16(F(x)), F the group-rational activation (x bf16 [M][K])
+    kChebyshev = 2  // A = bf16(T_k(tanh(x_i))) at K position 8 i + k, k = 0..7 (x bf16 [M][K / 8])
+};
+
 struct LayerArgs {
-    const uint16_t *x;  // [M][K] bf16 (activation input, or y for the plain GEMM)
+    const uint16_t *x;  // A's source (see Prologue)
     const uint16_t *w;  // [N][K] bf16
     uint16_t *z;        // [M][N] bf16
-    const float *A;     // [n_groups][6] (fused variant)
+    const float *A;     // [n_groups][6] (kRational)
     const float *B;     // [n_groups][4]
     int32_t M, N, K, d_g, n_groups;
 };
@@ -96,8 +103,40 @@ __device__ static inline u32x4 activate8(u32x4 v, const Coefs<5, 4> &c) {
     return Io<bf16io>::pack(f);
 }
 
-template <bool FUSED>
+// tanh in fp32, absolute error below 2^-21: for |x| < 0.55 its odd Taylor
+// series through x^15 (the next term is below 3e-8 there); above, 1 - 2 /
+// (e^(2|x|) + 1) with the sign of x, from the hardware base-2 exponential
+// and reciprocal (no cancellation: the fraction is below 0.55).
+__device__ static inline float tanh_f32(float x) {
+    const float ax = fabsf(x), x2 = x * x;
+    float p = -929569.0f / 638512875.0f;
+    p = fmaf(p, x2, 21844.0f / 6081075.0f);
+    p = fmaf(p, x2, -1382.0f / 155925.0f);
+    p = fmaf(p, x2, 62.0f / 2835.0f);
+    p = fmaf(p, x2, -17.0f / 315.0f);
+    p = fmaf(p, x2, 2.0f / 15.0f);
+    p = fmaf(p, x2, -1.0f / 3.0f);
+    const float series = fmaf(p * x2, x, x);
+    const float e = __builtin_amdgcn_exp2f(ax * 2.8853900817779268f);  // e^(2|x|)
+    const float q = 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
+    return ax < 0.55f ? series : __builtin_copysignf(q, x);
+}
+
+// The Chebyshev basis T_0..T_7 of t = tanh(x) as 8 bf16 (the order of the K
+// positions 8 i .. 8 i + 7), by the three-term recurrence.
+__device__ static inline u32x4 chebyshev8(uint32_t xbits) {
+    const float t = tanh_f32(__uint_as_float(xbits << 16)), t2 = t + t;
+    float T[8];
+    T[0] = 1.0f;
+    T[1] = t;
+#pragma unroll
+    for (int k = 1; k < 7; ++k) T[k + 1] = fmaf(t2, T[k], -T[k - 1]);
+    return Io<bf16io>::pack(T);
+}
+
+template <int PRO>
 __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a) {
+    constexpr bool FUSED = PRO == kRational;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     __shared__ float coef[kMaxLayerGroups * 12];
     const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -114,14 +153,18 @@ __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a)
     }
 
     // Source rows of this thread's chunks.  Rows past the end are clamped to
-    // the last row: they only feed outputs that are never stored.
+    // the last row: they only feed outputs that are never stored.  A
+    // Chebyshev chunk is the basis of one x value: x index 8 k-step + cc.
     const int cc = t % kChunksPerRow;
     const uint16_t *pa[kCA];
     const uint16_t *pb[kCB];
 #pragma unroll
     for (int j = 0; j < kCA; ++j) {
         const int r = (t + kThreads * j) / kChunksPerRow;
-        pa[j] = a.x + (size_t)min(m0 + r, a.M - 1) * a.K + cc * 8;
+        if constexpr (PRO == kChebyshev)
+            pa[j] = a.x + (size_t)min(m0 + r, a.M - 1) * (a.K / 8) + cc;
+        else
+            pa[j] = a.x + (size_t)min(m0 + r, a.M - 1) * a.K + cc * 8;
     }
 #pragma unroll
     for (int j = 0; j < kCB; ++j) {
@@ -129,9 +172,15 @@ __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a)
         pb[j] = a.w + (size_t)min(n0 + r, a.N - 1) * a.K + cc * 8;
     }
     u32x4 ra[kCA], rb[kCB];
+    uint32_t rx[kCA];
     auto load_tiles = [&](int kt) {
 #pragma unroll
-        for (int j = 0; j < kCA; ++j) ra[j] = *reinterpret_cast<const u32x4 *>(pa[j] + kt * kBK);
+        for (int j = 0; j < kCA; ++j) {
+            if constexpr (PRO == kChebyshev)
+                rx[j] = pa[j][kt * (kBK / 8)];
+            else
+                ra[j] = *reinterpret_cast<const u32x4 *>(pa[j] + kt * kBK);
+        }
 #pragma unroll
         for (int j = 0; j < kCB; ++j) rb[j] = *reinterpret_cast<const u32x4 *>(pb[j] + kt * kBK);
     };
@@ -145,7 +194,8 @@ __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a)
     };
     // Chunk j of this thread's share of both tiles -> LDS stage buf.
     auto stage_chunk = [&](int buf, int j) {
-        if (FUSED) ra[j] = activate8(ra[j], c);
+        if constexpr (FUSED) ra[j] = activate8(ra[j], c);
+        if constexpr (PRO == kChebyshev) ra[j] = chebyshev8(rx[j]);
         uint16_t *s = lds + buf * kStage;
         const int r = (t + kThreads * j) / kChunksPerRow;
         *reinterpret_cast<u32x4 *>(s + r * kLdk + cc * 8) = ra[j];
@@ -246,7 +296,8 @@ constexpr size_t kWgLdsBytes = 2 * (size_t)kWgStage * 2;
 
 struct WgradArgs {
     const uint16_t *a;   // [rows][M] bf16 (dZ)
-    const uint16_t *b;   // [rows][N] bf16 (Y = F(x))
+    const uint16_t *b;   // [rows][N] bf16 (Y = F(x)); with CHEBY_B x [rows][N / 8], whose
+                         // Chebyshev basis (chebyshev8) is the operand
     float *partials;     // [splits][M][N]
     int32_t rows, M, N, splits, rows_per_split;
 };
@@ -261,6 +312,7 @@ __device__ static inline int wg_chunk(int m, int chunk) {
     return m * kWgRow + ((chunk ^ ((m + (m >> 3)) & 7)) << 3);
 }
 
+template <bool CHEBY_B>
 __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -280,8 +332,11 @@ __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
     static_assert(kThreads / kColChunks * 4 == kBK && kBM == kBN, "one 64-row step per thread set");
     const int cc = t % kColChunks, rg = t / kColChunks;
     const uint16_t *pa = a.a + min(m0 + cc * 8, a.M - 8);
-    const uint16_t *pb = a.b + min(n0 + cc * 8, a.N - 8);
+    const int bld = CHEBY_B ? a.N / 8 : a.N;  // elements per row of b
+    const uint16_t *pb = CHEBY_B ? a.b + min(n0 / 8 + cc, bld - 1) : a.b + min(n0 + cc * 8, a.N - 8);
     u32x4 ra[4], rb[4];
+    uint32_t rx[4];
+    bool rin[4];
     auto load_tiles = [&](int kt) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -289,13 +344,24 @@ __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
             const bool in = r < r_end;
             const size_t rr = (size_t)(in ? r : r_begin);
             const u32x4 va = *reinterpret_cast<const u32x4 *>(pa + rr * a.M);
-            const u32x4 vb = *reinterpret_cast<const u32x4 *>(pb + rr * a.N);
             ra[q] = in ? va : u32x4{0u, 0u, 0u, 0u};
-            rb[q] = in ? vb : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (CHEBY_B) {
+                rx[q] = pb[rr * bld];
+                rin[q] = in;
+            } else {
+                const u32x4 vb = *reinterpret_cast<const u32x4 *>(pb + rr * a.N);
+                rb[q] = in ? vb : u32x4{0u, 0u, 0u, 0u};
+            }
         }
     };
     // Columns 2h and 2h + 1 of the chunks -> LDS rows cc*8 + 2h (+ 1), k = 4 rg .. 4 rg + 3.
     auto stage_pair = [&](int buf, int h) {
+        if constexpr (CHEBY_B) {
+            if (h == 0) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) rb[q] = rin[q] ? chebyshev8(rx[q]) : u32x4{0u, 0u, 0u, 0u};
+            }
+        }
         uint16_t *s = lds + buf * kWgStage;
         const int sub = (rg & 1) * 4;
 #pragma unroll
@@ -397,17 +463,44 @@ __global__ __launch_bounds__(256) void grkan_transpose16_kernel(const uint16_t *
     }
 }
 
-std::once_flag g_attr_once[3];
-hipError_t g_attr_err[3];
+// Chebyshev-KAN input gradient from G = dy C (bf16 [rows][8 d_in]):
+// dx[r][i] = (1 - t^2) sum_k T_k'(t) G[r][8 i + k], t = tanh(x[r][i]),
+// T_k' = k U_{k-1} (U: the second-kind polynomials, U_0 = 1, U_1 = 2t,
+// U_{k+1} = 2t U_k - U_{k-1}).  One thread per element: its 16 bytes of G
+// sit next to its neighbours', so a wave reads 1 KB of G contiguously.
+__global__ __launch_bounds__(256) void grkan_cheby_dx_kernel(const uint16_t *__restrict__ x,
+                                                             const uint16_t *__restrict__ G,
+                                                             uint16_t *__restrict__ dx, int64_t n) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n) return;
+    float g[8];
+    Io<bf16io>::unpack(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(G + idx * 8)), g);
+    const float t = tanh_f32(__uint_as_float((uint32_t)x[idx] << 16)), t2 = t + t;
+    float um = 1.0f, u = t2;                   // U_0, U_1
+    float sum = g[1];                          // T_1' = 1 U_0
+    sum = fmaf(2.0f * u, g[2], sum);           // T_2' = 2 U_1
+#pragma unroll
+    for (int k = 3; k <= 7; ++k) {
+        const float un = fmaf(t2, u, -um);     // U_{k-1}
+        um = u;
+        u = un;
+        sum = fmaf((float)k * u, g[k], sum);
+    }
+    const __bf16 h = (__bf16)(fmaf(-t, t, 1.0f) * sum);
+    dx[idx] = __builtin_bit_cast(uint16_t, h);
+}
 
-template <bool FUSED>
+std::once_flag g_attr_once[4];
+hipError_t g_attr_err[4];
+
+template <int PRO>
 hipError_t launch(const LayerArgs &a, hipStream_t s) {
-    auto kern = grkan_layer_gemm_kernel<FUSED>;
-    std::call_once(g_attr_once[FUSED], [&] {
-        g_attr_err[FUSED] = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    auto kern = grkan_layer_gemm_kernel<PRO>;
+    std::call_once(g_attr_once[PRO], [&] {
+        g_attr_err[PRO] = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     });
-    if (g_attr_err[FUSED] != hipSuccess) return g_attr_err[FUSED];
+    if (g_attr_err[PRO] != hipSuccess) return g_attr_err[PRO];
     const int64_t mb = (a.M + kBM - 1) / kBM, nb = (a.N + kBN - 1) / kBN;
     const int64_t grid = (mb + 7) / 8 * 8 * nb;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
@@ -423,7 +516,7 @@ hipError_t launch_layer_forward(const void *x, const float *A, const float *B, c
                                 int64_t rows, int64_t d_in, int64_t d_out, int32_t n_groups, hipStream_t s) {
     LayerArgs a{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(W), static_cast<uint16_t *>(z),
                 A, B, (int32_t)rows, (int32_t)d_out, (int32_t)d_in, (int32_t)(d_in / n_groups), n_groups};
-    return launch<true>(a, s);
+    return launch<kRational>(a, s);
 }
 
 int wgrad_splits(int64_t rows, int64_t M, int64_t N) {
@@ -438,14 +531,17 @@ size_t wgrad_partials_bytes(int64_t rows, int64_t M, int64_t N) {
     return (size_t)wgrad_splits(rows, M, N) * (size_t)M * (size_t)N * sizeof(float);
 }
 
-hipError_t launch_wgrad(const void *dz, const void *y, float *partials, float *dW, int64_t rows, int64_t M,
-                        int64_t N, hipStream_t s) {
-    auto kern = grkan_wgrad_kernel;
-    std::call_once(g_attr_once[2], [&] {
-        g_attr_err[2] = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWgLdsBytes);
+template <bool CHEBY_B>
+hipError_t launch_wgrad_impl(const void *dz, const void *y, float *partials, float *dW, int64_t rows, int64_t M,
+                             int64_t N, hipStream_t s) {
+    auto kern = grkan_wgrad_kernel<CHEBY_B>;
+    static std::once_flag once;
+    static hipError_t err;
+    std::call_once(once, [&] {
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)kWgLdsBytes);
     });
-    if (g_attr_err[2] != hipSuccess) return g_attr_err[2];
+    if (err != hipSuccess) return err;
     const int splits = wgrad_splits(rows, M, N);
     const int64_t steps = (rows + kBK - 1) / kBK;
     const int rps = (int)((steps + splits - 1) / splits) * kBK;
@@ -461,6 +557,24 @@ hipError_t launch_wgrad(const void *dz, const void *y, float *partials, float *d
     return hipGetLastError();
 }
 
+hipError_t launch_wgrad(const void *dz, const void *y, float *partials, float *dW, int64_t rows, int64_t M,
+                        int64_t N, hipStream_t s) {
+    return launch_wgrad_impl<false>(dz, y, partials, dW, rows, M, N, s);
+}
+
+hipError_t launch_cheby_wgrad(const void *dy, const void *x, float *partials, float *dC, int64_t rows,
+                              int64_t d_out, int64_t d_in, hipStream_t s) {
+    return launch_wgrad_impl<true>(dy, x, partials, dC, rows, d_out, d_in * 8, s);
+}
+
+hipError_t launch_cheby_dx(const void *x, const void *G, void *dx, int64_t rows, int64_t d_in, hipStream_t s) {
+    const int64_t n = rows * d_in;
+    hipLaunchKernelGGL(grkan_cheby_dx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(G), static_cast<uint16_t *>(dx),
+                       n);
+    return hipGetLastError();
+}
+
 hipError_t launch_transpose16(const void *in, void *out, int64_t R, int64_t C, hipStream_t s) {
     hipLaunchKernelGGL(grkan_transpose16_kernel, dim3((unsigned)((C + 31) / 32), (unsigned)((R + 31) / 32)),
                        dim3(256), 0, s, static_cast<const uint16_t *>(in), static_cast<uint16_t *>(out), (int)R,
@@ -468,11 +582,18 @@ hipError_t launch_transpose16(const void *in, void *out, int64_t R, int64_t C, h
     return hipGetLastError();
 }
 
+hipError_t launch_cheby_forward(const void *x, const void *C, void *y, int64_t rows, int64_t d_in, int64_t d_out,
+                                hipStream_t s) {
+    LayerArgs a{static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(C), static_cast<uint16_t *>(y),
+                nullptr, nullptr, (int32_t)rows, (int32_t)d_out, (int32_t)(d_in * 8), 1, 1};
+    return launch<kChebyshev>(a, s);
+}
+
 hipError_t launch_linear_forward(const void *y, const void *W, void *z, int64_t rows, int64_t d_in,
                                  int64_t d_out, hipStream_t s) {
     LayerArgs a{static_cast<const uint16_t *>(y), static_cast<const uint16_t *>(W), static_cast<uint16_t *>(z),
                 nullptr, nullptr, (int32_t)rows, (int32_t)d_out, (int32_t)d_in, 1, 1};
-    return launch<false>(a, s);
+    return launch<kPlain>(a, s);
 }
 
 }  // namespace grkan

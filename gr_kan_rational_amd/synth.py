@@ -38,6 +38,15 @@ no initialisation for it), rounded to bf16:
 upstream gradient dZ [rows, d_out] ~ N(0, 1e-2) (tensor 3 below) in place of
 dY.
 
+A Chebyshev-KAN layer (degree 7: 8 basis functions per input) draws its
+coefficients C [d_out, d, 8] ~ N(0, 1/sqrt(8 d)) the same way, rounded to
+bf16, and its upstream gradient as a layer's dZ:
+
+    kat-b-cheby-bf16   X [1024, 197, 768]  -> 768 outputs             seed 13
+
+(the shape of a KAT-B token mixer's input stands in for PolyKAN's speech,
+audio and tabular workloads, which the pages do not size).
+
 Recipe (reproducible, independent of the number of threads):
   * A then B (then W, for a layer) from ``numpy.random.default_rng(seed)``
     as float32 standard normals, multiplied by the std in float32;
@@ -76,6 +85,7 @@ class Workload:
     m: int = 5         # numerator degree (a_0..a_m)
     n: int = 4         # denominator degree (b_1..b_n)
     d_out: int = 0     # outputs of the layer's linear map (0: the activation alone)
+    cheby: int = 0     # Chebyshev-KAN degree (0: a GR-KAN workload)
 
     @property
     def rows(self) -> int:
@@ -113,6 +123,7 @@ WORKLOADS = {
         Workload("kat-b-perchan", 1024, 197, 768, 768, "f32", 0.5, 1.0, 1e-2, 10),
         Workload("kat-b-layer1-bf16", 1024, 197, 768, 8, "bf16", 0.5, 1.0, 1e-2, 11, d_out=3072),
         Workload("kat-b-layer2-bf16", 1024, 197, 3072, 8, "bf16", 0.5, 1.0, 1e-2, 12, d_out=768),
+        Workload("kat-b-cheby-bf16", 1024, 197, 768, 1, "bf16", 0.5, 1.0, 1e-2, 13, d_out=768, cheby=7),
     )
 }
 
@@ -120,12 +131,15 @@ WORKLOADS = {
 GRKAN_WORKLOADS = ("tiny", "kat-t", "kat-s-hid", "kat-b", "kat-b-hid-bf16")
 PAU_WORKLOADS = ("kat-b-pau", "kat-b-r32", "kat-b-r76", "kat-b-poly5", "kat-b-perchan")
 LAYER_WORKLOADS = ("kat-b-layer1-bf16", "kat-b-layer2-bf16")
+CHEBY_WORKLOADS = ("kat-b-cheby-bf16",)
 
 
 def custom(name: str, rows: int, d: int, n_groups: int, m: int = 5, n: int = 4, io: str = "f32",
-           seed: int = 100, coef_std: float = 0.5, dy_std: float = 1e-2, d_out: int = 0) -> Workload:
+           seed: int = 100, coef_std: float = 0.5, dy_std: float = 1e-2, d_out: int = 0,
+           cheby: int = 0) -> Workload:
     """A workload of the same recipe with any shape, group count and degrees."""
-    return Workload(name, rows, 1, d, n_groups, io, coef_std, 1.0, dy_std, seed, m=m, n=n, d_out=d_out)
+    return Workload(name, rows, 1, d, n_groups, io, coef_std, 1.0, dy_std, seed, m=m, n=n, d_out=d_out,
+                    cheby=cheby)
 
 
 def _threads() -> int:
@@ -165,10 +179,15 @@ def coefficients(w: Workload) -> tuple[np.ndarray, np.ndarray]:
 
 
 def weight(w: Workload) -> np.ndarray:
-    """The layer's W [d_out, d] as bf16 bit patterns (uint16)."""
+    """The layer's W [d_out, d] (Chebyshev: C [d_out, d, degree + 1]) as bf16 bit patterns."""
     if w.d_out <= 0:
         raise ValueError("not a layer workload")
     rng, _, _ = _draws(w)
+    if w.cheby:
+        nb = w.cheby + 1
+        C = rng.standard_normal((w.d_out, w.d, nb), dtype=np.float32)
+        C *= np.float32(1.0 / np.sqrt(w.d * nb))
+        return bf16_bits(C).reshape(w.d_out, w.d, nb)
     W = rng.standard_normal((w.d_out, w.d), dtype=np.float32)
     W *= np.float32(1.0 / np.sqrt(w.d))
     return bf16_bits(W).reshape(w.d_out, w.d)

@@ -275,6 +275,44 @@ GRKAN_API grkan_status_t grkan_layer_backward(const void *x, const void *dz, con
 GRKAN_API size_t grkan_layer_backward_workspace_size(int64_t rows, int64_t d_in, int64_t d_out,
                                            int32_t n_groups);
 
+/*
+ * Chebyshev-KAN layer ([PolyKAN]: "PolyKAN: Efficient Fused GPU Operators for
+ * Polynomial Kolmogorov-Arnold Network Variants", abstract page, arXiv
+ * 2511.14852, whose case study it is):
+ *   y[r][o] = sum_i sum_{k=0..D} C[o][i][k] T_k(tanh(x[r][i]))
+ * with T_k the Chebyshev polynomials of the first kind.  bf16 x, C, y; the
+ * basis is computed in fp32 and rounded to nearest-even bf16 as the matrix
+ * operand, products accumulate in fp32 on the matrix cores; the basis is
+ * built while x is staged for the product, so it never goes to memory.
+ *   x     bf16 [rows][d_in] (2-byte aligned; 16-byte aligned for the backward).
+ *   C     bf16 [d_out][d_in][D + 1] (degree fastest), 16-byte aligned.
+ *   y     bf16 [rows][d_out]; must not overlap x or C.
+ *   degree D = 7 only (8 basis functions; others GRKAN_ERR_UNSUPPORTED);
+ *   d_in a multiple of 8; rows >= 0 (0 is a no-op).
+ */
+GRKAN_API grkan_status_t grkan_chebykan_forward(const void *x, const void *C, void *y, int64_t rows,
+                                      int64_t d_in, int64_t d_out, int32_t degree,
+                                      hipStream_t stream);
+
+/*
+ * Its backward, given dy = dL/dy (bf16 [rows][d_out], 16-byte aligned):
+ *   dC[o][i][k] = sum_r dy[r][o] T_k(tanh x[r][i])     fp32 [d_out][d_in][D+1]
+ *   dx[r][i]    = (1 - t^2) sum_k T_k'(t) G[r][i][k]   bf16, t = tanh x[r][i]
+ * with G = dy C formed on the matrix cores and held in bf16 (as a bf16
+ * layer's gradient of its basis); dC sums row splits in fp32 and the
+ * splits in a fixed order in fp64 (bitwise reproducible).  dx may be x
+ * itself; workspace: grkan_chebykan_backward_workspace_size() bytes,
+ * 256-byte aligned.  Also needs d_out a multiple of 64.  rows == 0 writes
+ * zeros to dC.
+ */
+GRKAN_API grkan_status_t grkan_chebykan_backward(const void *x, const void *dy, const void *C,
+                                       void *dx, float *dC, int64_t rows, int64_t d_in,
+                                       int64_t d_out, int32_t degree, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+GRKAN_API size_t grkan_chebykan_backward_workspace_size(int64_t rows, int64_t d_in, int64_t d_out,
+                                              int32_t degree);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,7 +42,8 @@ def test_header_declares_the_abi():
         "grkan_pau_backward_workspace_size", "grkan_pau_query_launch",
         "grkan_inflated_forward", "grkan_inflated_backward",
         "grkan_layer_forward", "grkan_linear_forward", "grkan_layer_backward",
-        "grkan_layer_backward_workspace_size"])
+        "grkan_layer_backward_workspace_size", "grkan_chebykan_forward", "grkan_chebykan_backward",
+        "grkan_chebykan_backward_workspace_size"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -312,3 +313,47 @@ def test_layer_backward_workspace_size(lib):
 ])
 def test_layer_backward_rejects(lib, kw, code):
     assert lbwd(lib, **kw) == code
+
+
+# ------------------------------------------------------------ Chebyshev KAN
+
+def cfwd(lib, x=P, C=P + 0x400000, y=P + 0x800000, rows=4, d_in=64, d_out=64, deg=7):
+    return lib.grkan_chebykan_forward(x, C, y, rows, d_in, d_out, deg, None)
+
+
+def cbwd(lib, x=P, dy=P + 0x100000, C=P + 0x400000, dx=P + 0x800000, dC=P + 0xA00000, rows=4, d_in=64,
+         d_out=64, deg=7, ws=P + 0x1000000, ws_bytes=1 << 30):
+    return lib.grkan_chebykan_backward(x, dy, C, dx, dC, rows, d_in, d_out, deg, ws, ws_bytes, None)
+
+
+def test_chebykan_workspace_size(lib):
+    f = lib.grkan_chebykan_backward_workspace_size
+    a256 = lambda v: (v + 255) // 256 * 256
+    # KAT-B shape: C^T (6144 x 768 bf16), G (rows x 6144 bf16), dC split partials: 3 x 24 = 72 output
+    # tiles -> ceil(1024 / 72) = 15 splits of fp32 [768][6144]
+    assert f(201728, 768, 768, 7) == a256(6144 * 768 * 2) + a256(201728 * 6144 * 2) + a256(15 * 768 * 6144 * 4)
+    assert f(0, 64, 64, 7) == 0
+    assert f(10, 64, 96, 7) == 0        # d_out not a multiple of 64
+    assert f(10, 64, 64, 3) == 0        # degree 7 only
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(C=None), INVALID), (dict(x=None), INVALID), (dict(y=None), INVALID), (dict(rows=-1), INVALID),
+    (dict(deg=3), UNSUPPORTED), (dict(deg=-1), INVALID), (dict(d_in=4), UNSUPPORTED),
+    (dict(C=P + 0x400008), UNSUPPORTED), (dict(x=P + 1), UNSUPPORTED), (dict(y=P + 64), INVALID),
+])
+def test_chebykan_forward_rejects(lib, kw, code):
+    assert cfwd(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dC=None), INVALID), (dict(dx=None), INVALID), (dict(ws=None), INVALID), (dict(ws_bytes=100), INVALID),
+    (dict(d_out=96), UNSUPPORTED), (dict(x=P + 2), UNSUPPORTED), (dict(dx=P + 64), INVALID),
+    (dict(dC=P + 0x400000), INVALID), (dict(ws=P + 0x1000010), UNSUPPORTED), (dict(ws=P + 0x800000), INVALID),
+])
+def test_chebykan_backward_rejects(lib, kw, code):
+    assert cbwd(lib, **kw) == code
+
+
+def test_chebykan_empty_is_ok_without_device(lib):
+    assert cfwd(lib, x=None, y=None, rows=0) == OK
