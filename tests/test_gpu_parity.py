@@ -128,6 +128,33 @@ def test_parity_full_size(gk, name):
         np.testing.assert_allclose(np.array(g["dB"]), ref["dB"], rtol=1e-12, atol=0)
 
 
+def test_parity_tensors_beyond_4_gib(gk):
+    """Tensors of 4.96 GB (fp32 [403456, 3072], twice KAT-B's hidden rows): byte offsets past
+    2^31 and 2^32 within one tensor, several launches of whole tile bundles.  Sampled
+    elements (including the first and last rows) and the full group sums against the oracle."""
+    w = synth.custom("beyond-4gib", 403456, 3072, 8, io="f32", seed=9100)
+    log(f"[parity_4gib] rows={w.rows} d={w.d}: generating inputs")
+    inp = synth.make_inputs(w)
+    x, dy, A, B = dev_inputs(inp)
+    log("[parity_4gib] forward + backward on GPU")
+    y = gk.grkan_forward(x, A, B, w.n_groups)
+    dx, dA, dB = gk.grkan_backward(x, dy, A, B, w.n_groups)
+    torch.cuda.synchronize()
+    edges = np.concatenate([np.arange(e - 3 * w.d, e + 3 * w.d, dtype=np.int64) for e in (1 << 29, 1 << 30)])
+    idx = np.unique(np.concatenate([sample_indices(w), edges]))   # byte offsets 2^31 and 2^32
+    it = torch.from_numpy(idx).to(DEV)
+    ys = to_host(y.reshape(-1).index_select(0, it), w.io)
+    dxs = to_host(dx.reshape(-1).index_select(0, it), w.io)
+    del y, dx, x, dy
+    log(f"[parity_4gib] oracle on {idx.size} sampled elements and the full group sums")
+    rec = orc.points(inp["x"], inp["A"], inp["B"], w.n_groups, idx, dy=inp["dy"], io=w.io)
+    parity.check_elem("4gib Y[sampled]", ys, rec[:, orc.F], rec[:, orc.FMAG], w.io)
+    parity.check_elem("4gib dX[sampled]", dxs, rec[:, orc.DX], rec[:, orc.DXMAG], w.io)
+    ref = orc.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io, elements=False)
+    parity.check_sums("4gib dA", dA.cpu().numpy(), ref["dA"], ref["nA"], mag=ref["mA"])
+    parity.check_sums("4gib dB", dB.cpu().numpy(), ref["dB"], ref["nB"], mag=ref["mB"])
+
+
 def special_inputs():
     """d = 64, 8 groups of 8 channels (32-byte group rows: a second geometry).
 
