@@ -34,6 +34,8 @@
 // LDS table -- interleaved with the MFMAs.
 // Workgroup order: XCD (b mod 8) takes whole 256-row panels, N tiles of a
 // panel back to back, so a panel of x is fetched into one XCD's L2 once.
+// Output: with 16-byte aligned rows of z, each wave stages its bf16 tile in
+// the idle LDS and writes 16-byte row chunks; otherwise one bf16 per store.
 //
 // Measured on MI355X (KAT-B MLP shapes, 201,728 rows, 951.9 GFLOP per
 // call): the plain GEMM runs at 900-1,040 TFLOP/s; the fused prologue costs
@@ -75,6 +77,8 @@ constexpr int kInterleave = 14;                       // VALU instructions sched
 static_assert(kBM * kChunksPerRow % kThreads == 0 && kBN * kChunksPerRow % kThreads == 0, "chunks");
 static_assert(kCA == kKSteps && kCB == kKSteps, "one chunk of each tile is staged per K sub-step");
 static_assert(kThreads % kChunksPerRow == 0, "a thread's chunks share one column");
+static_assert((kThreads / 64) * (kWTM / 2) * kWTN * 4 <= (int)kLdsBytes && kWTN == 128 && kWTM % 32 == 0,
+              "the bf16 output staging fits in the operand stages");
 
 // What the A operand is made of.
 enum Prologue : int {
@@ -255,7 +259,56 @@ __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a)
         if (more) load_fragments(cur ^ 1, 0, 0);
     }
 
-    // bf16 results; full tiles skip the range checks.
+    // bf16 results.  When rows of z are 16-byte aligned (N a multiple of 8),
+    // each wave stages its 64 x 128 tile in 16 KB of the (now idle) LDS and
+    // writes it back as 16-byte row chunks: an accumulator lane holds one
+    // column of 4-row runs, so pairs of rows are packed into one dword
+    // ([row pair][column], columns of row pairs 2, 3 mod 4 offset by 32 so
+    // the two lane halves of a write use different banks), then each lane
+    // reads 8 columns of a row pair and splits them into the two rows.
+    if ((a.N & 7) == 0 && (reinterpret_cast<uintptr_t>(a.z) & 15) == 0) {
+        __syncthreads();  // every wave is done with the operand stages
+        uint32_t *rd = reinterpret_cast<uint32_t *>(lds) + wv * (kWTM / 2) * kWTN;
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; v += 2) {
+                    const int p = i * 16 + 4 * (v >> 2) + 2 * (lane >> 5) + ((v & 3) >> 1);
+                    const int col = j * 32 + (lane & 31);
+                    const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][v]);
+                    const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][v + 1]);
+                    rd[p * kWTN + (col ^ (((p >> 1) & 1) << 5))] = lo | (hi << 16);
+                }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        constexpr int kGroups = (kWTM / 2) * (kWTN / 8);  // (row pair, 8 columns) per wave
+#pragma unroll
+        for (int u = 0; u < kGroups / 64; ++u) {
+            const int g = u * 64 + lane, p = g / (kWTN / 8), c8 = (g % (kWTN / 8)) * 8;
+            const uint32_t *src = rd + p * kWTN + (c8 ^ (((p >> 1) & 1) << 5));
+            const u32x4 d0 = *reinterpret_cast<const u32x4 *>(src);
+            const u32x4 d1 = *reinterpret_cast<const u32x4 *>(src + 4);
+            u32x4 r0, r1;  // rows 2 p and 2 p + 1: low and high halves of the dwords
+            r0[0] = __builtin_amdgcn_perm(d0[1], d0[0], 0x05040100u);
+            r0[1] = __builtin_amdgcn_perm(d0[3], d0[2], 0x05040100u);
+            r0[2] = __builtin_amdgcn_perm(d1[1], d1[0], 0x05040100u);
+            r0[3] = __builtin_amdgcn_perm(d1[3], d1[2], 0x05040100u);
+            r1[0] = __builtin_amdgcn_perm(d0[1], d0[0], 0x07060302u);
+            r1[1] = __builtin_amdgcn_perm(d0[3], d0[2], 0x07060302u);
+            r1[2] = __builtin_amdgcn_perm(d1[1], d1[0], 0x07060302u);
+            r1[3] = __builtin_amdgcn_perm(d1[3], d1[2], 0x07060302u);
+            const int row = m0 + wm * kWTM + 2 * p, col = n0 + wn * kWTN + c8;
+            if (col < a.N) {
+                if (row < a.M) *reinterpret_cast<u32x4 *>(a.z + (size_t)row * a.N + col) = r0;
+                if (row + 1 < a.M) *reinterpret_cast<u32x4 *>(a.z + (size_t)(row + 1) * a.N + col) = r1;
+            }
+        }
+        return;
+    }
+    // Otherwise one bf16 per store; full tiles skip the range checks.
     const bool full = m0 + kBM <= a.M && n0 + kBN <= a.N;
 #pragma unroll
     for (int i = 0; i < kTM; ++i)
