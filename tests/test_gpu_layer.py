@@ -83,6 +83,23 @@ def test_linear_parity(gk, shape):
     parity.check_layer(f"linear {shape}", host(z), ref, d_in)
 
 
+def test_linear_output_not_16_byte_aligned(gk):
+    """z two bytes past a 16-byte boundary: the kernel must store one bf16 at a time (the
+    16-byte row stores need aligned rows) and leave the element before z untouched."""
+    rows, d_in, d_out = 300, 256, 272
+    log(f"[linear misaligned z] rows={rows} d_in={d_in} d_out={d_out}")
+    inp = inputs(rows, d_in, 8, d_out, 6150)
+    buf = torch.full((rows * d_out + 8,), 7.0, dtype=torch.bfloat16, device=DEV)
+    z = buf[1:1 + rows * d_out].view(rows, d_out)
+    gk.grkan_linear_forward(bf(inp["x"]), bf(inp["W"]), out=z)
+    torch.cuda.synchronize()
+    assert float(buf[0]) == 7.0 and float(buf[-1]) == 7.0
+    yv = orc.to_f64(inp["x"], "bf16")
+    wv = orc.to_f64(inp["W"], "bf16")
+    ref = {"z": yv @ wv.T, "amb": np.zeros((rows, d_out)), "mag": np.abs(yv) @ np.abs(wv).T}
+    parity.check_layer("linear misaligned z", host(z), ref, d_in)
+
+
 def test_layer_special_values(gk):
     """Identity numerators with b = 0 (F = x, so z = x W^T exactly up to accumulation), exact
     zeros, a group at a root of Q, and an identity weight (z = bf16(F(x)))."""
