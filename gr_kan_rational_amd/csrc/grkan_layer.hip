@@ -340,9 +340,11 @@ __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a)
 // reads (8 consecutive m, one chunk) and the transposed writes (m = 8 cc + i
 // for 32 chunk columns cc) both spread over the banks.  The rows are cut
 // into splits so that the few output tiles (36 at the KAT-B shapes) still
-// fill the GPU; each workgroup writes its fp32 tile of partial sums, and
+// fill the GPU in whole rounds of one workgroup per CU (14 splits, 504
+// workgroups = 2 rounds at KAT-B); each workgroup writes its fp32 tile of partial sums, and
 // grkan_wgrad_reduce_kernel adds the splits in order (bitwise reproducible).
-constexpr int kWgSplitsTarget = 1024;  // workgroups to aim for
+constexpr int kWgSlots = 256;          // workgroups resident at once on MI355X (one per CU)
+constexpr int64_t kWgMaxSplitRows = 16384;  // rows summed in fp32 by one workgroup at most
 constexpr int kWgRow = kBK;            // bf16 per LDS row (unpadded)
 constexpr int kWgStage = (kBM + kBN) * kWgRow;
 constexpr size_t kWgLdsBytes = 2 * (size_t)kWgStage * 2;
@@ -573,11 +575,24 @@ hipError_t launch_layer_forward(const void *x, const float *A, const float *B, c
 }
 
 int wgrad_splits(int64_t rows, int64_t M, int64_t N) {
+    // A workgroup holds one CU (its LDS), so workgroups run in rounds of
+    // kWgSlots.  Take the fewest splits of at most kWgMaxSplitRows rows each
+    // whose rounds are at least 95% full (else the fullest within 64 more);
+    // a fixed rule, so the summation order does not depend on the device.
     const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
     const int64_t steps = (rows + kBK - 1) / kBK;
-    int64_t splits = (kWgSplitsTarget + tiles - 1) / tiles;
-    if (splits > steps) splits = steps;
-    return (int)(splits < 1 ? 1 : splits);
+    int64_t lo = (rows + kWgMaxSplitRows - 1) / kWgMaxSplitRows;
+    if (lo < 1) lo = 1;
+    if (lo >= steps) return (int)(steps < 1 ? 1 : steps);
+    int64_t best = lo;
+    double best_fill = 0.0;
+    for (int64_t sp = lo; sp <= steps && sp < lo + 64; ++sp) {
+        const int64_t wgs = tiles * sp, rounds = (wgs + kWgSlots - 1) / kWgSlots;
+        const double fill = (double)wgs / (double)(rounds * kWgSlots);
+        if (fill >= 0.95) return (int)sp;
+        if (fill > best_fill) best_fill = fill, best = sp;
+    }
+    return (int)best;
 }
 
 size_t wgrad_partials_bytes(int64_t rows, int64_t M, int64_t N) {

@@ -290,12 +290,13 @@ def lbwd(lib, x=P, dz=P + 0x100000, A=P + 0x200000, B=P + 0x300000, W=P + 0x4000
 def test_layer_backward_workspace_size(lib):
     f = lib.grkan_layer_backward_workspace_size
     # KAT-B layer 2: W^T (768 x 3072 bf16), one [rows][3072] bf16 buffer, the bf16 activation
-    # backward's partials (as grkan_backward_workspace_size), 29 row splits of fp32 dW partials
-    # (ceil(1024 / 36 output tiles)), each piece 256-byte aligned
+    # backward's partials (as grkan_backward_workspace_size), 14 row splits of fp32 dW partials
+    # (at most 16384 rows each: 13 at least; 36 output tiles x 14 = 504 workgroups fill two
+    # rounds of 256 to 98%, 13 would fill 91%), each piece 256-byte aligned
     a256 = lambda v: (v + 255) // 256 * 256
     act = lib.grkan_backward_workspace_size(201728, 3072, 8, BF16, 0)
     assert f(201728, 3072, 768, 8) == (a256(768 * 3072 * 2) + a256(201728 * 3072 * 2) + a256(act)
-                                      + a256(29 * 768 * 3072 * 4))
+                                      + a256(14 * 768 * 3072 * 4))
     assert f(0, 256, 64, 8) == 0
     assert f(100, 256, 96, 8) == 0      # d_out not a multiple of 64
     assert f(100, 96, 64, 8) == 0       # d_in not a multiple of 64
@@ -330,8 +331,8 @@ def test_chebykan_workspace_size(lib):
     f = lib.grkan_chebykan_backward_workspace_size
     a256 = lambda v: (v + 255) // 256 * 256
     # KAT-B shape: C^T (6144 x 768 bf16), G (rows x 6144 bf16), dC split partials: 3 x 24 = 72 output
-    # tiles -> ceil(1024 / 72) = 15 splits of fp32 [768][6144]
-    assert f(201728, 768, 768, 7) == a256(6144 * 768 * 2) + a256(201728 * 6144 * 2) + a256(15 * 768 * 6144 * 4)
+    # tiles x 14 splits = 1008 workgroups (four rounds of 256, 98% full) of fp32 [768][6144]
+    assert f(201728, 768, 768, 7) == a256(6144 * 768 * 2) + a256(201728 * 6144 * 2) + a256(14 * 768 * 6144 * 4)
     assert f(0, 64, 64, 7) == 0
     assert f(10, 64, 96, 7) == 0        # d_out not a multiple of 64
     assert f(10, 64, 64, 3) == 0        # degree 7 only
