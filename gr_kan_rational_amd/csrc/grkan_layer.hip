@@ -334,20 +334,37 @@ __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a)
 // both operands, while an MFMA fragment wants 8 consecutive k of one m (or
 // n).  Each thread loads one 16-byte chunk (8 consecutive m) from each of 4
 // consecutive rows -- a wave reads 2 rows x 512 contiguous bytes per
-// instruction -- and writes it transposed: for each of its 8 m, the 4 rows
-// as one 8-byte LDS write.  LDS rows are [m][64 k] without padding, their
-// eight 16-byte chunks permuted by chunk ^ ((m + m / 8) mod 8): fragment
-// reads (8 consecutive m, one chunk) and the transposed writes (m = 8 cc + i
-// for 32 chunk columns cc) both spread over the banks.  The rows are cut
+// instruction -- and stages it in one of two ways:
+//   transposed writes (dW): for each of its 8 m, the 4 rows as one 8-byte
+//     LDS write.  LDS rows are [m][64 k] without padding, their eight
+//     16-byte chunks permuted by chunk ^ ((m + m / 8) mod 8): fragment reads
+//     (8 consecutive m, one chunk) and the transposed writes (m = 8 cc + i
+//     for 32 chunk columns cc) both spread over the banks;
+//   transposed reads (the Chebyshev dC, whose B chunks are built in
+//     registers): the tiles are stored as they lie, [64 k][256 m] with rows
+//     padded to 288 elements (rows k .. k + 3 start in four different
+//     quarters of the bank space), and fragments are read with gfx950's
+//     ds_read_b64_tr_b16 -- in each group of 16 lanes, lane i receives value
+//     j = i mod 4 of lane 4 j + i / 4's 8-byte read, so lanes 4 j + q
+//     pointing at row k0 + j, columns m0 + 4 q leave lane i with rows
+//     k0 .. k0 + 3 of column m0 + i; two such reads give the 8 k of a
+//     32 x 32 x 16 fragment.  Twice the LDS read instructions of the first
+//     way, but no packing and half the write instructions: faster where the
+//     basis already takes vector work, slower for the plain dW.
+// The rows are cut
 // into splits so that the few output tiles (36 at the KAT-B shapes) still
 // fill the GPU in whole rounds of one workgroup per CU (14 splits, 504
 // workgroups = 2 rounds at KAT-B); each workgroup writes its fp32 tile of partial sums, and
 // grkan_wgrad_reduce_kernel adds the splits in order (bitwise reproducible).
 constexpr int kWgSlots = 256;          // workgroups resident at once on MI355X (one per CU)
 constexpr int64_t kWgMaxSplitRows = 16384;  // rows summed in fp32 by one workgroup at most
-constexpr int kWgRow = kBK;            // bf16 per LDS row (unpadded)
-constexpr int kWgStage = (kBM + kBN) * kWgRow;
-constexpr size_t kWgLdsBytes = 2 * (size_t)kWgStage * 2;
+constexpr int kWgRow = kBK;            // transposed writes: bf16 per LDS row [m][64 k] (unpadded)
+constexpr int kWgPitch = kBM + 32;     // transposed reads: bf16 per LDS row [k][m] (padded)
+template <bool TR>
+constexpr int kWgStage = TR ? 2 * kBK * kWgPitch : (kBM + kBN) * kWgRow;
+template <bool TR>
+constexpr size_t kWgLdsBytes = 2 * (size_t)kWgStage<TR> * 2;
+static_assert(kBM == kBN, "A and B tiles share one layout");
 
 struct WgradArgs {
     const uint16_t *a;   // [rows][M] bf16 (dZ)
@@ -367,8 +384,18 @@ __device__ static inline int wg_chunk(int m, int chunk) {
     return m * kWgRow + ((chunk ^ ((m + (m >> 3)) & 7)) << 3);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing read: 4 consecutive rows of one column per lane (see above).
+__device__ static inline s16x4 read_tr(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+}
+
 template <bool CHEBY_B>
 __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
+    constexpr bool TR = CHEBY_B;  // staging by transposed reads (else transposed writes)
+    constexpr int kStg = kWgStage<TR>;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
     const int wm = wv / kWavesN, wn = wv % kWavesN;
@@ -409,15 +436,24 @@ __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
             }
         }
     };
-    // Columns 2h and 2h + 1 of the chunks -> LDS rows cc*8 + 2h (+ 1), k = 4 rg .. 4 rg + 3.
-    auto stage_pair = [&](int buf, int h) {
+    // Sub-step h's share of the staging.  Transposed reads: row 4 rg + h of
+    // this thread's chunks, as it lies.  Transposed writes: columns 2h and
+    // 2h + 1 of the chunks -> LDS rows cc*8 + 2h (+ 1), k = 4 rg .. 4 rg + 3.
+    auto stage_part = [&](int buf, int h) {
+        if constexpr (TR) {
+            if constexpr (CHEBY_B) rb[h] = rin[h] ? chebyshev8(rx[h]) : u32x4{0u, 0u, 0u, 0u};
+            uint16_t *s = lds + buf * kStg + (rg * 4 + h) * kWgPitch + cc * 8;
+            *reinterpret_cast<u32x4 *>(s) = ra[h];
+            *reinterpret_cast<u32x4 *>(s + kBK * kWgPitch) = rb[h];
+            return;
+        }
         if constexpr (CHEBY_B) {
             if (h == 0) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) rb[q] = rin[q] ? chebyshev8(rx[q]) : u32x4{0u, 0u, 0u, 0u};
             }
         }
-        uint16_t *s = lds + buf * kWgStage;
+        uint16_t *s = lds + buf * kStg;
         const int sub = (rg & 1) * 4;
 #pragma unroll
         for (int odd = 0; odd < 2; ++odd) {
@@ -438,8 +474,28 @@ __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
 #pragma unroll
         for (int j = 0; j < kTN; ++j) acc[i][j] = f32x16{};
     bf16x8 fa[2][kTM], fb[2][kTN];
+    // Transposed reads: lane l (group g = l / 16, i = l mod 16) points its two
+    // reads at rows 16 ks + 8 (g / 2) + 4 r + i / 4, columns base + 16 (g mod
+    // 2) + 4 (i mod 4).
+    const int frow = 8 * (lane >> 5) + ((lane & 15) >> 2), fcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     auto load_fragments = [&](int buf, int ks, int set) {
-        const uint16_t *s = lds + buf * kWgStage;
+        if constexpr (TR) {
+            const uint16_t *s = lds + buf * kStg + (16 * ks + frow) * kWgPitch + fcol;
+#pragma unroll
+            for (int i = 0; i < kTM; ++i) {
+                const uint16_t *p = s + wm * kWTM + i * 32;
+                const s16x4 lo = read_tr(p), hi = read_tr(p + 4 * kWgPitch);
+                fa[set][i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+#pragma unroll
+            for (int j = 0; j < kTN; ++j) {
+                const uint16_t *p = s + kBK * kWgPitch + wn * kWTN + j * 32;
+                const s16x4 lo = read_tr(p), hi = read_tr(p + 4 * kWgPitch);
+                fb[set][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            return;
+        }
+        const uint16_t *s = lds + buf * kStg;
         const int chunk = 2 * ks + (lane >> 5);
 #pragma unroll
         for (int i = 0; i < kTM; ++i)
@@ -453,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
     if (nk > 0) {
         load_tiles(0);
 #pragma unroll
-        for (int h = 0; h < 4; ++h) stage_pair(0, h);
+        for (int h = 0; h < 4; ++h) stage_part(0, h);
         if (nk > 1) load_tiles(1);
         __syncthreads();
         load_fragments(0, 0, 0);
@@ -470,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void grkan_wgrad_kernel(WgradArgs a) {
 #pragma unroll
                 for (int j = 0; j < kTN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
-            if (more) stage_pair(cur ^ 1, ks);
+            if (more) stage_part(cur ^ 1, ks);
         }
         if (kt + 2 < nk) load_tiles(kt + 2);
         __syncthreads();
@@ -607,7 +663,7 @@ hipError_t launch_wgrad_impl(const void *dz, const void *y, float *partials, flo
     static hipError_t err;
     std::call_once(once, [&] {
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)kWgLdsBytes);
+                                  (int)kWgLdsBytes<CHEBY_B>);
     });
     if (err != hipSuccess) return err;
     const int splits = wgrad_splits(rows, M, N);
@@ -616,7 +672,7 @@ hipError_t launch_wgrad_impl(const void *dz, const void *y, float *partials, flo
     WgradArgs a{static_cast<const uint16_t *>(dz), static_cast<const uint16_t *>(y), partials, (int32_t)rows,
                 (int32_t)M, (int32_t)N, splits, rps};
     const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * splits)), dim3(kThreads), kWgLdsBytes, s, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * splits)), dim3(kThreads), kWgLdsBytes<CHEBY_B>, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t n = M * N;
