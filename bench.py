@@ -361,8 +361,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the activation shards by rows with no "
-              "communication but the dA/dB all-reduce, which is not part of this build); "
+        print("bench.py measures one GPU only: the activation would shard by rows, with no "
+              "communication but an all-reduce of dA/dB, and no multi-GPU path is implemented; "
               "use --gpus 1", file=sys.stderr)
         return 2
 
