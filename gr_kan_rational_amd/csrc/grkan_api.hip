@@ -603,7 +603,7 @@ grkan_status_t cheby_shape(int64_t rows, int64_t d_in, int64_t d_out, int32_t de
 }
 
 struct ChebyBwdPlan {
-    size_t off_ct, off_g, off_wg, total;
+    size_t off_ct, off_wg, total;
 };
 
 grkan_status_t cheby_bwd_plan(int64_t rows, int64_t d_in, int64_t d_out, int32_t degree, ChebyBwdPlan *cp) {
@@ -612,8 +612,7 @@ grkan_status_t cheby_bwd_plan(int64_t rows, int64_t d_in, int64_t d_out, int32_t
     if (d_out % layer_k_step() != 0) return GRKAN_ERR_UNSUPPORTED;
     const int64_t kb = d_in * 8;
     cp->off_ct = 0;
-    cp->off_g = align256((size_t)kb * d_out * 2);
-    cp->off_wg = cp->off_g + align256((size_t)rows * kb * 2);
+    cp->off_wg = align256((size_t)kb * d_out * 2);
     cp->total = cp->off_wg + align256(wgrad_partials_bytes(rows, d_out, kb));
     return GRKAN_OK;
 }
@@ -681,12 +680,11 @@ extern "C" grkan_status_t grkan_chebykan_backward(const void *x, const void *dy,
     st = from_hip(launch_cheby_wgrad(dy, x, reinterpret_cast<float *>(ws + cp.off_wg), dC, rows, d_out, d_in,
                                      stream));
     if (st != GRKAN_OK) return st;
-    // G = dy C (bf16), over C^T so that both operands are K-contiguous; then dx
+    // G = dy C (bf16), over C^T so that both operands are K-contiguous, turned
+    // into dx in the matrix kernel's epilogue (G is never stored)
     st = from_hip(launch_transpose16(C, ws + cp.off_ct, d_out, kb, stream));
     if (st != GRKAN_OK) return st;
-    st = from_hip(launch_linear_forward(dy, ws + cp.off_ct, ws + cp.off_g, rows, d_out, kb, stream));
-    if (st != GRKAN_OK) return st;
-    return from_hip(launch_cheby_dx(x, ws + cp.off_g, dx, rows, d_in, stream));
+    return from_hip(launch_cheby_g_dx(dy, ws + cp.off_ct, x, dx, rows, d_out, d_in, stream));
 }
 
 extern "C" grkan_status_t grkan_inflated_forward(const void *x, void *y, const float *A,

@@ -154,12 +154,15 @@ hipError_t launch_wgrad(const void *dz, const void *y, float *partials, float *d
 // y = bf16(basis(x)) C^T with the basis built while staging (x bf16
 // [rows][d_in], C bf16 [d_out][8 d_in]); dC = dy^T basis(x) through the
 // weight-gradient kernel (fp32 partials as launch_wgrad with M = d_out,
-// N = 8 d_in); dx from G = dy C (bf16 [rows][8 d_in], d_in a multiple of 8).
+// N = 8 d_in); dx from G = dy C, computed by the plain GEMM over C^T
+// (Ct bf16 [8 d_in][d_out]) whose epilogue turns each bf16 row chunk of G
+// (the 8 values of one input) into that input's dx without storing G.
 hipError_t launch_cheby_forward(const void *x, const void *C, void *y, int64_t rows, int64_t d_in, int64_t d_out,
                                 hipStream_t s);
 hipError_t launch_cheby_wgrad(const void *dy, const void *x, float *partials, float *dC, int64_t rows,
                               int64_t d_out, int64_t d_in, hipStream_t s);
-hipError_t launch_cheby_dx(const void *x, const void *G, void *dx, int64_t rows, int64_t d_in, hipStream_t s);
+hipError_t launch_cheby_g_dx(const void *dy, const void *Ct, const void *x, void *dx, int64_t rows,
+                             int64_t d_out, int64_t d_in, hipStream_t s);
 // out [C][R] = in [R][C]^T, bf16.
 hipError_t launch_transpose16(const void *in, void *out, int64_t R, int64_t C, hipStream_t s);
 

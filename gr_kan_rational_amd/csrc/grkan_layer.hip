@@ -84,7 +84,9 @@ static_assert((kThreads / 64) * (kWTM / 2) * kWTN * 4 <= (int)kLdsBytes && kWTN 
 enum Prologue : int {
     kPlain = 0,     // A = x itself (bf16 [M][K])
     kRational = 1,  // A = bf16(F(x)), F the group-rational activation (x bf16 [M][K])
-    kChebyshev = 2  // A = bf16(T_k(tanh(x_i))) at K position 8 i + k, k = 0..7 (x bf16 [M][K / 8])
+    kChebyshev = 2, // A = bf16(T_k(tanh(x_i))) at K position 8 i + k, k = 0..7 (x bf16 [M][K / 8])
+    kChebyDx = 3    // A = x itself; the bf16 result G is not stored but turned into the
+                    // Chebyshev layer's dx (cheby_dx8) in the epilogue
 };
 
 struct LayerArgs {
@@ -94,6 +96,8 @@ struct LayerArgs {
     const float *A;     // [n_groups][6] (kRational)
     const float *B;     // [n_groups][4]
     int32_t M, N, K, d_g, n_groups;
+    const uint16_t *xc; // kChebyDx: the layer input x, bf16 [M][N / 8]
+    uint16_t *dxc;      // kChebyDx: dx, bf16 [M][N / 8]
 };
 
 // The coefficient table: group g at [g * 12]: a_0..a_5, b_1..b_4.
@@ -138,9 +142,31 @@ __device__ static inline u32x4 chebyshev8(uint32_t xbits) {
     return Io<bf16io>::pack(T);
 }
 
+// The Chebyshev layer's dx of one input from its 8 values g_k = (dy C)[8 i + k]
+// (bf16) and x (bf16): dx = (1 - t^2) sum_k k U_{k-1}(t) g_k, t = tanh(x), with
+// U the second-kind polynomials by their recurrence; rounded to bf16.
+__device__ static inline uint16_t cheby_dx8(u32x4 gbits, uint32_t xbits) {
+    float g[8];
+    Io<bf16io>::unpack(gbits, g);
+    const float t = tanh_f32(__uint_as_float(xbits << 16)), t2 = t + t;
+    float um = 1.0f, u = t2;                   // U_0, U_1
+    float sum = g[1];                          // T_1' = 1 U_0
+    sum = fmaf(2.0f * u, g[2], sum);           // T_2' = 2 U_1
+#pragma unroll
+    for (int k = 3; k <= 7; ++k) {
+        const float un = fmaf(t2, u, -um);     // U_{k-1}
+        um = u;
+        u = un;
+        sum = fmaf((float)k * u, g[k], sum);
+    }
+    const __bf16 h = (__bf16)(fmaf(-t, t, 1.0f) * sum);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
 template <int PRO>
 __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a) {
     constexpr bool FUSED = PRO == kRational;
+    constexpr bool CHEBY_DX = PRO == kChebyDx;
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     __shared__ float coef[kMaxLayerGroups * 12];
     const int t = (int)threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -266,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a)
     // ([row pair][column], columns of row pairs 2, 3 mod 4 offset by 32 so
     // the two lane halves of a write use different banks), then each lane
     // reads 8 columns of a row pair and splits them into the two rows.
-    if ((a.N & 7) == 0 && (reinterpret_cast<uintptr_t>(a.z) & 15) == 0) {
+    if (CHEBY_DX || ((a.N & 7) == 0 && (reinterpret_cast<uintptr_t>(a.z) & 15) == 0)) {
         __syncthreads();  // every wave is done with the operand stages
         uint32_t *rd = reinterpret_cast<uint32_t *>(lds) + wv * (kWTM / 2) * kWTN;
 #pragma unroll
@@ -301,7 +327,15 @@ __global__ __launch_bounds__(kThreads) void grkan_layer_gemm_kernel(LayerArgs a)
             r1[2] = __builtin_amdgcn_perm(d1[1], d1[0], 0x07060302u);
             r1[3] = __builtin_amdgcn_perm(d1[3], d1[2], 0x07060302u);
             const int row = m0 + wm * kWTM + 2 * p, col = n0 + wn * kWTN + c8;
-            if (col < a.N) {
+            if constexpr (CHEBY_DX) {
+                // the 8 columns are the 8 basis values of input col / 8
+                const int d_in = a.N >> 3;
+                const size_t e = (size_t)row * d_in + (col >> 3);
+                if (col < a.N) {
+                    if (row < a.M) a.dxc[e] = cheby_dx8(r0, a.xc[e]);
+                    if (row + 1 < a.M) a.dxc[e + d_in] = cheby_dx8(r1, a.xc[e + d_in]);
+                }
+            } else if (col < a.N) {
                 if (row < a.M) *reinterpret_cast<u32x4 *>(a.z + (size_t)row * a.N + col) = r0;
                 if (row + 1 < a.M) *reinterpret_cast<u32x4 *>(a.z + (size_t)(row + 1) * a.N + col) = r1;
             }
@@ -574,32 +608,6 @@ __global__ __launch_bounds__(256) void grkan_transpose16_kernel(const uint16_t *
     }
 }
 
-// Chebyshev-KAN input gradient from G = dy C (bf16 [rows][8 d_in]):
-// dx[r][i] = (1 - t^2) sum_k T_k'(t) G[r][8 i + k], t = tanh(x[r][i]),
-// T_k' = k U_{k-1} (U: the second-kind polynomials, U_0 = 1, U_1 = 2t,
-// U_{k+1} = 2t U_k - U_{k-1}).  One thread per element: its 16 bytes of G
-// sit next to its neighbours', so a wave reads 1 KB of G contiguously.
-__global__ __launch_bounds__(256) void grkan_cheby_dx_kernel(const uint16_t *__restrict__ x,
-                                                             const uint16_t *__restrict__ G,
-                                                             uint16_t *__restrict__ dx, int64_t n) {
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= n) return;
-    float g[8];
-    Io<bf16io>::unpack(__builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(G + idx * 8)), g);
-    const float t = tanh_f32(__uint_as_float((uint32_t)x[idx] << 16)), t2 = t + t;
-    float um = 1.0f, u = t2;                   // U_0, U_1
-    float sum = g[1];                          // T_1' = 1 U_0
-    sum = fmaf(2.0f * u, g[2], sum);           // T_2' = 2 U_1
-#pragma unroll
-    for (int k = 3; k <= 7; ++k) {
-        const float un = fmaf(t2, u, -um);     // U_{k-1}
-        um = u;
-        u = un;
-        sum = fmaf((float)k * u, g[k], sum);
-    }
-    const __bf16 h = (__bf16)(fmaf(-t, t, 1.0f) * sum);
-    dx[idx] = __builtin_bit_cast(uint16_t, h);
-}
 
 std::once_flag g_attr_once[4];
 hipError_t g_attr_err[4];
@@ -691,12 +699,12 @@ hipError_t launch_cheby_wgrad(const void *dy, const void *x, float *partials, fl
     return launch_wgrad_impl<true>(dy, x, partials, dC, rows, d_out, d_in * 8, s);
 }
 
-hipError_t launch_cheby_dx(const void *x, const void *G, void *dx, int64_t rows, int64_t d_in, hipStream_t s) {
-    const int64_t n = rows * d_in;
-    hipLaunchKernelGGL(grkan_cheby_dx_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(G), static_cast<uint16_t *>(dx),
-                       n);
-    return hipGetLastError();
+hipError_t launch_cheby_g_dx(const void *dy, const void *Ct, const void *x, void *dx, int64_t rows,
+                             int64_t d_out, int64_t d_in, hipStream_t s) {
+    LayerArgs a{static_cast<const uint16_t *>(dy), static_cast<const uint16_t *>(Ct), nullptr, nullptr, nullptr,
+                (int32_t)rows, (int32_t)(d_in * 8), (int32_t)d_out, 1, 1, static_cast<const uint16_t *>(x),
+                static_cast<uint16_t *>(dx)};
+    return launch<kChebyDx>(a, s);
 }
 
 hipError_t launch_transpose16(const void *in, void *out, int64_t R, int64_t C, hipStream_t s) {

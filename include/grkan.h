@@ -299,7 +299,8 @@ GRKAN_API grkan_status_t grkan_chebykan_forward(const void *x, const void *C, vo
  *   dC[o][i][k] = sum_r dy[r][o] T_k(tanh x[r][i])     fp32 [d_out][d_in][D+1]
  *   dx[r][i]    = (1 - t^2) sum_k T_k'(t) G[r][i][k]   bf16, t = tanh x[r][i]
  * with G = dy C formed on the matrix cores and held in bf16 (as a bf16
- * layer's gradient of its basis); dC sums row splits in fp32 and the
+ * layer's gradient of its basis), turned into dx by the same kernel (G
+ * never goes to memory); dC sums row splits in fp32 and the
  * splits in a fixed order in fp64 (bitwise reproducible).  dx may be x
  * itself; workspace: grkan_chebykan_backward_workspace_size() bytes,
  * 256-byte aligned.  Also needs d_out a multiple of 64.  rows == 0 writes

@@ -330,9 +330,9 @@ def cbwd(lib, x=P, dy=P + 0x100000, C=P + 0x400000, dx=P + 0x800000, dC=P + 0xA0
 def test_chebykan_workspace_size(lib):
     f = lib.grkan_chebykan_backward_workspace_size
     a256 = lambda v: (v + 255) // 256 * 256
-    # KAT-B shape: C^T (6144 x 768 bf16), G (rows x 6144 bf16), dC split partials: 3 x 24 = 72 output
-    # tiles x 14 splits = 1008 workgroups (four rounds of 256, 98% full) of fp32 [768][6144]
-    assert f(201728, 768, 768, 7) == a256(6144 * 768 * 2) + a256(201728 * 6144 * 2) + a256(14 * 768 * 6144 * 4)
+    # KAT-B shape: C^T (6144 x 768 bf16) and the dC split partials: 3 x 24 = 72 output tiles x 14
+    # splits = 1008 workgroups (four rounds of 256, 98% full) of fp32 [768][6144]
+    assert f(201728, 768, 768, 7) == a256(6144 * 768 * 2) + a256(14 * 768 * 6144 * 4)
     assert f(0, 64, 64, 7) == 0
     assert f(10, 64, 96, 7) == 0        # d_out not a multiple of 64
     assert f(10, 64, 64, 3) == 0        # degree 7 only
