@@ -84,9 +84,22 @@ def cpu_baseline(w, target_s: float = 10.0) -> dict:
     oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io, m=w.m, n=w.n)
     dt = time.perf_counter() - t0
     n = rows * w.d
+    # the same oracle on one thread, on a sample sized to ~a quarter of target_s
+
+    def one_thread(r):
+        i1 = synth.make_inputs(w, rows=r)
+        t = time.perf_counter()
+        oracle.run(i1["x"], i1["A"], i1["B"], w.n_groups, dy=i1["dy"], io=w.io, m=w.m, n=w.n, nthreads=1)
+        return time.perf_counter() - t
+
+    c1 = min(rows, calib_rows)
+    rows1 = int(min(rows, max(c1, c1 * target_s / 4 / max(one_thread(c1), 1e-3))))
+    dt1 = one_thread(rows1)
     return {"value": n / dt, "unit": "elements/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"first {rows} of {w.rows} rows ({n} elements) of {w.name}, forward + backward "
-                      f"(Y, dX, dA, dB) in fp64, {dt:.1f} s wall"}
+                      f"(Y, dX, dA, dB) in fp64, {dt:.1f} s wall",
+            "value_1_thread": rows1 * w.d / dt1,
+            "sample_1_thread": f"first {rows1} rows ({rows1 * w.d} elements), {dt1:.1f} s wall"}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
