@@ -31,7 +31,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "grkan_oracle.c")
-_LIB = os.path.join(_HERE, "libgrkan_oracle.so")
+# GRKAN_ORACLE_LIB names another build of grkan_oracle.c to load instead (the
+# mutation tests point it at copies with a planted mistake); never built here.
+_BUILT = os.path.join(_HERE, "libgrkan_oracle.so")
+_LIB_ENV = os.environ.get("GRKAN_ORACLE_LIB")
+_LIB = _LIB_ENV or _BUILT
 
 M, N = 5, 4             # GR-KAN's degrees: numerator a_0..a_5, denominator b_1..b_4
 NA, NB = M + 1, N
@@ -56,14 +60,14 @@ _CHUNK_ELEMS = 1 << 16
 
 def build(force: bool = True) -> str:
     """Compile ``grkan_oracle.c`` with gcc into ``libgrkan_oracle.so``."""
-    if not force and os.path.exists(_LIB):
-        return _LIB
-    tmp = _LIB + ".tmp"
+    if not force and os.path.exists(_BUILT):
+        return _BUILT
+    tmp = _BUILT + ".tmp"
     cmd = ["gcc", "-std=gnu11", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
            "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, _BUILT)
+    return _BUILT
 
 
 _lib_handle = None
@@ -73,6 +77,8 @@ def _lib():
     global _lib_handle
     if _lib_handle is None:
         if not os.path.exists(_LIB):
+            if _LIB_ENV:
+                raise FileNotFoundError(f"GRKAN_ORACLE_LIB={_LIB_ENV} does not exist")
             build()
         lib = ctypes.CDLL(_LIB)
         dp = ctypes.POINTER(ctypes.c_double)

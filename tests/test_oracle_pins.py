@@ -363,6 +363,52 @@ def test_magnitude_bounds_fp32_evaluation():
         assert abs(float(P / D) - r[orc.F]) <= 16 * u * r[orc.FMAG]
 
 
+def test_magnitude_covers_cancellation_in_the_denominator():
+    """Where Q(x) = x + b_2 x^2 nearly cancels (b_2 = fp32(-1/x), x in [1e3, 1e4]), an fp32
+    evaluation of Q is off by up to about 2^-24 x, so F = a_0 / (1 + |Q|) is off by up to
+    about |a_0| 2^-24 x: an error far above 2^-24 |F| that FMAG must still bound (it carries
+    the rounding of the denominator's terms, not only of the numerator's)."""
+    u = 2.0 ** -24
+    worst = 0.0
+    gen = np.random.default_rng(77)
+    for _ in range(64):
+        xv = np.float32(gen.uniform(1e3, 1e4))
+        b2 = np.float32(-1.0) / xv
+        a0 = np.float32(gen.uniform(0.5, 2.0))
+        r = orc.point(float(xv), 1.0, [float(a0), 0, 0, 0, 0, 0], [1.0, float(b2), 0, 0])
+        q = b2 * xv + np.float32(1)                      # fp32 Horner of b_1 + b_2 x, then times x
+        Q = q * xv
+        F32 = a0 / (np.float32(1) + np.abs(Q))
+        err = abs(float(F32) - r[orc.F])
+        assert err <= 16 * u * r[orc.FMAG]
+        worst = max(worst, err / (u * abs(r[orc.F])))
+    assert worst > 64        # the case does exercise the denominator's rounding
+
+
+def test_dx_magnitude_covers_cancellation_in_the_denominator_derivative():
+    """Where Q'(x) = 1 + 2 b_2 x nearly cancels (b_2 = fp32(-1/(2x)), so Q = x/2 > 0 and the sign
+    is certain), dF/dx = -a_0 Q' / D^2 is tiny and an fp32 evaluation of Q' is off by about
+    2^-25: DXMAG must bound that error, which is many times |dX| itself."""
+    u = 2.0 ** -24
+    worst = 0.0
+    gen = np.random.default_rng(78)
+    for _ in range(64):
+        xv = np.float32(gen.uniform(1e3, 1e4))
+        b2 = np.float32(-0.5) / xv
+        a0 = np.float32(gen.uniform(0.5, 2.0))
+        dyv = np.float32(gen.uniform(0.5, 2.0))
+        r = orc.point(float(xv), float(dyv), [float(a0), 0, 0, 0, 0, 0], [1.0, float(b2), 0, 0])
+        assert r[orc.SIGN] == 1
+        Q = (b2 * xv + np.float32(1)) * xv
+        Qd = (np.float32(2) * b2) * xv + np.float32(1)
+        D = np.float32(1) + np.abs(Q)
+        dX32 = dyv * (-(a0 * Qd) / (D * D))
+        err = abs(float(dX32) - r[orc.DX])
+        assert err <= 16 * u * r[orc.DXMAG]
+        worst = max(worst, err / (u * max(abs(r[orc.DX]), 1e-300)))
+    assert worst > 64        # the case does exercise the rounding of Q'
+
+
 def test_bf16_decode_is_exact():
     """bf16 bit patterns decode to their exact values: 0x3F80 = 1, 0xC000 = -2, 0x3EAB = 0.333984375."""
     bits = np.array([0x3F80, 0xC000, 0x3EAB, 0x0000, 0x8000], dtype=np.uint16)
