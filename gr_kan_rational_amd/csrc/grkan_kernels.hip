@@ -370,22 +370,25 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
 // Measured on MI355X with copy probes of this layout at KAT-B: 128-row
 // one-shot tiles with that mapping streamed 6.1 TB/s, the same tiles dealt
 // column block first 5.6 TB/s, lanes looping over 4-row batches 5.2 TB/s
-// (128-row tiles) to 4.5 TB/s (512-row tiles).  Tiles are 128 rows: with one
-// group per channel the partials are then ~2.6% of the backward's traffic,
-// written once and read once by the merge.
+// (128-row tiles) to 4.5 TB/s (512-row tiles).  The backward's tiles are 256
+// rows: with one group per channel the partials are then ~1.3% of its
+// traffic, written once and read once by the merge.
 
 constexpr int kNarrowCols = 64;
 constexpr int kNarrowRowLanes = 16;  // forward
 constexpr int kNarrowThreads = kNarrowCols * kNarrowRowLanes;
-// Backward: 4 row lanes, each walking 8 batches of 4 rows (128-row tiles).
-// The one-shot 128-row shape of the forward needs 1024-lane blocks, which
-// run one per CU at the backward's register count and stall the CU during
-// the workgroup reduction (measured 440-460 us against 397 us for this shape
-// with one function per channel at KAT-B).
+// Backward: 4 row lanes, each walking 8 batches of 8 rows (256-row tiles)
+// with the next batch's loads in flight.  The one-shot 128-row shape of the
+// forward needs 1024-lane blocks, which run one per CU at the backward's
+// register count and stall the CU during the workgroup reduction (440-460 us
+// with one function per channel at KAT-B).  Batches x rows per batch, with
+// the prefetch, at that workload (backward call, merge included): 8 x 4
+// 390 us, 4 x 8 383, 16 x 4 372, 8 x 8 361 (chosen), 16 x 8 369, 32 x 4 373,
+// 12 x 6 370, 12 x 8 377, 16 x 2 403; without the prefetch 8 x 4 took 396 us.
 constexpr int kNarrowBwdRowLanes = 4;
 constexpr int kNarrowBwdThreads = kNarrowCols * kNarrowBwdRowLanes;
 constexpr int kNarrowBwdIters = 8;
-template <int M, int N> constexpr int narrow_bwd_unroll() { return 4; }
+template <int M, int N> constexpr int narrow_bwd_unroll() { return 8; }
 // Forward rows per lane: 8 (128-row tiles); 4 for high degrees.
 template <int M, int N> constexpr int narrow_unroll() { return M + N <= 9 ? 8 : 4; }
 
@@ -455,42 +458,68 @@ __global__ __launch_bounds__(kNarrowThreads) void grkan_fwd_narrow_kernel(FwdArg
     else narrow_fwd_rows<IO, M, N, U, true>(sx, sy, w, c);
 }
 
-// One lane's rows of a narrow tile: dX stored, the terms added to acc.
-template <class IO, int M, int N, int U, bool CHECK>
-__device__ static inline void narrow_bwd_rows(Span sx, Span sdy, Span sdx, const Window &w, int it,
+// One lane's rows of a narrow tile, K batches of U rows: dX stored, the terms
+// added to acc.  The next batch's loads are issued before the current batch
+// is computed, so two batches (2 x U x 2 loads) are in flight per wave: a
+// lane moves only one channel per row, and the reads in flight, not the
+// arithmetic, decide this kernel's rate.
+template <class IO, int M, int N, int U, int K, bool CHECK>
+__device__ static inline void narrow_bwd_rows(Span sx, Span sdy, Span sdx, const Window &w,
                                               const BwdCoefs<M, N> &k, float (&acc)[Deg<M, N>::kNumCoef]) {
     using V = Elem<IO>;
     constexpr int KP = Deg<M, N>::kTop;
-    const uint32_t lane = w.lane + (uint32_t)(it * U) * w.stride;
     float xf[U], dyf[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        xf[u] = V::template load<CHECK>(sx, lane + u * w.stride);
-        dyf[u] = V::template load<CHECK>(sdy, lane + u * w.stride);
+        xf[u] = V::template load<CHECK>(sx, w.lane + u * w.stride);
+        dyf[u] = V::template load<CHECK>(sdy, w.lane + u * w.stride);
         // keeps the two variants' arithmetic from being hoisted above the
         // branch between them (see bwd_tile)
         if constexpr (CHECK) asm volatile("" : "+v"(xf[u]), "+v"(dyf[u]));
     }
-    float dxf[U];
-    bool sure = true;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const Pow<KP> X(xf[u]);
-        const ElemBwd eb = backward_element<M, N, KP>(X, dyf[u], k);
-        accumulate<M, N>(eb.w, eb.sv, X, acc);
-        dxf[u] = eb.dx;
-        sure = sure && eb.sure;
-    }
-    if constexpr (N > 0) {
-        // Rare: an element whose sign of Q the fp32 guard did not prove
-        // (x == 0, a root of Q, or b = 0 in its group): fix this lane's rows.
-        if (__builtin_expect(!sure, 0)) {
+    for (int it = 0; it < K; ++it) {
+        const uint32_t lane = w.lane + (uint32_t)(it * U) * w.stride;
+        float xn[U], dyn[U];
+        if (it + 1 < K) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) dxf[u] = exact_fix<M, N>(xf[u], dyf[u], k, acc);
+            for (int u = 0; u < U; ++u) {
+                xn[u] = V::template load<CHECK>(sx, lane + (U + u) * w.stride);
+                dyn[u] = V::template load<CHECK>(sdy, lane + (U + u) * w.stride);
+                if constexpr (CHECK) asm volatile("" : "+v"(xn[u]), "+v"(dyn[u]));
+            }
         }
-    }
+        float dxf[U];
+        bool sure = true;
 #pragma unroll
-    for (int u = 0; u < U; ++u) V::template store<CHECK>(sdx, lane + u * w.stride, dxf[u]);
+        for (int u = 0; u < U; ++u) {
+            const Pow<KP> X(xf[u]);
+            const ElemBwd eb = backward_element<M, N, KP>(X, dyf[u], k);
+            accumulate<M, N>(eb.w, eb.sv, X, acc);
+            dxf[u] = eb.dx;
+            sure = sure && eb.sure;
+        }
+        if constexpr (N > 0) {
+            // Rare: an element whose sign of Q the fp32 guard did not prove
+            // (x == 0, a root of Q, or b = 0 in its group): fix this lane's rows.
+            if (__builtin_expect(!sure, 0)) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) dxf[u] = exact_fix<M, N>(xf[u], dyf[u], k, acc);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) V::template store<CHECK>(sdx, lane + u * w.stride, dxf[u]);
+        if (it + 1 < K) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                xf[u] = xn[u];
+                dyf[u] = dyn[u];
+            }
+        }
+        // one batch ahead, no further: the scheduler would otherwise pull
+        // later batches' loads up and hold them all in registers
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 template <class IO, int M, int N>
@@ -513,10 +542,8 @@ __global__ __launch_bounds__(kNarrowBwdThreads) void grkan_bwd_narrow_kernel(Bwd
     float acc[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) acc[i] = 0.0f;
-    for (int it = 0; it < K; ++it) {
-        if (w.full) narrow_bwd_rows<IO, M, N, U, false>(sx, sdy, sdx, w, it, k, acc);
-        else narrow_bwd_rows<IO, M, N, U, true>(sx, sdy, sdx, w, it, k, acc);
-    }
+    if (w.full) narrow_bwd_rows<IO, M, N, U, K, false>(sx, sdy, sdx, w, k, acc);
+    else narrow_bwd_rows<IO, M, N, U, K, true>(sx, sdy, sdx, w, k, acc);
 
     // Workgroup sums in a fixed order: per channel over the row lanes, then
     // per group over its channels in this column block, in fp64.

@@ -27,9 +27,11 @@ constexpr int kMergeThreads = 1024;
 constexpr int kMergeLoads = 8;
 constexpr uint32_t kMergeChunk = (uint32_t)kMergeThreads * kMergeLoads;
 // Coefficients with at most this many slots (many groups, few tiles: one
-// function per channel) are merged by 256-thread workgroups.
-constexpr int kSmallThreads = 256;
-constexpr uint32_t kSmallChunk = (uint32_t)kSmallThreads * kMergeLoads;
+// function per channel) are merged one wave each: lane l adds slots l,
+// l + 64, ... in order, then the wave adds its lanes in a fixed tree.
+constexpr int kWaveLoads = 32;
+constexpr uint32_t kSmallChunk = 64u * kWaveLoads;
+constexpr int kWaveMergeThreads = 256;
 
 __device__ static inline void write_sum(int gk, int32_t na, int32_t nb, double total, float *dA,
                                         float *dB) {
@@ -61,24 +63,37 @@ __device__ static inline uint32_t parts_of(int g, uint32_t parts, int32_t dg, in
     return (uint32_t)(last - first + 1);
 }
 
+// Slot geometry of a launch: tile t of a part sits at slot (t mod 8) * bundles
+// + t / 8; the divisions by the part length and by bundles are multiply-highs
+// by host-computed constants (a vector integer division costs tens of
+// instructions, and the merge does two per slot).
+struct SlotMap {
+    uint32_t tiles, bundles, per_part;
+    FastDiv div_part, div_bundles;
+};
+
+// Whether slot q (below 2^31) holds a tile's partial.
+__device__ static inline bool slot_holds_tile(uint32_t q, const SlotMap &sm) {
+    const uint32_t r = q - fastdiv(q, sm.div_part) * sm.per_part;
+    const uint32_t a = fastdiv(r, sm.div_bundles);
+    return (r - a * sm.bundles) * 8u + a < sm.tiles;
+}
+
 template <int T>
 __global__ __launch_bounds__(T) void grkan_merge_kernel(
-    const float *__restrict__ partials, uint32_t tiles, uint32_t bundles, uint32_t slots,
+    const float *__restrict__ partials, SlotMap sm, uint32_t slots,
     int32_t na, int32_t nb, int32_t dg, int32_t cpb, uint32_t chunks, double *__restrict__ chunk_sums,
     float *__restrict__ dA, float *__restrict__ dB) {
     constexpr uint32_t chunk = (uint32_t)T * kMergeLoads;
     const int gk = (int)blockIdx.x;
     const uint32_t c = blockIdx.y;
-    const uint32_t per_part = 8u * bundles;
-    const uint32_t valid = parts_of(gk / (na + nb), slots / per_part, dg, cpb) * per_part;
+    const uint32_t valid = parts_of(gk / (na + nb), slots / sm.per_part, dg, cpb) * sm.per_part;
     const float *p = partials + (int64_t)gk * slots;
     float v[kMergeLoads];
 #pragma unroll
     for (int i = 0; i < kMergeLoads; ++i) {
         const uint32_t q = c * chunk + (uint32_t)i * T + threadIdx.x;
-        const uint32_t r = q % per_part;
-        const uint32_t tile = (r % bundles) * 8u + r / bundles;
-        v[i] = (q < valid && tile < tiles) ? p[q] : 0.0f;
+        v[i] = (q < valid && slot_holds_tile(q, sm)) ? p[q] : 0.0f;
     }
     double s = 0.0;
 #pragma unroll
@@ -88,6 +103,29 @@ __global__ __launch_bounds__(T) void grkan_merge_kernel(
         if (chunks == 1) write_sum(gk, na, nb, total, dA, dB);
         else chunk_sums[(int64_t)gk * chunks + c] = total;
     }
+}
+
+template <int L>
+__global__ __launch_bounds__(kWaveMergeThreads) void grkan_merge_wave_kernel(
+    const float *__restrict__ partials, SlotMap sm, uint32_t slots, int32_t na,
+    int32_t nb, int32_t dg, int32_t cpb, uint32_t n_gk, float *__restrict__ dA, float *__restrict__ dB) {
+    const uint32_t gk = blockIdx.x * (kWaveMergeThreads / 64) + (threadIdx.x >> 6);
+    if (gk >= n_gk) return;  // whole waves: the shuffles below see only active waves
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t valid = parts_of((int)gk / (na + nb), slots / sm.per_part, dg, cpb) * sm.per_part;
+    const float *p = partials + (int64_t)gk * slots;
+    float v[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const uint32_t q = (uint32_t)i * 64u + lane;
+        v[i] = (q < valid && slot_holds_tile(q, sm)) ? p[q] : 0.0f;
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < L; ++i) s += (double)v[i];
+#pragma unroll
+    for (int mask = 32; mask >= 1; mask >>= 1) s += __shfl_xor(s, mask, 64);
+    if (lane == 0) write_sum((int)gk, na, nb, s, dA, dB);
 }
 
 constexpr int kChunkThreads = 256;
@@ -121,17 +159,31 @@ hipError_t launch_merge(const float *partials, double *chunk_sums, int32_t n_gro
                         int32_t narrow_cpb, float *dA, float *dB, hipStream_t s) {
     const int32_t na = m + 1, nc = m + 1 + n;
     const int64_t slots = (int64_t)parts * 8 * bundles;
+    SlotMap sm;
+    sm.tiles = (uint32_t)tiles;
+    sm.bundles = (uint32_t)bundles;
+    sm.per_part = 8u * (uint32_t)bundles;
+    sm.div_part = make_fastdiv(sm.per_part);
+    sm.div_bundles = make_fastdiv(sm.bundles);
     const dim3 grid_gk((unsigned)(n_groups * nc));
     if (slots <= (int64_t)kSmallChunk) {
-        hipLaunchKernelGGL(grkan_merge_kernel<kSmallThreads>, grid_gk, dim3(kSmallThreads), 0, s, partials,
-                           (uint32_t)tiles, (uint32_t)bundles, (uint32_t)slots, na, n, narrow_dg, narrow_cpb,
-                           1u, chunk_sums, dA, dB);
+        const uint32_t n_gk = (uint32_t)(n_groups * nc);
+        const dim3 grid((n_gk + kWaveMergeThreads / 64 - 1) / (kWaveMergeThreads / 64));
+        const uint32_t sl = (uint32_t)slots;
+        if (slots <= 64 * 8)
+            hipLaunchKernelGGL(grkan_merge_wave_kernel<8>, grid, dim3(kWaveMergeThreads), 0, s, partials,
+                               sm, sl, na, n, narrow_dg, narrow_cpb, n_gk, dA, dB);
+        else if (slots <= 64 * 16)
+            hipLaunchKernelGGL(grkan_merge_wave_kernel<16>, grid, dim3(kWaveMergeThreads), 0, s, partials,
+                               sm, sl, na, n, narrow_dg, narrow_cpb, n_gk, dA, dB);
+        else
+            hipLaunchKernelGGL(grkan_merge_wave_kernel<kWaveLoads>, grid, dim3(kWaveMergeThreads), 0, s, partials,
+                               sm, sl, na, n, narrow_dg, narrow_cpb, n_gk, dA, dB);
         return hipGetLastError();
     }
     const uint32_t chunks = merge_chunks(slots);
     hipLaunchKernelGGL(grkan_merge_kernel<kMergeThreads>, dim3(grid_gk.x, chunks), dim3(kMergeThreads), 0, s,
-                       partials, (uint32_t)tiles, (uint32_t)bundles, (uint32_t)slots, na, n, narrow_dg,
-                       narrow_cpb, chunks, chunk_sums, dA, dB);
+                       partials, sm, (uint32_t)slots, na, n, narrow_dg, narrow_cpb, chunks, chunk_sums, dA, dB);
     if (chunks == 1) return hipGetLastError();
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -74,11 +74,11 @@ def test_workspace_size(lib):
     assert ws(lib, 201728, 768, 8, flags=BLOCK) == 0        # atomic modes need none
     assert ws(lib, 201728, 768, 8, flags=NAIVE) == 0
     assert ws(lib, 100, 770, 8) == 0                        # d % n_g != 0: rejected
-    # 5-channel groups (20 bytes, not whole 16-byte vectors): one channel per lane, 128-row tiles,
+    # 5-channel groups (20 bytes, not whole 16-byte vectors): one channel per lane, 256-row tiles,
     # 64 channels per column block; a group spans at most 2 blocks
     assert ws(lib, 100, 40, 8) == 8 * 10 * 2 * 8 * 4
-    # one function per channel at KAT-B: 1576 tiles of 128 rows -> 197 bundles -> 1576 slots
-    assert ws(lib, 201728, 768, 768) == 768 * 10 * 1576 * 4
+    # one function per channel at KAT-B: 788 tiles of 256 rows -> 99 bundles -> 792 slots
+    assert ws(lib, 201728, 768, 768) == 768 * 10 * 792 * 4
     assert ws(lib, 0, 768, 8) == 0                          # no rows, no tiles
 
 

@@ -96,8 +96,9 @@ def test_pau_parity(gk, m, n, io, geom):
 
 # Narrow groups (row segments that are not whole 16-byte vectors): one PAU per channel, 5-channel
 # groups, 3-channel groups, 125-channel groups spanning up to 3 column blocks of 64 channels,
-# and an odd channel count (bf16 rows that are not whole 4-byte words).
-NARROW = [(301, 768, 768), (203, 40, 8), (129, 300, 100), (97, 1000, 8), (67, 99, 33)]
+# an odd channel count (bf16 rows that are not whole 4-byte words), and 5-channel groups over
+# several whole 256-row backward tiles and a ragged tail.
+NARROW = [(301, 768, 768), (203, 40, 8), (129, 300, 100), (97, 1000, 8), (67, 99, 33), (1100, 200, 40)]
 
 
 @pytest.mark.parametrize("m,n", [(5, 4), (3, 2), (7, 6), (5, 0), (2, 1)])
