@@ -239,14 +239,17 @@ __device__ static inline BwdCoefs<M, N> derive(const Coefs<M, N> &c) {
     for (int i = 1; i <= M; ++i) k.da[i - 1] = (float)i * c.a[i];
     if constexpr (M == 0) k.da[0] = 0.0f;
     float bsum = 0.0f;
-    bool zero = true;
+    // b == 0 (either sign of zero) tested on the bits, so that the uniform
+    // test runs on the scalar unit (gfx950 has no scalar float compare)
+    uint32_t nonzero = 0u;
 #pragma unroll
     for (int j = 0; j < N; ++j) {
         k.b[j] = c.b[j];
         k.db[j] = (float)(j + 1) * c.b[j];
         bsum += fabsf(c.b[j]);
-        zero = zero && (c.b[j] == 0.0f);
+        nonzero |= __float_as_uint(c.b[j]) << 1;
     }
+    const bool zero = nonzero == 0u;
     if constexpr (N == 0) {
         k.b[0] = 0.0f;
         k.db[0] = 0.0f;
