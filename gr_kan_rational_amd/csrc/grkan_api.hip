@@ -267,7 +267,7 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
                              float *dA, float *dB, int64_t rows, int64_t d, int32_t n_groups,
                              int32_t m, int32_t n, grkan_dtype_t io, uint32_t flags,
                              void *workspace, size_t workspace_bytes, hipStream_t stream,
-                             int32_t repeat = 1) {
+                             int32_t repeat = 1, void *y = nullptr) {
     if (flags & ~(uint32_t)(GRKAN_BLOCK_ATOMIC | GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
     if ((flags & GRKAN_BLOCK_ATOMIC) && (flags & GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
     const DegreeOps *deg = find_degree(m, n);
@@ -322,7 +322,7 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
     float *partials = static_cast<float *>(workspace);
     for (int64_t b0 = 0; b0 < launch_units(P); b0 += units_per_launch(P)) {
         const int64_t nz = (launch_units(P) - b0 < units_per_launch(P)) ? launch_units(P) - b0 : units_per_launch(P);
-        BwdArgs a{x, dy, dx, A, B, dA, dB, partials, det ? kModePartials : kModeAtomic, P, b0};
+        BwdArgs a{x, dy, dx, A, B, dA, dB, partials, det ? kModePartials : kModeAtomic, P, b0, y};
         st = from_hip(deg->backward(io, a, repeat, grid_of(P, nz), stream));
         if (st != GRKAN_OK) return st;
     }
@@ -486,9 +486,10 @@ extern "C" grkan_status_t grkan_linear_forward(const void *y, const void *W, voi
     return from_hip(launch_linear_forward(y, W, z, rows, d_in, d_out, stream));
 }
 
-// Layer backward workspace: W^T, one bf16 [rows][d_in] buffer (Y = F(x),
-// then dY), the activation backward's partials, the weight gradient's split
-// partials; each 256-byte aligned.
+// Layer backward workspace: W^T, one bf16 [rows][d_in] buffer (dY, then
+// Y = F(x) written over it by the activation backward), the activation
+// backward's partials, the weight gradient's split partials; each 256-byte
+// aligned.
 namespace {
 
 struct LayerBwdPlan {
@@ -573,19 +574,19 @@ extern "C" grkan_status_t grkan_layer_backward(const void *x, const void *dz, co
     }
     char *ws = static_cast<char *>(workspace);
     void *wt = ws + lp.off_wt, *buf = ws + lp.off_buf;
-    // Y = F(x) (bf16), then dW = dz^T Y
-    st = forward_impl(x, buf, A, B, rows, d_in, n_groups, kGrkanM, kGrkanN, GRKAN_BF16, stream);
-    if (st != GRKAN_OK) return st;
-    st = from_hip(launch_wgrad(dz, buf, reinterpret_cast<float *>(ws + lp.off_wg), dW, rows, d_out, d_in, stream));
-    if (st != GRKAN_OK) return st;
-    // dY = dz W (bf16, over W^T so that both operands are K-contiguous), into the same buffer
+    // dY = dz W (bf16, over W^T so that both operands are K-contiguous)
     st = from_hip(launch_transpose16(W, wt, d_out, d_in, stream));
     if (st != GRKAN_OK) return st;
     st = from_hip(launch_linear_forward(dz, wt, buf, rows, d_out, d_in, stream));
     if (st != GRKAN_OK) return st;
-    // dx, dA, dB: the activation's backward on (x, dY), deterministic scheme
-    return backward_impl(x, buf, A, B, dx, dA, dB, rows, d_in, n_groups, kGrkanM, kGrkanN, GRKAN_BF16, 0,
-                         ws + lp.off_act, workspace_need(lp.act), stream);
+    // dx, dA, dB: the activation's backward on (x, dY), deterministic scheme; it
+    // also stores Y = F(x) (bf16) over dY, from the P and 1/D it forms anyway,
+    // so that x is read once.  dx may be x: nothing after this reads x.
+    st = backward_impl(x, buf, A, B, dx, dA, dB, rows, d_in, n_groups, kGrkanM, kGrkanN, GRKAN_BF16, 0,
+                       ws + lp.off_act, workspace_need(lp.act), stream, 1, buf);
+    if (st != GRKAN_OK) return st;
+    // dW = dz^T Y
+    return from_hip(launch_wgrad(dz, buf, reinterpret_cast<float *>(ws + lp.off_wg), dW, rows, d_out, d_in, stream));
 }
 
 // ------------------------------------------------------- Chebyshev KAN

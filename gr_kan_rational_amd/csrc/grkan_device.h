@@ -300,6 +300,7 @@ struct ElemBwd {
     float sv;   // s v             (dB terms: -sv x^j)
     float Qd;   // Q'
     float wPd;  // w P'
+    float F;    // P / D, the forward value
     bool sure;
 };
 
@@ -321,6 +322,7 @@ __device__ static inline ElemBwd backward_element(const Pow<K> &X, float dy, con
         e.Qd = 0.0f;
         e.wPd = dy * Pd;
         e.dx = e.wPd;
+        e.F = P;
         e.sure = true;
     } else {
         float q = k.b[0];
@@ -332,7 +334,8 @@ __device__ static inline ElemBwd backward_element(const Pow<K> &X, float dy, con
         const float Q = x * q;
         const float r = __builtin_amdgcn_rcpf(1.0f + fabsf(Q));
         e.w = dy * r;
-        e.v = e.w * (P * r);
+        e.F = P * r;
+        e.v = e.w * e.F;
         e.sv = __uint_as_float(__float_as_uint(e.v) ^ (__float_as_uint(Q) & 0x80000000u));
         e.sure = fabsf(Q) > k.kguard * (fabsf(x) + fabsf(X.p[N]));
         e.Qd = Qd;

@@ -43,6 +43,8 @@
 //     pages' Algorithm 2) or as one partial per coefficient merged afterwards
 //     in fp64 in a fixed order (the two-stage reduction of [PolyKAN]), which
 //     is bitwise reproducible: the tiling depends only on the shape.
+#include <type_traits>
+
 #include "grkan_device.h"
 #include "grkan_launch.h"
 
@@ -215,9 +217,12 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_fwd_kernel(FwdArgs a) {
 // One tile's elements: dX stored, this lane's gradient sums in acc.  The rare
 // exact-sign fix runs once per tile, before any dX is stored; it re-reads x
 // and dy, which is safe even when dx aliases x or dy.
-template <class IO, int M, int N, int U, bool QZERO, bool CHECK, int R = 1>
+// With WY, F(x) is stored too, through ry (which may be rdy: every load
+// precedes every store).
+template <class IO, int M, int N, int U, bool QZERO, bool CHECK, int R = 1, bool WY = false>
 __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window &w,
-                                       const BwdCoefs<M, N> &k, float (&acc)[Deg<M, N>::kNumCoef]) {
+                                       const BwdCoefs<M, N> &k, float (&acc)[Deg<M, N>::kNumCoef],
+                                       Span ry = Span{}) {
     using V = Io<IO>;
     constexpr int E = V::kElems;
     constexpr int K = Deg<M, N>::kTop;
@@ -229,6 +234,7 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
         din[u] = win_load16<CHECK>(rdy, w.lane + u * w.stride);
     }
     float dxf[U][E];
+    [[maybe_unused]] u32x4 ypk[WY ? U : 1];  // F, packed to the I/O type as each pass ends
     bool sure = true;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -238,6 +244,7 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
         // which costs ~30 registers.
         if constexpr (QZERO && N > 0) asm volatile("" : "+v"(xin[u]), "+v"(din[u]));
         float xf[E], dyf[E];
+        [[maybe_unused]] float yf[E];
         V::unpack(xin[u], xf);
         V::unpack(din[u], dyf);
 #pragma unroll
@@ -252,13 +259,21 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
                 for (int i = 2; i <= M; ++i) Pd = fmaf(k.da[i - 1], X.p[i - 1], Pd);
                 dxf[u][e] = dy * Pd;
                 accumulate<M, N>(dy, 0.0f, X, acc);
+                if constexpr (WY) {
+                    float P = k.a[0];
+#pragma unroll
+                    for (int i = 1; i <= M; ++i) P = fmaf(k.a[i], X.p[i], P);
+                    yf[e] = P;
+                }
             } else {
                 const ElemBwd eb = backward_element<M, N, K>(X, dy, k);
                 accumulate<M, N>(eb.w, eb.sv, X, acc);
                 dxf[u][e] = eb.dx;
+                if constexpr (WY) yf[e] = eb.F;
                 sure = sure && eb.sure;
             }
         }
+        if constexpr (WY) ypk[u] = V::pack(yf);
     }
     if constexpr (!QZERO) {
         // Rare: some element's sign of Q was not proven by the fp32 guard.
@@ -277,6 +292,10 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) win_store16<CHECK>(rdx, w.lane + u * w.stride, V::pack(dxf[u]));
+    if constexpr (WY) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) win_store16<CHECK>(ry, w.lane + u * w.stride, ypk[u]);
+    }
 }
 
 // Slot of a tile's partial within its part: tiles of one XCD side by side.
@@ -284,8 +303,9 @@ __device__ static inline int64_t slot_in_part(const Plan &P, int64_t tile) {
     return (tile & 7) * P.bundles + (tile >> 3);
 }
 
-// R = 1: the plain backward; R = 2, 4, 8: the FLOP-inflation probe.
-template <class IO, int M, int N, int U, int R>
+// R = 1: the plain backward; R = 2, 4, 8: the FLOP-inflation probe.  WY: F(x)
+// is stored too (a.y), for the layer backward.
+template <class IO, int M, int N, int U, int R, bool WY = false>
 __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
     constexpr int NC = Deg<M, N>::kNumCoef;
     const Plan &P = a.plan;
@@ -301,10 +321,11 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
     for (int i = 0; i < NC; ++i) acc[i] = 0.0f;
     // (A second, unchecked copy of the tile for full tiles spilled: the
     // per-access checks cost < 1 VALU operation per element here.)
+    const Span ry = WY ? make_span(at(a.y, w.base), w.avail) : Span{};
     if (k.q_zero) {
-        bwd_tile<IO, M, N, U, true, true, R>(rx, rdy, rdx, w, k, acc);
+        bwd_tile<IO, M, N, U, true, true, R, WY>(rx, rdy, rdx, w, k, acc, ry);
     } else {
-        if constexpr (N > 0) bwd_tile<IO, M, N, U, false, true, R>(rx, rdy, rdx, w, k, acc);
+        if constexpr (N > 0) bwd_tile<IO, M, N, U, false, true, R, WY>(rx, rdy, rdx, w, k, acc, ry);
     }
 
     // Workgroup sum of the NC terms, in a fixed order: transposed through LDS
@@ -618,8 +639,9 @@ size_t bwd_lds_bytes(int block) {
 
 template <class IO, int M, int N>
 hipError_t bwd_impl(const BwdArgs &a, int repeat, dim3 grid, hipStream_t s) {
+    if (a.y && repeat != 1) return hipErrorInvalidValue;
     if (a.plan.kind == kNarrow) {
-        if (repeat != 1) return hipErrorInvalidValue;
+        if (repeat != 1 || a.y) return hipErrorInvalidValue;
         hipLaunchKernelGGL((grkan_bwd_narrow_kernel<IO, M, N>), grid,
                            dim3(kNarrowCols, kNarrowBwdRowLanes), 0, s, a);
         return hipGetLastError();
@@ -635,6 +657,14 @@ hipError_t bwd_impl(const BwdArgs &a, int repeat, dim3 grid, hipStream_t s) {
             case 8: hipLaunchKernelGGL((grkan_bwd_kernel<IO, M, N, U, 8>), grid, block, lds, s, a); break;
             default: return hipErrorInvalidValue;
             }
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    if (a.y) {
+        // F(x) as a second output: the GR-KAN bf16 layer backward only
+        if constexpr (std::is_same<IO, bf16io>::value && M == 5 && N == 4) {
+            hipLaunchKernelGGL((grkan_bwd_kernel<IO, M, N, U, 1, true>), grid, block, lds, s, a);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;

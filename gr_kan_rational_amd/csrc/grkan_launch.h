@@ -98,6 +98,10 @@ struct BwdArgs {
     int32_t mode;
     Plan plan;
     int64_t bundle0;
+    // Optional second output of the GR-KAN bf16 segment backward: F(x) in the
+    // I/O type (the layer backward's operand of the weight gradient; may be
+    // dy itself, each element being read before it is overwritten).
+    void *y = nullptr;
 };
 
 // Kernels of one degree pair, defined in grkan_kernels.hip (compiled once per

@@ -256,9 +256,14 @@ GRKAN_API grkan_status_t grkan_linear_forward(const void *y, const void *W, void
  *   dx, dA, dB                 the activation's backward on (x, dy), as
  *                              grkan_backward computes them (bf16 dx,
  *                              deterministic two-stage sums for dA, dB)
- * all on the matrix cores except the activation's own kernels.  dW sums over
- * all rows: fixed-size row splits are summed in fp32 on the matrix cores and
- * the splits in a fixed order in fp64, so the result is bitwise reproducible.
+ * all on the matrix cores except the activation's own kernels.  bf16(F(x))
+ * for dW comes out of the activation's backward kernel, which evaluates F in
+ * fp32 from the powers of x it forms anyway (grkan_layer_forward uses Horner's
+ * rule): both are correctly rounded fp32 evaluations, so where F lies within
+ * fp32 rounding of a bf16 midpoint the two bf16 values may differ by one step.
+ * dW sums over all rows: fixed-size row splits are summed in fp32 on the
+ * matrix cores and the splits in a fixed order in fp64, so the result is
+ * bitwise reproducible.
  *   dx may be x itself; every other output must overlap nothing.
  *   workspace: grkan_layer_backward_workspace_size() bytes, 256-byte aligned.
  *   Limits as grkan_layer_forward, and d_out a multiple of 64.
