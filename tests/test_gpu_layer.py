@@ -197,6 +197,29 @@ def test_layer_backward_parity(gk, shape):
         assert torch.equal(a.view(it), b.view(it)) and torch.equal(a.view(it), c.view(it))
 
 
+def test_layer_backward_zero_denominator_groups(gk):
+    """Groups with b = 0 (KAT initialises its first GR-KAN layer to the identity, a = (0, 1, 0, ...)
+    and b = 0) take the activation backward's D = 1 branch, which also forms the dW operand
+    F(x) = P(x) there; the other groups are random.  Both tile variants in one call, against the
+    oracle; the identity groups' dB is exactly zero."""
+    rows, d_in, n_g, d_out = 700, 512, 8, 256
+    log(f"[layer_bwd_b0] rows={rows} d_in={d_in} n_g={n_g} d_out={d_out}")
+    inp = backward_inputs(rows, d_in, n_g, d_out, 7300)
+    A0, B0 = inp["A"].copy(), inp["B"].copy()
+    A0[0] = [0, 1, 0, 0, 0, 0]
+    B0[0] = 0
+    B0[1] = 0
+    B0[5] = -0.0
+    x, dz, W = bf(inp["x"]), bf(inp["dz"]), bf(inp["W"])
+    A, B = torch.from_numpy(A0).to(DEV), torch.from_numpy(B0).to(DEV)
+    got = gk.grkan_layer_backward(x, dz, A, B, W, n_g)
+    torch.cuda.synchronize()
+    ref = layer.backward(inp["x"], inp["dz"], A0, B0, inp["W"], n_g)
+    check_backward("layer bwd b = 0 groups", got, ref)
+    dB = got[2].cpu().numpy()
+    assert np.all(dB[[0, 1, 5]] == 0)
+
+
 def test_layer_backward_empty(gk):
     inp = backward_inputs(4, 64, 8, 64, 7100)
     A, B = torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV)
