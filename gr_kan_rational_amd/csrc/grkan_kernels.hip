@@ -59,19 +59,20 @@ namespace {
 constexpr int kMaxBlock = 1024;
 
 // Tuning, chosen by measurement on MI355X at the KAT-B shapes.  U = passes
-// per workgroup (all of a lane's loads are issued together).  The backward
-// prefers small blocks (with ~90 VGPRs a SIMD holds 5 of its waves; 3-wave
-// blocks fill those slots in finer steps than 6-wave ones) and 4 passes to
-// amortise the block reduction; the bf16 backward, which is bound by its
-// arithmetic rather than by memory, and high-degree fp32 backwards, which
-// need more registers per element, use 2 passes.
+// per workgroup (all of a lane's loads are issued together).  Forward: 2
+// passes, 384-lane blocks.  The fp32 backward at GR-KAN-sized degrees: 2
+// passes, 384-lane blocks (292 us; 4 passes of 192 lanes -- the same 32-row
+// tiles -- 302 us, 2 x 192 303, 2 x 768 293, 3 x 384 295, 1 x 384 327).  The
+// bf16 backward, which is bound by its arithmetic rather than by memory, and
+// high-degree fp32 backwards, which need more registers per element: 2 passes,
+// 192-lane blocks.
 template <class IO> constexpr bool is_f32() { return __is_same(IO, float); }
 template <class IO, int M, int N> constexpr int fwd_unroll() { return 2; }
-template <class IO, int M, int N> constexpr int bwd_unroll() {
-    return (is_f32<IO>() && M + N <= 9) ? 4 : 2;
-}
+template <class IO, int M, int N> constexpr int bwd_unroll() { return 2; }
+template <class IO, int M, int N> constexpr bool bwd_wide_block() { return is_f32<IO>() && M + N <= 9; }
 constexpr int kFwdBlock = 384;
 constexpr int kBwdBlock = 192;
+constexpr int kBwdWideBlock = 384;
 // One fp32 atomic per coefficient per workgroup serialises on the few cache
 // lines of dA and dB in L2, so the atomic mode uses 4x larger workgroups.
 constexpr int kAtomicModeBlock = 768;
@@ -689,9 +690,11 @@ void Kernels<M, N>::narrow_shape(grkan_dtype_t, int pass, int *row_lanes, int *u
 }
 
 template <int M, int N>
-int Kernels<M, N>::target_block(grkan_dtype_t, int pass, bool atomic_mode) {
+int Kernels<M, N>::target_block(grkan_dtype_t io, int pass, bool atomic_mode) {
     if (pass == 1 && atomic_mode) return kAtomicModeBlock;
-    return pass ? kBwdBlock : kFwdBlock;
+    if (pass == 0) return kFwdBlock;
+    const bool wide = io == GRKAN_BF16 ? bwd_wide_block<bf16io, M, N>() : bwd_wide_block<float, M, N>();
+    return wide ? kBwdWideBlock : kBwdBlock;
 }
 
 template <int M, int N>

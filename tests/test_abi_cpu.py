@@ -62,8 +62,8 @@ def ws(lib, rows, d, n_g, io=F32, flags=DEFAULT):
 
 
 def test_workspace_size(lib):
-    # KAT-B backward: 96 channels x 4 B = 24 vectors per group row; 8 rows x 24 = 192 lanes per
-    # pass, 4 passes -> 32-row tiles; ceil(201728 / 32) = 6304 tiles; one fp32 partial per
+    # KAT-B backward: 96 channels x 4 B = 24 vectors per group row; 16 rows x 24 = 384 lanes per
+    # pass, 2 passes -> 32-row tiles; ceil(201728 / 32) = 6304 tiles; one fp32 partial per
     # (group, coefficient, tile), slots rounded up to a multiple of 8 tiles.  Above 8192 slots
     # the merge adds them in chunks and needs one fp64 chunk sum per (group, coefficient, chunk).
     assert ws(lib, 201728, 768, 8) == 8 * 10 * 6304 * 4
@@ -158,15 +158,15 @@ def pws(lib, rows, d, n_g, m, n, io=F32, flags=DEFAULT):
 def test_pau_workspace_size(lib):
     # One fp32 partial per (group, coefficient, part, tile); m + 1 + n coefficients.
     assert pws(lib, 201728, 768, 8, 5, 4) == ws(lib, 201728, 768, 8)
-    assert pws(lib, 201728, 768, 8, 3, 2) == 8 * 6 * 6304 * 4     # 4 passes of 8 rows: 32-row tiles
+    assert pws(lib, 201728, 768, 8, 3, 2) == 8 * 6 * 6304 * 4     # 2 passes of 16 rows: 32-row tiles
     assert pws(lib, 201728, 768, 8, 7, 6) == 8 * 14 * 12608 * 4 + 8 * 14 * 2 * 8  # 16-row tiles
     assert pws(lib, 201728, 768, 8, 5, 0) == 8 * 6 * 6304 * 4     # polynomial: no dB sums
-    # n_groups = 1 (one PAU for all channels): a 192-vector segment, one row per pass, 4-row tiles
+    # n_groups = 1 (one PAU for all channels): a 192-vector segment, two rows per pass, 4-row tiles
     assert pws(lib, 201728, 768, 1, 5, 4) == 1 * 10 * 50432 * 4 + 1 * 10 * 7 * 8
-    # a 768-vector segment is cut into 4 parts of 192 vectors
+    # a 768-vector segment is cut into 2 parts of 384 vectors (one row per pass, 2-row tiles)
     assert pws(lib, 201728, 3072, 1, 5, 4) == 1 * 10 * 4 * 50432 * 4 + 1 * 10 * 25 * 8
-    # 1026 vectors per segment (16416 bytes): 6 parts of 171
-    assert pws(lib, 4, 8 * 4104, 8, 5, 4) == 8 * 10 * 6 * 8 * 4
+    # 1026 vectors per segment (16416 bytes): 3 parts of 342
+    assert pws(lib, 4, 8 * 4104, 8, 5, 4) == 8 * 10 * 3 * 8 * 4
     assert pws(lib, 100, 768, 8, 5, 3) == 0                        # pair not compiled in
     assert pws(lib, 100, 768, 8, 3, 2, flags=BLOCK) == 0
 

@@ -25,7 +25,7 @@ pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
 PAIRS = [(5, 4), (3, 2), (4, 3), (6, 5), (7, 6), (2, 1), (4, 4), (5, 0)]
 # (rows, d, n_groups): 32-channel groups; one group of 768 channels; two groups of 4000
-# channels (16000 / 8000 bytes per row segment: 6 or 3 ragged column parts)
+# channels (16000 / 8000 bytes per row segment: 3 to 6 ragged column parts)
 GEOMS = [(301, 256, 8), (203, 768, 1), (37, 8000, 2)]
 
 
