@@ -17,9 +17,11 @@ LIB_PATH = os.path.join(_HERE, "libgrkan.so")
 
 GRKAN_OK, GRKAN_ERR_INVALID_ARG, GRKAN_ERR_UNSUPPORTED, GRKAN_ERR_HIP = 0, 1, 2, 3
 GRKAN_F32, GRKAN_BF16 = 0, 1
-GRKAN_BLOCK_ATOMIC = 1 << 0
-GRKAN_NAIVE_ATOMIC = 1 << 1
-_MODES = {"deterministic": 0, "block_atomic": GRKAN_BLOCK_ATOMIC, "naive": GRKAN_NAIVE_ATOMIC}
+GRKAN_DETERMINISTIC = 1 << 0
+GRKAN_BLOCK_ATOMIC = 1 << 1
+GRKAN_NAIVE_ATOMIC = 1 << 2
+_MODES = {"deterministic": GRKAN_DETERMINISTIC, "block_atomic": GRKAN_BLOCK_ATOMIC,
+          "naive": GRKAN_NAIVE_ATOMIC}
 
 
 class GRKANError(RuntimeError):

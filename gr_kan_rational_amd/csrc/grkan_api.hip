@@ -253,9 +253,21 @@ grkan_status_t forward_impl(const void *x, void *y, const float *A, const float 
     return GRKAN_OK;
 }
 
+// The reduction scheme a flags word asks for: 0 deterministic, 1 per-block
+// atomics, 2 per-element atomics, -1 an invalid word (two schemes, or a bit
+// that names none).  flags = 0 is the deterministic default.
+constexpr uint32_t kSchemeBits = GRKAN_DETERMINISTIC | GRKAN_BLOCK_ATOMIC | GRKAN_NAIVE_ATOMIC;
+int scheme_of(uint32_t flags) {
+    if (flags & ~kSchemeBits) return -1;
+    if (flags & (flags - 1)) return -1;  // more than one bit
+    if (flags == GRKAN_BLOCK_ATOMIC) return 1;
+    if (flags == GRKAN_NAIVE_ATOMIC) return 2;
+    return 0;
+}
+
 size_t workspace_impl(int64_t rows, int64_t d, int32_t n_groups, int32_t m, int32_t n,
                       grkan_dtype_t io, uint32_t flags) {
-    if (flags != 0) return 0;
+    if (scheme_of(flags) != 0) return 0;
     const DegreeOps *deg = find_degree(m, n);
     if (!deg) return 0;
     Plan P;
@@ -268,16 +280,17 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
                              int32_t m, int32_t n, grkan_dtype_t io, uint32_t flags,
                              void *workspace, size_t workspace_bytes, hipStream_t stream,
                              int32_t repeat = 1, void *y = nullptr) {
-    if (flags & ~(uint32_t)(GRKAN_BLOCK_ATOMIC | GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
-    if ((flags & GRKAN_BLOCK_ATOMIC) && (flags & GRKAN_NAIVE_ATOMIC)) return GRKAN_ERR_INVALID_ARG;
+    const int scheme = scheme_of(flags);
+    if (scheme < 0) return GRKAN_ERR_INVALID_ARG;
+    const bool det = scheme == 0, naive = scheme == 2;
     const DegreeOps *deg = find_degree(m, n);
     if (!deg) return (m < 0 || n < 0) ? GRKAN_ERR_INVALID_ARG : GRKAN_ERR_UNSUPPORTED;
     if (!valid_repeat(repeat)) return GRKAN_ERR_INVALID_ARG;
-    if ((flags & GRKAN_NAIVE_ATOMIC) && (m != kGrkanM || n != kGrkanN)) return GRKAN_ERR_UNSUPPORTED;
+    if (naive && (m != kGrkanM || n != kGrkanN)) return GRKAN_ERR_UNSUPPORTED;
     Plan P;
-    grkan_status_t st = plan_shape(rows, d, n_groups, *deg, io, 1, flags != 0, &P);
+    grkan_status_t st = plan_shape(rows, d, n_groups, *deg, io, 1, !det, &P);
     if (st != GRKAN_OK) return st;
-    if (repeat != 1 && (P.kind == kNarrow || m != kGrkanM || n != kGrkanN || (flags & GRKAN_NAIVE_ATOMIC)))
+    if (repeat != 1 && (P.kind == kNarrow || m != kGrkanM || n != kGrkanN || naive))
         return GRKAN_ERR_UNSUPPORTED;
     if (!A || !dA || (n > 0 && (!B || !dB))) return GRKAN_ERR_INVALID_ARG;
     if (!aligned(A, 4) || !aligned(B, 4) || !aligned(dA, 4) || !aligned(dB, 4))
@@ -296,7 +309,6 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
     for (int i = 0; i < 5; ++i)
         if (overlap(dA, ab, others[i], sizes[i]) || overlap(dB, bb, others[i], sizes[i]))
             return GRKAN_ERR_INVALID_ARG;
-    const bool det = flags == 0;
     if (det && rows > 0) {
         const size_t need = workspace_need(P);
         if (!workspace || workspace_bytes < need) return GRKAN_ERR_INVALID_ARG;
@@ -310,7 +322,7 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
     // ---- validation done; HIP calls from here on
     const int64_t na = (int64_t)n_groups * (m + 1), nb = (int64_t)n_groups * n;
     if (rows == 0) return from_hip(launch_zero(dA, dB, na, nb, stream));
-    if (flags & GRKAN_NAIVE_ATOMIC) {
+    if (naive) {
         st = from_hip(launch_zero(dA, dB, na, nb, stream));
         if (st != GRKAN_OK) return st;
         return from_hip(launch_naive(io, x, dy, dx, A, B, dA, dB, rows, d, n_groups, stream));

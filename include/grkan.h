@@ -80,18 +80,24 @@ typedef enum {
 } grkan_dtype_t;
 
 enum {
-    /* Backward reduction schemes.  The default (flags = 0) writes one partial
-       sum per (row tile, group, coefficient) to `workspace` and merges them
-       with a second kernel in fp64 in a fixed order: bitwise reproducible for
-       a given shape and library build, on any device, and accurate to the
-       fp32 rounding of the individual terms.  The two flags below select the
-       schemes the pages compare ([FlashKAT notes], sections "2. 原始 KAT 的
-       atomic add 问题分析" and "3. FlashKAT 核函数重构（Algorithm 2）"); they
-       are kept for measurement and their fp32 accumulation error grows with
+    /* Backward reduction schemes (the `flags` argument).
+       GRKAN_DETERMINISTIC (or flags = 0, the same request): one partial sum
+       per (row tile, group, coefficient) goes to `workspace` and a second
+       kernel adds them in fp64 in a fixed order -- bitwise reproducible for a
+       given shape and library build, on any device, and accurate to the fp32
+       rounding of the individual terms; the two-stage reduction of [PolyKAN]
+       ("PolyKAN: Efficient Fused GPU Operators for Polynomial
+       Kolmogorov-Arnold Network Variants", abstract page, arXiv 2511.14852).
+       The two atomic flags select the schemes the pages compare ([FlashKAT
+       notes], sections "2. 原始 KAT 的 atomic add 问题分析" and "3. FlashKAT
+       核函数重构（Algorithm 2）"); they are kept for measurement, are not
+       reproducible run to run, and their fp32 accumulation error grows with
        the number of workgroups or elements, as the pages' rounding-error
-       table shows for their GPUs. */
-    GRKAN_BLOCK_ATOMIC = 1u << 0, /* one fp32 atomic add per coefficient per workgroup */
-    GRKAN_NAIVE_ATOMIC = 1u << 1  /* ten fp32 atomic adds per element (KAT's original) */
+       table shows for their GPUs.  At most one of the three bits may be
+       set; any other bit is GRKAN_ERR_INVALID_ARG. */
+    GRKAN_DETERMINISTIC = 1u << 0, /* fixed-order two-stage reduction (also flags = 0) */
+    GRKAN_BLOCK_ATOMIC = 1u << 1,  /* one fp32 atomic add per coefficient per workgroup */
+    GRKAN_NAIVE_ATOMIC = 1u << 2   /* ten fp32 atomic adds per element (KAT's original) */
 };
 
 /*
@@ -114,12 +120,13 @@ GRKAN_API grkan_status_t grkan_forward(const void *x, void *y, const float *A, c
  *   dA, dB    fp32 outputs [n_groups][6], [n_groups][4]; overwritten, not
  *             accumulated; must not overlap any other argument.  rows == 0
  *             writes zeros.
- *   flags     0 (two-stage deterministic reduction), GRKAN_BLOCK_ATOMIC or
- *             GRKAN_NAIVE_ATOMIC (both zero dA, dB first).  Other bits, or
- *             both, are INVALID_ARG.
+ *   flags     0 or GRKAN_DETERMINISTIC (two-stage fixed-order reduction),
+ *             GRKAN_BLOCK_ATOMIC or GRKAN_NAIVE_ATOMIC (both zero dA, dB
+ *             first).  Two of these bits together, or any other bit, are
+ *             INVALID_ARG.
  *   workspace device memory of at least grkan_backward_workspace_size()
- *             bytes, 16-byte aligned, for the default scheme; ignored (may
- *             be NULL) with an atomic flag.  Its contents on entry do not
+ *             bytes, 16-byte aligned, for the deterministic scheme; ignored
+ *             (may be NULL) with an atomic flag.  Its contents on entry do not
  *             matter.  Two calls in flight at once must not share one
  *             workspace.
  */
@@ -130,8 +137,11 @@ GRKAN_API grkan_status_t grkan_backward(const void *x, const void *dy, const flo
                               void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace grkan_backward needs for these arguments (0 when it
- * needs none, or for arguments grkan_backward would reject).  Host-only: it
- * makes no HIP call and works without a GPU. */
+ * needs none, or for arguments grkan_backward would reject).  It takes the
+ * I/O dtype because the row tiles depend on it: a workgroup covers a fixed
+ * number of 16-byte vectors, i.e. twice as many bf16 channels as fp32 ones,
+ * so the number of tiles -- one partial sum each -- differs between the two.
+ * Host-only: it makes no HIP call and works without a GPU. */
 GRKAN_API size_t grkan_backward_workspace_size(int64_t rows, int64_t d, int32_t n_groups,
                                      grkan_dtype_t io, uint32_t flags);
 

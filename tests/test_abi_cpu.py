@@ -13,7 +13,7 @@ LIB = os.path.join(ROOT, "gr_kan_rational_amd", "libgrkan.so")
 
 OK, INVALID, UNSUPPORTED, HIPERR = 0, 1, 2, 3
 F32, BF16 = 0, 1
-DEFAULT, BLOCK, NAIVE = 0, 1, 2
+DEFAULT, DET, BLOCK, NAIVE = 0, 1, 2, 4
 
 
 @pytest.fixture(scope="module")
@@ -49,6 +49,38 @@ def test_header_declares_the_abi():
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
+
+
+def header_enum(name):
+    m = re.search(rf"\b{name}\s*=\s*([^,/\n]+)", open(HEADER).read())
+    assert m, name
+    return int(eval(m.group(1).replace("1u", "1")))  # "1u << k" as Python
+
+
+def test_flag_values_are_pinned():
+    """The reduction-scheme bits: deterministic is bit 0 (and flags = 0 means the same), the
+    two atomic comparison schemes bits 1 and 2; the binding uses the same values."""
+    from gr_kan_rational_amd import binding
+
+    assert header_enum("GRKAN_DETERMINISTIC") == DET == binding.GRKAN_DETERMINISTIC == 1
+    assert header_enum("GRKAN_BLOCK_ATOMIC") == BLOCK == binding.GRKAN_BLOCK_ATOMIC == 2
+    assert header_enum("GRKAN_NAIVE_ATOMIC") == NAIVE == binding.GRKAN_NAIVE_ATOMIC == 4
+    assert header_enum("GRKAN_F32") == F32 and header_enum("GRKAN_BF16") == BF16
+    assert header_enum("GRKAN_OK") == OK and header_enum("GRKAN_ERR_INVALID_ARG") == INVALID
+    assert header_enum("GRKAN_ERR_UNSUPPORTED") == UNSUPPORTED and header_enum("GRKAN_ERR_HIP") == HIPERR
+    assert binding._MODES == {"deterministic": DET, "block_atomic": BLOCK, "naive": NAIVE}
+
+
+def test_deterministic_flag_is_the_default_scheme(lib):
+    """flags = GRKAN_DETERMINISTIC asks for exactly what flags = 0 asks for: the same workspace
+    and the same validation; combined with an atomic bit it is rejected."""
+    for args in ((201728, 768, 8, F32), (201728, 3072, 8, BF16), (100, 40, 8, F32), (16, 32, 8, F32)):
+        assert ws(lib, *args, flags=DET) == ws(lib, *args, flags=DEFAULT) > 0
+    for f in (DET | BLOCK, DET | NAIVE, BLOCK | NAIVE, DET | BLOCK | NAIVE, 8, 1 << 31):
+        assert ws(lib, 201728, 768, 8, flags=f) == 0
+        assert bwd(lib, flags=f) == INVALID
+    assert bwd(lib, flags=DET, ws_bytes=100) == INVALID      # deterministic needs its workspace
+    assert bwd(lib, flags=DET, ws_ptr=None) == INVALID
 
 
 def test_status_strings(lib):
@@ -115,7 +147,7 @@ def test_forward_empty_is_ok_without_device(lib):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dA=None), INVALID), (dict(dB=None), INVALID), (dict(dx=None), INVALID), (dict(dy=None), INVALID),
-    (dict(flags=4), INVALID), (dict(flags=BLOCK | NAIVE), INVALID),
+    (dict(flags=8), INVALID), (dict(flags=BLOCK | NAIVE), INVALID), (dict(flags=DET | BLOCK), INVALID),
     (dict(ws_ptr=None), INVALID), (dict(ws_bytes=100), INVALID),
     (dict(ws_ptr=P + 0x700008), UNSUPPORTED),
     (dict(dx=P + 16), INVALID),                      # dx partially overlaps x
