@@ -12,8 +12,9 @@
 // 突破与残留问题" and "损失函数 / 训练策略"); the pages note that the same
 // kernel restructuring applies to PAU and its variants (section "局限性与未来
 // 工作"), i.e. to other (M, N), which the templates below cover.  N = 0 is a
-// plain polynomial.  Everything here is fp32 register arithmetic; the only
-// fp64 use is deciding the sign of Q for the rare element whose fp32 Q is
+// plain polynomial.  Everything here is fp32 register arithmetic except two
+// fp64 uses in the backward: Q is evaluated in fp64 (see backward_element),
+// and the sign of Q is decided exactly for the rare element whose Q is
 // within rounding of 0.
 #pragma once
 
@@ -212,25 +213,63 @@ template <int K> struct Pow {
     }
 };
 
+// Exact fp64 value of an fp32 number, formed with integer operations only:
+// for a coefficient loaded with a uniform address (held in scalar registers)
+// the whole conversion runs on the scalar unit, where gfx950 has no float
+// conversion instruction, instead of taking vector registers and instructions
+// in every lane.  Normal numbers move their exponent and mantissa fields;
+// subnormals are normalised; zeros, infinities and NaNs keep their class.
+__device__ static inline double widen_exact(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = u & 0x80000000u;
+    const uint32_t e = (u >> 23) & 0xffu;
+    const uint32_t m = u & 0x7fffffu;
+    uint32_t hi, lo;
+    if (e == 0xffu) {                      // infinity or NaN
+        hi = sign | 0x7ff00000u | (m >> 3);
+        lo = m << 29;
+    } else if (e != 0u) {                  // normal: 2^(e - 127) * 1.m
+        hi = sign | ((e + 896u) << 20) | (m >> 3);
+        lo = m << 29;
+    } else if (m == 0u) {                  // signed zero
+        hi = sign;
+        lo = 0u;
+    } else {                               // subnormal: m * 2^-149, top bit at p
+        const uint32_t p = 31u - (uint32_t)__builtin_clz(m);
+        const uint32_t mm = (m << (23u - p)) & 0x7fffffu;
+        hi = sign | ((p + 874u) << 20) | (mm >> 3);
+        lo = mm << 29;
+    }
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Constants of the backward pass derived from one group's coefficients.
 template <int M, int N> struct BwdCoefs {
     float a[M + 1];              // a_0..a_M
     float da[M > 0 ? M : 1];     // i * a_i, i = 1..M   (P')
     float b[N > 0 ? N : 1];      // b_1..b_N
     float db[N > 0 ? N : 1];     // j * b_j, j = 1..N   (Q')
+    double bd[N > 0 ? N : 1];    // b_1..b_N in fp64 (exact), for Q
     float kguard;                // sign guard scale, see below
     bool q_zero;                 // b = 0 (or N = 0): Q vanishes identically, s = 0
 };
 
-// The sign guard.  With powers formed as above and Q = x (b_1 + b_2 x + ...)
-// summed by FMAs over them, the fp32 Q differs from the exact Q(x) by at most
-// about (2N + 1) 2^-24 sum_j |b_j| |x|^j, and sum_j |b_j| |x|^j is at most
-// (sum_j |b_j|) (|x| + |x|^N).  So |Q| > (N + 4) 2^-21 (sum_j |b_j|)
-// (|x| + |x|^N) -- at least four times that bound -- proves Q != 0 and
-// sign(fl(Q)) = sign(Q).  (For GR-KAN's N = 4 the scale is 2^-18.)
+// The sign guard.  The backward's Q is x q(x) by Horner's rule in fp64,
+// rounded once to fp32 (backward_element); it differs from the exact Q(x) by
+// at most 2^-24 |Q| plus an fp64 error far below 2^-24 sum_j |b_j| |x|^j,
+// and sum_j |b_j| |x|^j is at most (sum_j |b_j|) (|x| + |x|^N).  So
+// |Q| > (N + 4) 2^-21 (sum_j |b_j|) (|x| + |x|^N) -- a bound derived for an
+// fp32 evaluation, (2N + 1) 2^-24 sum_j |b_j| |x|^j, times four, and thus a
+// conservative one here -- proves Q != 0 and sign(fl(Q)) = sign(Q).  (For
+// GR-KAN's N = 4 the scale is 2^-18.)  It fails at x = 0 (Q = 0), next to a
+// root of Q (rare: about 1e-5 of the elements at the workloads' inputs) and
+// for NaN or huge x; those elements take the exact path.
 template <int N> constexpr float sign_guard_scale() { return (float)(N + 4) / 2097152.0f; }
 
-template <int M, int N>
+// UNIFORM: the coefficients are the same in every lane (scalar registers), so
+// their fp64 copies are formed on the scalar unit; otherwise (per-lane
+// coefficients) by the vector conversion.
+template <int M, int N, bool UNIFORM = true>
 __device__ static inline BwdCoefs<M, N> derive(const Coefs<M, N> &c) {
     BwdCoefs<M, N> k;
 #pragma unroll
@@ -246,6 +285,7 @@ __device__ static inline BwdCoefs<M, N> derive(const Coefs<M, N> &c) {
     for (int j = 0; j < N; ++j) {
         k.b[j] = c.b[j];
         k.db[j] = (float)(j + 1) * c.b[j];
+        k.bd[j] = UNIFORM ? widen_exact(c.b[j]) : (double)c.b[j];
         bsum += fabsf(c.b[j]);
         nonzero |= __float_as_uint(c.b[j]) << 1;
     }
@@ -253,6 +293,7 @@ __device__ static inline BwdCoefs<M, N> derive(const Coefs<M, N> &c) {
     if constexpr (N == 0) {
         k.b[0] = 0.0f;
         k.db[0] = 0.0f;
+        k.bd[0] = 0.0;
     }
     k.kguard = sign_guard_scale<N>() * bsum;
     k.q_zero = zero;
@@ -287,8 +328,16 @@ __device__ static inline int sign_q_exact(float xf, const BwdCoefs<M, N> &k) {
     return (q > 0.0) - (q < 0.0);
 }
 
-// Everything the backward needs about one element, fast fp32 evaluation.
-// s = sign(Q) is taken from the fp32 Q; `sure` says whether the guard proves
+// Everything the backward needs about one element.  fp32 arithmetic except Q:
+// Q = x q(x) is evaluated by Horner's rule in fp64 from the exact fp64 value
+// of x and rounded once to fp32.  In fp32, Q's rounding error is relative to
+// sum_j |b_j x^j| rather than to |Q|; next to a root of Q with large terms
+// (|x| ~ 3 at GR-KAN's coefficients) that error reaches ~1e-6 of D = 1 + |Q|
+// and passes into every gradient term of the element, which is enough to move
+// a group sum that cancels to a few thousandths of its terms' norm by more
+// than 1e-4 of itself.  In fp64 D is correctly rounded up to 2 units.  (gfx950
+// issues fp64 FMAs at the fp32 rate; this costs two conversions per element.)
+// s = sign(Q) is taken from that Q; `sure` says whether the guard proves
 // that sign right.  When it does not (x == 0, x within rounding of a root of
 // Q, NaN), the element still gets the fp32 sign here and exact_fix() later
 // swaps in the exact one.  One function so that the hot loop and the fix
@@ -325,13 +374,14 @@ __device__ static inline ElemBwd backward_element(const Pow<K> &X, float dy, con
         e.F = P;
         e.sure = true;
     } else {
-        float q = k.b[0];
+        const double xd = (double)x;
+        double qd = k.bd[N - 1];
 #pragma unroll
-        for (int j = 1; j < N; ++j) q = fmaf(k.b[j], X.p[j], q);
+        for (int j = N - 2; j >= 0; --j) qd = fma(qd, xd, k.bd[j]);
+        const float Q = (float)(xd * qd);
         float Qd = k.db[0];
 #pragma unroll
         for (int j = 1; j < N; ++j) Qd = fmaf(k.db[j], X.p[j], Qd);
-        const float Q = x * q;
         const float r = __builtin_amdgcn_rcpf(1.0f + fabsf(Q));
         e.w = dy * r;
         e.F = P * r;

@@ -220,7 +220,38 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_fwd_kernel(FwdArgs a) {
 // and dy, which is safe even when dx aliases x or dy.
 // With WY, F(x) is stored too, through ry (which may be rdy: every load
 // precedes every store).
-template <class IO, int M, int N, int U, bool QZERO, bool CHECK, int R = 1, bool WY = false>
+template <int U>
+__device__ static inline void load_pair(Span ra, Span rb, const Window &w, u32x4 (&a)[U], u32x4 (&b)[U]) {
+    // Only the loads and stores differ between full and partial tiles, so only
+    // they are branched on (a uniform branch); a second copy of the whole tile
+    // for full tiles costs registers.
+    if (w.full) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            a[u] = win_load16<false>(ra, w.lane + u * w.stride);
+            b[u] = win_load16<false>(rb, w.lane + u * w.stride);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            a[u] = win_load16<true>(ra, w.lane + u * w.stride);
+            b[u] = win_load16<true>(rb, w.lane + u * w.stride);
+        }
+    }
+}
+
+template <int U>
+__device__ static inline void store_all(Span r, const Window &w, const u32x4 (&v)[U]) {
+    if (w.full) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) win_store16<false>(r, w.lane + u * w.stride, v[u]);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) win_store16<true>(r, w.lane + u * w.stride, v[u]);
+    }
+}
+
+template <class IO, int M, int N, int U, bool QZERO, int R = 1, bool WY = false>
 __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window &w,
                                        const BwdCoefs<M, N> &k, float (&acc)[Deg<M, N>::kNumCoef],
                                        Span ry = Span{}) {
@@ -229,11 +260,7 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
     constexpr int K = Deg<M, N>::kTop;
 
     u32x4 xin[U], din[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        xin[u] = win_load16<CHECK>(rx, w.lane + u * w.stride);
-        din[u] = win_load16<CHECK>(rdy, w.lane + u * w.stride);
-    }
+    load_pair<U>(rx, rdy, w, xin, din);
     float dxf[U][E];
     [[maybe_unused]] u32x4 ypk[WY ? U : 1];  // F, packed to the I/O type as each pass ends
     bool sure = true;
@@ -275,6 +302,7 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
             }
         }
         if constexpr (WY) ypk[u] = V::pack(yf);
+        if constexpr (!is_f32<IO>()) __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (!QZERO) {
         // Rare: some element's sign of Q was not proven by the fp32 guard.
@@ -284,24 +312,86 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 float xf[E], dyf[E];
-                V::unpack(win_reload16<CHECK>(rx, w.lane + u * w.stride), xf);
-                V::unpack(win_reload16<CHECK>(rdy, w.lane + u * w.stride), dyf);
+                V::unpack(win_reload16<true>(rx, w.lane + u * w.stride), xf);
+                V::unpack(win_reload16<true>(rdy, w.lane + u * w.stride), dyf);
 #pragma unroll
                 for (int e = 0; e < E; ++e) dxf[u][e] = exact_fix<M, N>(xf[e], dyf[e], k, acc);
             }
         }
     }
+    u32x4 dxpk[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) win_store16<CHECK>(rdx, w.lane + u * w.stride, V::pack(dxf[u]));
-    if constexpr (WY) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) win_store16<CHECK>(ry, w.lane + u * w.stride, ypk[u]);
-    }
+    for (int u = 0; u < U; ++u) dxpk[u] = V::pack(dxf[u]);
+    store_all<U>(rdx, w, dxpk);
+    if constexpr (WY) store_all<U>(ry, w, ypk);
 }
 
 // Slot of a tile's partial within its part: tiles of one XCD side by side.
 __device__ static inline int64_t slot_in_part(const Plan &P, int64_t tile) {
     return (tile & 7) * P.bundles + (tile >> 3);
+}
+
+// Workgroup sum of the NC lane sums, in a fixed order, and its exit: one fp32
+// partial per (group, coefficient, part, tile), or one fp32 atomic add per
+// coefficient.
+//   1. Each wave writes its lanes' sums to its own LDS rows [wave][NC][64]:
+//      one base address per lane, the coefficient index in the instruction's
+//      immediate offset.  Lanes a partial last wave lacks are zero-filled.
+//   2. Slice s (0..15) of a coefficient is lanes 4s..4s+3 of every wave;
+//      thread (k, s) adds slice s of coefficient k in fp32, wave by wave, one
+//      16-byte LDS read per wave (consecutive threads read consecutive 16-byte
+//      words: no bank conflicts).
+//   3. Thread k adds its coefficient's 16 slices in fp64.
+// About 4 vector instructions and 5 paired LDS writes per lane for step 1 and
+// 5 per wave for step 2, against ~60 for DPP sums of ten values across each
+// wave; the order
+// depends only on the block shape, so the partials are bitwise reproducible.
+template <int M, int N>
+__device__ static inline void reduce_and_emit(const BwdArgs &a, const Plan &P, const Pos &p,
+                                              const float (&acc)[Deg<M, N>::kNumCoef]) {
+    constexpr int NC = Deg<M, N>::kNumCoef;
+    extern __shared__ float4 red4[];  // [nw][NC][64] lane sums, then [NC][16] slices
+    float *red = reinterpret_cast<float *>(red4);
+    const int nb = (int)(blockDim.x * blockDim.y);
+    const int nw = (nb + 63) >> 6;
+    const int t = (int)(threadIdx.y * blockDim.x + threadIdx.x);
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int lane = t & 63;
+    float *mine = red + wave * (NC * 64) + lane;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) mine[i * 64] = acc[i];
+    const int tail = nb & 63;  // lanes of a partial last wave (0: none)
+    if (tail != 0) {
+        const int missing = 64 - tail;
+        float *last = red + (nw - 1) * (NC * 64);
+        for (int q = t; q < NC * missing; q += nb) last[(q / missing) * 64 + tail + q % missing] = 0.0f;
+    }
+    __syncthreads();
+    float *slices = red + nw * (NC * 64);
+    for (int idx = t; idx < NC * 16; idx += nb) {
+        // slice s = idx mod 16 of coefficient idx / 16: lanes 4s..4s+3 of every
+        // wave, i.e. the 16-byte row element idx + j * NC * 16 for wave j
+        const float4 *src = red4 + idx;
+        float slice = 0.0f;
+        for (int j = 0; j < nw; ++j, src += NC * 16) {
+            const float4 q = *src;
+            slice += ((q.x + q.y) + q.z) + q.w;
+        }
+        slices[idx] = slice;
+    }
+    __syncthreads();
+    if (t < NC) {
+        double total = 0.0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) total += (double)slices[t * 16 + j];
+        if (a.mode == kModePartials) {
+            const int64_t slot = (int64_t)p.part * 8 * P.bundles + slot_in_part(P, p.tile);
+            a.partials[((int64_t)p.g * NC + t) * plan_slots(P) + slot] = (float)total;
+        } else {
+            float *dst = (t <= M) ? (a.dA + p.g * (M + 1) + t) : (a.dB + p.g * N + (t - M - 1));
+            unsafeAtomicAdd(dst, (float)total);
+        }
+    }
 }
 
 // R = 1: the plain backward; R = 2, 4, 8: the FLOP-inflation probe.  WY: F(x)
@@ -320,58 +410,13 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
     float acc[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) acc[i] = 0.0f;
-    // (A second, unchecked copy of the tile for full tiles spilled: the
-    // per-access checks cost < 1 VALU operation per element here.)
     const Span ry = WY ? make_span(at(a.y, w.base), w.avail) : Span{};
     if (k.q_zero) {
-        bwd_tile<IO, M, N, U, true, true, R, WY>(rx, rdy, rdx, w, k, acc, ry);
+        bwd_tile<IO, M, N, U, true, R, WY>(rx, rdy, rdx, w, k, acc, ry);
     } else {
-        if constexpr (N > 0) bwd_tile<IO, M, N, U, false, true, R, WY>(rx, rdy, rdx, w, k, acc, ry);
+        if constexpr (N > 0) bwd_tile<IO, M, N, U, false, R, WY>(rx, rdy, rdx, w, k, acc, ry);
     }
-
-    // Workgroup sum of the NC terms, in a fixed order: transposed through LDS
-    // (lane sums -> red[k][lane], zero-padded to whole waves); 16 threads per
-    // coefficient add nbp/16 consecutive lanes each in fp32; thread k adds its
-    // coefficient's 16 slices in fp64.  About 13 VALU operations per lane for
-    // GR-KAN's 10 sums, against 60 for DPP sums of the ten values across each
-    // wave (measured faster on MI355X, where the backward's VALU load and
-    // power draw matter).
-    extern __shared__ float red[];  // [NC][nbp], then [NC][16] slices
-    const int nb = (int)(blockDim.x * blockDim.y);
-    const int nbp = (nb + 63) & ~63;
-    const int t = (int)(threadIdx.y * blockDim.x + threadIdx.x);
-#pragma unroll
-    for (int i = 0; i < NC; ++i) red[i * nbp + t] = acc[i];
-    for (int q = t; q < nbp - nb; q += nb) {
-#pragma unroll
-        for (int i = 0; i < NC; ++i) red[i * nbp + nb + q] = 0.0f;
-    }
-    __syncthreads();
-    float *slices = red + NC * nbp;
-    const int per = nbp / 16;  // a multiple of 4
-    for (int idx = t; idx < NC * 16; idx += nb) {
-        const int kk = idx >> 4, seg = idx & 15;
-        const float4 *src = reinterpret_cast<const float4 *>(red + kk * nbp + seg * per);
-        float slice = 0.0f;
-        for (int j = 0; j < per / 4; ++j) {
-            const float4 q = src[j];
-            slice += ((q.x + q.y) + q.z) + q.w;
-        }
-        slices[idx] = slice;
-    }
-    __syncthreads();
-    if (t < NC) {
-        double total = 0.0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) total += (double)slices[t * 16 + j];
-        if (a.mode == kModePartials) {
-            const int64_t slot = (int64_t)p.part * 8 * P.bundles + slot_in_part(P, p.tile);
-            a.partials[((int64_t)p.g * NC + t) * plan_slots(P) + slot] = (float)total;
-        } else {
-            float *dst = (t <= M) ? (a.dA + p.g * (M + 1) + t) : (a.dB + p.g * N + (t - M - 1));
-            unsafeAtomicAdd(dst, (float)total);
-        }
-    }
+    reduce_and_emit<M, N>(a, P, p, acc);
 }
 
 // ------------------------------------------------------ narrow groups
@@ -556,7 +601,7 @@ __global__ __launch_bounds__(kNarrowBwdThreads) void grkan_bwd_narrow_kernel(Bwd
     if (p.tile >= P.tiles) return;
     int64_t ch;
     const Window w = narrow_window<RW, U, K>(P, p, ch);
-    const BwdCoefs<M, N> k = derive<M, N>(load_coefs<M, N>(a.A, a.B, narrow_group(P, ch)));
+    const BwdCoefs<M, N> k = derive<M, N, false>(load_coefs<M, N>(a.A, a.B, narrow_group(P, ch)));
     const Span sx = make_span(at(a.x, w.base), w.avail);
     const Span sdy = make_span(at(a.dy, w.base), w.avail);
     const Span sdx = make_span(at(a.dx, w.base), w.avail);
@@ -634,8 +679,8 @@ hipError_t fwd_impl(const FwdArgs &a, int repeat, dim3 grid, hipStream_t s) {
 
 template <int M, int N>
 size_t bwd_lds_bytes(int block) {
-    const int nbp = (block + 63) & ~63;
-    return (size_t)Deg<M, N>::kNumCoef * (nbp + 16) * sizeof(float);
+    const int nw = (block + 63) / 64;
+    return (size_t)Deg<M, N>::kNumCoef * (nw * 64 + 16) * sizeof(float);
 }
 
 template <class IO, int M, int N>

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void grkan_bwd_naive_kernel(const void *x, con
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         const int g = (int)((i % d) / d_g);
-        const BwdCoefs<kM, kN> k = derive<kM, kN>(load_coefs<kM, kN>(A, B, g));
+        const BwdCoefs<kM, kN> k = derive<kM, kN, false>(load_coefs<kM, kN>(A, B, g));
         float acc[kNumCoef];
 #pragma unroll
         for (int c = 0; c < kNumCoef; ++c) acc[c] = 0.0f;

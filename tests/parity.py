@@ -15,13 +15,19 @@ Tolerances (fixed here, used by every parity test):
   leaves an error of order 2^-24 * ||t||_2 whatever the summation; a sum
   that cancels to |ref| << ||t||_2 is therefore compared at 1e-6 ||t||_2,
   about 17 units of that floor.
-* dA and dB, plus 8 * 2^-24 * ||m||_2 with ||m||_2 the L2 norm of the terms'
-  first-order rounding scales (oracle: magsq).  Each term is evaluated from
-  an fp32 Q whose rounding error is relative to Qabs, the sum of |b_j x^j|,
-  not to |Q|; next to a root of Q with large terms (high degrees, |x| ~ 3)
-  one element's term can be off by far more than 2^-24 |t|, and no fp32
-  evaluation avoids that.  The scale is the sums' analogue of the elements'
-  M above; for GR-KAN's workloads it is below the 1e-6 ||t||_2 floor.
+* dA and dB in the deterministic scheme at GR-KAN's degrees (5, 4), the five
+  GR-KAN workloads included: additionally the literal rule of the task,
+  |gpu - ref| <= max(1e-4 |ref|, 1e-6), asserted (``literal=True``).
+* dA and dB at the PAU degree pairs (6, 5) and (7, 6) only: plus
+  8 * 2^-24 * ||m||_2 with ||m||_2 the L2 norm of the terms' first-order
+  rounding scales (oracle: magsq).  Each term is evaluated from an fp32 Q
+  whose rounding error is relative to Qabs, the sum of |b_j x^j|, not to |Q|;
+  next to a root of Q with large terms (degree-5 and -6 denominators at
+  |x| ~ 3) one element's term can be off by far more than 2^-24 |t|, and no
+  fp32 evaluation avoids that.  At GR-KAN's degrees this allowance is not
+  needed and not given: on the committed full-size sums of the five GR-KAN
+  workloads it would exceed the 1e-6 ||t||_2 floor (by up to ~100x on dB),
+  i.e. it would widen the bound where nothing requires it.
 * dA and dB of the comparison scheme GRKAN_BLOCK_ATOMIC (one fp32 atomic add
   per coefficient per workgroup, the pages' Algorithm 2): the above plus
   8 * 2^-24 * sqrt(n) * ||t||_2 for n workgroup partials added in fp32 in an
@@ -83,6 +89,20 @@ def check_elem(name: str, gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray, io:
 
 
 TERM_ROUNDING = 8 * 2.0 ** -24
+# Degree pairs whose dA / dB comparison carries the TERM_ROUNDING allowance (see above): the
+# ones where fp32 terms next to a root of a high-degree Q were measured to need it.
+TERM_ROUNDING_PAIRS = {(6, 5), (7, 6)}
+
+
+def term_mag(m: int, n: int, mag):
+    """The rounding-scale norms to pass as ``mag`` for degrees (m, n): only for the pairs that
+    need the allowance, else None."""
+    return mag if (m, n) in TERM_ROUNDING_PAIRS else None
+
+
+def literal_tol(ref: np.ndarray) -> np.ndarray:
+    """The task's literal dA / dB rule: rel 1e-4 with an absolute floor of 1e-6."""
+    return np.maximum(REL_SUM * np.abs(ref), ABS_SUM)
 
 
 def sum_tol(ref: np.ndarray, norm: np.ndarray, mag=None) -> np.ndarray:
@@ -93,8 +113,9 @@ def sum_tol(ref: np.ndarray, norm: np.ndarray, mag=None) -> np.ndarray:
 
 
 def check_sums(name: str, gpu: np.ndarray, ref: np.ndarray, norm: np.ndarray,
-               atomic_adds: int = 0, mag=None, extra=None) -> dict:
-    """``mag``: L2 norm of the terms' rounding scales (oracle ``mA`` / ``mB``)."""
+               atomic_adds: int = 0, mag=None, extra=None, literal: bool = False) -> dict:
+    """``mag``: L2 norm of the terms' rounding scales (oracle ``mA`` / ``mB``), given only for the
+    degree pairs in TERM_ROUNDING_PAIRS.  ``literal``: also assert the literal rule."""
     gpu = np.asarray(gpu, dtype=np.float64)
     err = np.abs(gpu - ref)
     tol = sum_tol(ref, norm, mag)
@@ -103,8 +124,9 @@ def check_sums(name: str, gpu: np.ndarray, ref: np.ndarray, norm: np.ndarray,
     if atomic_adds:
         tol = tol + 8 * 2.0 ** -24 * np.sqrt(atomic_adds) * norm
     bad = ~(err <= tol)
-    literal = int(np.sum(err > np.maximum(REL_SUM * np.abs(ref), ABS_SUM)))
-    stats = {"bad": int(bad.sum()), "literal_fail": literal,
+    lit_bad = ~(err <= literal_tol(ref))
+    stats = {"bad": int(bad.sum()), "literal_fail": int(lit_bad.sum()),
+             "max_err_over_literal": float(np.max(err / literal_tol(ref))) if err.size else 0.0,
              "max_rel": float(np.max(err / np.maximum(np.abs(ref), 1e-300))),
              "max_err_over_norm": float(np.max(err / np.maximum(norm, 1e-300)))}
     if bad.any():
@@ -112,6 +134,11 @@ def check_sums(name: str, gpu: np.ndarray, ref: np.ndarray, norm: np.ndarray,
         raise AssertionError(f"{name}: {stats['bad']} coefficients outside tolerance at {idx}: "
                              f"gpu={gpu[bad][:8].tolist()} ref={ref[bad][:8].tolist()} "
                              f"tol={tol[bad][:8].tolist()}")
+    if literal and lit_bad.any():
+        idx = np.argwhere(lit_bad)[:8].tolist()
+        raise AssertionError(f"{name}: {int(lit_bad.sum())} coefficients fail the literal rule "
+                             f"(rel 1e-4, abs 1e-6) at {idx}: gpu={gpu[lit_bad][:8].tolist()} "
+                             f"ref={ref[lit_bad][:8].tolist()}")
     return stats
 
 

@@ -76,9 +76,11 @@ def run_and_check(gk, w, inp, mode, tag):
         n_add *= gk.grkan_pau_query_launch(w.rows, w.d, w.n_groups, m, n, iocode(gk, w.io), 2)["parts"]
     parity.check_elem(f"{tag} Y", to_host(y, w.io), ref["y"], ref["ymag"], w.io)
     parity.check_elem(f"{tag} dX", to_host(dx, w.io), ref["dx"], ref["dxmag"], w.io)
-    parity.check_sums(f"{tag} dA", dA.cpu().numpy(), ref["dA"], ref["nA"], n_add, ref["mA"])
+    parity.check_sums(f"{tag} dA", dA.cpu().numpy(), ref["dA"], ref["nA"], n_add,
+                      parity.term_mag(m, n, ref["mA"]))
     if n > 0:
-        parity.check_sums(f"{tag} dB", dB.cpu().numpy(), ref["dB"], ref["nB"], n_add, ref["mB"])
+        parity.check_sums(f"{tag} dB", dB.cpu().numpy(), ref["dB"], ref["nB"], n_add,
+                          parity.term_mag(m, n, ref["mB"]))
     else:
         assert dB is None
 
@@ -199,7 +201,9 @@ def test_pau_full_size(gk, name):
     parity.check_elem(f"{name} dX[sampled]", dxs, rec[:, orc.DX], rec[:, orc.DXMAG], w.io)
     g = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                                     f"{name}.sums.json")))
-    parity.check_sums(f"{name} dA", dA.cpu().numpy(), np.array(g["dA"]), np.array(g["nA"]), mag=np.array(g["mA"]))
+    parity.check_sums(f"{name} dA", dA.cpu().numpy(), np.array(g["dA"]), np.array(g["nA"]),
+                      mag=parity.term_mag(m, n, np.array(g["mA"])))
     if n > 0:
-        parity.check_sums(f"{name} dB", dB.cpu().numpy(), np.array(g["dB"]), np.array(g["nB"]), mag=np.array(g["mB"]))
+        parity.check_sums(f"{name} dB", dB.cpu().numpy(), np.array(g["dB"]), np.array(g["nB"]),
+                          mag=parity.term_mag(m, n, np.array(g["mB"])))
     log(f"[pau_full] {name}: ok")
