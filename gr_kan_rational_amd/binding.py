@@ -60,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grkan_forward.restype = ctypes.c_int
     lib.grkan_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, ctypes.c_int, u32, vp, sz, vp]
     lib.grkan_backward.restype = ctypes.c_int
+    lib.grkan_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, ctypes.c_int, vp]
+    lib.grkan_backward_noalloc.restype = ctypes.c_int
     lib.grkan_backward_workspace_size.argtypes = [i64, i64, i32, ctypes.c_int, u32]
     lib.grkan_backward_workspace_size.restype = sz
     lib.grkan_status_string.argtypes = [ctypes.c_int]
@@ -253,6 +255,31 @@ def grkan_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B: torch.
     """
     return _backward(x, dy, A, B, n_groups, GRKAN_M, GRKAN_N, mode, dx, dA, dB, workspace, stream,
                      pau=False)
+
+
+def grkan_backward_noalloc(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                           n_groups: int = 8, dx: torch.Tensor | None = None, dA: torch.Tensor | None = None,
+                           dB: torch.Tensor | None = None, stream=None):
+    """(dx, dA, dB) by ``grkan_backward_noalloc``: the deterministic scheme with the library's own
+    fixed scratch array instead of a workspace (no device allocation inside the call; the output
+    tensors are allocated here only when not given)."""
+    lib = load_library()
+    io = _io(x)
+    if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device or not dy.is_contiguous():
+        raise ValueError("dy must match x")
+    _check_coefs(A, B, n_groups, x.device)
+    rows, d = _rows_d(x)
+    dx = torch.empty_like(x) if dx is None else dx
+    dA = torch.empty((n_groups, GRKAN_M + 1), dtype=torch.float32, device=x.device) if dA is None else dA
+    dB = torch.empty((n_groups, GRKAN_N), dtype=torch.float32, device=x.device) if dB is None else dB
+    st = lib.grkan_backward_noalloc(_ptr(x), _ptr(dy), _ptr(A), _ptr(B), _ptr(dx), _ptr(dA), _ptr(dB),
+                                    rows, d, n_groups, io, ctypes.c_void_p(_stream(stream)))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_backward_noalloc")
+    return dx, dA, dB
+
+
+GRKAN_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 def grkan_pau_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B, n_groups: int,

@@ -279,7 +279,7 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
                              float *dA, float *dB, int64_t rows, int64_t d, int32_t n_groups,
                              int32_t m, int32_t n, grkan_dtype_t io, uint32_t flags,
                              void *workspace, size_t workspace_bytes, hipStream_t stream,
-                             int32_t repeat = 1, void *y = nullptr) {
+                             int32_t repeat = 1, void *y = nullptr, bool validate_only = false) {
     const int scheme = scheme_of(flags);
     if (scheme < 0) return GRKAN_ERR_INVALID_ARG;
     const bool det = scheme == 0, naive = scheme == 2;
@@ -309,7 +309,7 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
     for (int i = 0; i < 5; ++i)
         if (overlap(dA, ab, others[i], sizes[i]) || overlap(dB, bb, others[i], sizes[i]))
             return GRKAN_ERR_INVALID_ARG;
-    if (det && rows > 0) {
+    if (det && rows > 0 && !validate_only) {
         const size_t need = workspace_need(P);
         if (!workspace || workspace_bytes < need) return GRKAN_ERR_INVALID_ARG;
         if (!aligned(workspace, 16)) return GRKAN_ERR_UNSUPPORTED;
@@ -318,6 +318,8 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
         if (overlap(workspace, need, dA, ab) || overlap(workspace, need, dB, bb))
             return GRKAN_ERR_INVALID_ARG;
     }
+
+    if (validate_only) return GRKAN_OK;
 
     // ---- validation done; HIP calls from here on
     const int64_t na = (int64_t)n_groups * (m + 1), nb = (int64_t)n_groups * n;
@@ -410,6 +412,66 @@ extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const fl
                                          size_t workspace_bytes, hipStream_t stream) {
     return backward_impl(x, dy, A, B, dx, dA, dB, rows, d, n_groups, kGrkanM, kGrkanN, io, flags,
                          workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------- backward without allocation
+//
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops, harnesses that forbid allocation): the deterministic
+// backward with its partial sums in a fixed device array of this library
+// instead of a caller's workspace.  The array lives as long as the process,
+// one copy per device the library runs on.  In host code its name is only a
+// stand-in for the symbol: the device address is asked of the runtime once
+// per device (hipGetSymbolAddress) and that address is what the kernels get.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[GRKAN_NOALLOC_SCRATCH_BYTES];
+
+void *g_scratch[kMaxDev];
+
+// The device address of `scratch` on the current device; looked up on the
+// first call on each device.
+grkan_status_t scratch_ptr(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return GRKAN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GRKAN_ERR_HIP;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return GRKAN_OK;
+}
+
+}  // namespace
+
+extern "C" grkan_status_t grkan_backward_noalloc(const void *x, const void *dy, const float *A,
+                                                 const float *B, void *dx, float *dA, float *dB,
+                                                 int64_t rows, int64_t d, int32_t n_groups,
+                                                 grkan_dtype_t io, hipStream_t stream) {
+    const DegreeOps *deg = find_degree(kGrkanM, kGrkanN);
+    Plan P;
+    grkan_status_t st = plan_shape(rows, d, n_groups, *deg, io, 1, false, &P);
+    if (st != GRKAN_OK) return st;
+    const size_t need = rows > 0 ? workspace_need(P) : 0;
+    if (need > (size_t)GRKAN_NOALLOC_SCRATCH_BYTES) return GRKAN_ERR_UNSUPPORTED;
+    // Every other check is backward_impl's, which runs before any HIP call;
+    // a null workspace with rows > 0 would be reported as INVALID_ARG there,
+    // so the lookup is only skipped when nothing needs the scratch.
+    void *ws = nullptr;
+    if (need > 0) {
+        // validate first with a stand-in (never dereferenced), so that an
+        // invalid call makes no HIP call at all
+        st = backward_impl(x, dy, A, B, dx, dA, dB, rows, d, n_groups, kGrkanM, kGrkanN, io,
+                           GRKAN_DETERMINISTIC, nullptr, 0, stream, 1, nullptr, /*validate_only=*/true);
+        if (st != GRKAN_OK) return st;
+        st = scratch_ptr(&ws);
+        if (st != GRKAN_OK) return st;
+    }
+    return backward_impl(x, dy, A, B, dx, dA, dB, rows, d, n_groups, kGrkanM, kGrkanN, io,
+                         GRKAN_DETERMINISTIC, ws, need, stream);
 }
 
 extern "C" grkan_status_t grkan_query_launch(int64_t rows, int64_t d, int32_t n_groups,

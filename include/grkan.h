@@ -145,6 +145,30 @@ GRKAN_API grkan_status_t grkan_backward(const void *x, const void *dy, const flo
 GRKAN_API size_t grkan_backward_workspace_size(int64_t rows, int64_t d, int32_t n_groups,
                                      grkan_dtype_t io, uint32_t flags);
 
+/*
+ * grkan_backward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The deterministic two-stage scheme of grkan_backward
+ * (same kernels, same bits), with its partial sums in a fixed device array of
+ * GRKAN_NOALLOC_SCRATCH_BYTES inside the library: one copy per device, held
+ * until the process ends, its address looked up on the first call on each
+ * device.  The call allocates nothing and frees nothing.
+ *   Arguments and errors as grkan_backward (no flags, no workspace); a shape
+ *   whose partial sums need more than GRKAN_NOALLOC_SCRATCH_BYTES (what
+ *   grkan_backward_workspace_size() reports for it) is GRKAN_ERR_UNSUPPORTED,
+ *   before any HIP call.  16 MiB covers every GR-KAN shape up to twice the
+ *   KAT-B hidden activations in bf16 (8.1 MB there).
+ *   Calls on one device share the array and must not overlap in time (e.g.
+ *   run on different streams without ordering): they would race on it.
+ *   Nothing in it needs to start at zero -- every partial sum is written
+ *   before it is read -- so no clearing is done between calls.
+ */
+#define GRKAN_NOALLOC_SCRATCH_BYTES (16u << 20)
+GRKAN_API grkan_status_t grkan_backward_noalloc(const void *x, const void *dy, const float *A,
+                                      const float *B, void *dx, float *dA, float *dB,
+                                      int64_t rows, int64_t d, int32_t n_groups,
+                                      grkan_dtype_t io, hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 GRKAN_API const char *grkan_status_string(grkan_status_t status);
 

@@ -43,7 +43,7 @@ def test_header_declares_the_abi():
         "grkan_inflated_forward", "grkan_inflated_backward",
         "grkan_layer_forward", "grkan_linear_forward", "grkan_layer_backward",
         "grkan_layer_backward_workspace_size", "grkan_chebykan_forward", "grkan_chebykan_backward",
-        "grkan_chebykan_backward_workspace_size"])
+        "grkan_chebykan_backward_workspace_size", "grkan_backward_noalloc"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -390,3 +390,35 @@ def test_chebykan_backward_rejects(lib, kw, code):
 
 def test_chebykan_empty_is_ok_without_device(lib):
     assert cfwd(lib, x=None, y=None, rows=0) == OK
+
+
+# ------------------------------------------------- backward without allocation
+
+def nbwd(lib, x=P, dy=P + 0x100000, A=P + 0x200000, B=P + 0x300000, dx=P + 0x400000,
+         dA=P + 0x500000, dB=P + 0x600000, rows=4, d=64, n_g=8, io=F32):
+    return lib.grkan_backward_noalloc(x, dy, A, B, dx, dA, dB, rows, d, n_g, io, None)
+
+
+def test_noalloc_scratch_limit_is_pinned():
+    from gr_kan_rational_amd import binding
+
+    m = re.search(r"#define GRKAN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.GRKAN_NOALLOC_SCRATCH_BYTES == 16 << 20
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dA=None), INVALID), (dict(dx=None), INVALID), (dict(d=66), INVALID), (dict(io=7), INVALID),
+    (dict(dx=P + 16), INVALID), (dict(dA=P + 0x600000 + 8), INVALID), (dict(x=P + 4), UNSUPPORTED),
+    # bf16 KAT-B hidden at 3x the batch: 24.2 MB of partial sums > the 16 MiB array
+    (dict(rows=3 * 201728, d=3072, io=BF16), UNSUPPORTED),
+])
+def test_noalloc_rejects_before_any_device_call(lib, kw, code):
+    assert nbwd(lib, **kw) == code
+
+
+def test_noalloc_covers_the_gr_kan_workloads(lib):
+    """The five GR-KAN workloads fit the array (their partial sums are what the workspace query
+    reports), and so does the KAT-B hidden bf16 shape at twice the batch."""
+    for rows, d, io in ((16, 32, F32), (25216, 192, F32), (201728, 1536, F32), (201728, 768, F32),
+                        (201728, 3072, BF16), (2 * 201728, 3072, BF16)):
+        assert 0 < ws(lib, rows, d, 8, io) <= 16 << 20
