@@ -14,7 +14,13 @@ Prints one JSON line.  `value` is elements per second of the whole step
 rates the dominant kernel -- the backward call (main kernel + merge) -- by
 its algorithmic bytes (read x and dy, write dx: 12 B per fp32 element) over
 its average duration in a loop of K back-to-back backward calls, timed with
-HIP events on the stream it runs on.
+HIP events on the stream it runs on.  Workloads whose tensors would fit the
+256 MB Infinity Cache (KAT-T: 58 MB per backward) rotate copies of their
+inputs in distinct buffers, call by call, so that every call streams from
+HBM; a second timing with the cache flushed before each call (a 512 MB write
+outside the events) cross-checks it.  `detail.stream_probe_GBps` is the
+measured ceiling of the backward's traffic: grkan_stream_probe (two reads,
+one write, no arithmetic) over the same buffers.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
 workload.  `detail` adds the forward's figures, the atomic-mode and naive
 per-element-atomic backward times, the rounding error of each backward
@@ -37,6 +43,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache
+MALL_DEFEAT_BYTES = 8 * MALL_BYTES  # rotated input sets hold at least this much
+MAX_SETS = 64
+FLUSH_BYTES = 2 * MALL_BYTES  # read before each call of the flushed cross-check
 PROFILES = os.path.join(ROOT, "profiles")
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
@@ -68,38 +78,63 @@ def error_stats(got: np.ndarray, ref: np.ndarray) -> dict:
     return {"mae": float(np.mean(np.abs(e))), "var": float(np.var(e)), "max_rel": float(np.max(rel))}
 
 
+def host_info() -> dict:
+    """The host the CPU baseline ran on: logical CPUs, the ones this process may use, the CPU
+    share declared through OMP_NUM_THREADS, and the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    return {"nproc": os.cpu_count(), "affinity": affinity,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"), "cpu_model": model}
+
+
 def cpu_baseline(w, target_s: float = 10.0) -> dict:
-    """fp64 oracle (forward + backward of every element) on the first rows of the workload."""
+    """The fp64 oracle, as it is, on the first rows of the workload: the forward alone (Y) and
+    the forward + backward (Y, dX, dA, dB: the oracle evaluates each element's value and
+    derivatives together), timed separately on the same rows, on the host's CPU share; and the
+    same forward + backward on one thread on a smaller sample."""
     from gr_kan_rational_amd import synth
     from oracle import oracle
 
-    calib_rows = 256
-    inp = synth.make_inputs(w, rows=calib_rows)
-    t0 = time.perf_counter()
-    oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io, m=w.m, n=w.n)
-    dt = time.perf_counter() - t0
+    def run(inp, with_dy, nthreads=None):
+        t0 = time.perf_counter()
+        oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"] if with_dy else None, io=w.io,
+                   m=w.m, n=w.n, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    calib_rows = min(256, w.rows)
+    dt = run(synth.make_inputs(w, rows=calib_rows), True)
     rows = int(min(w.rows, max(calib_rows, calib_rows * target_s / max(dt, 1e-3))))
     inp = synth.make_inputs(w, rows=rows)
-    t0 = time.perf_counter()
-    oracle.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io, m=w.m, n=w.n)
-    dt = time.perf_counter() - t0
+    run(inp, True)  # first touch of the output buffers' pages, outside the timing
+    # a workload the oracle finishes in well under a second (tiny) is repeated until ~1 s
+    reps = max(1, int(1.0 / max(run(inp, True), 1e-6))) if rows == w.rows else 1
+    dt = sum(run(inp, True) for _ in range(reps)) / reps
+    dt_fwd = sum(run(inp, False) for _ in range(reps)) / reps
     n = rows * w.d
-    # the same oracle on one thread, on a sample sized to ~a quarter of target_s
-
-    def one_thread(r):
-        i1 = synth.make_inputs(w, rows=r)
-        t = time.perf_counter()
-        oracle.run(i1["x"], i1["A"], i1["B"], w.n_groups, dy=i1["dy"], io=w.io, m=w.m, n=w.n, nthreads=1)
-        return time.perf_counter() - t
-
     c1 = min(rows, calib_rows)
-    rows1 = int(min(rows, max(c1, c1 * target_s / 4 / max(one_thread(c1), 1e-3))))
-    dt1 = one_thread(rows1)
+    rows1 = int(min(rows, max(c1, c1 * target_s / 4 / max(run(synth.make_inputs(w, rows=c1), True, 1), 1e-3))))
+    inp1 = synth.make_inputs(w, rows=rows1)
+    reps1 = max(1, int(0.5 / max(run(inp1, True, 1), 1e-6))) if rows1 == w.rows else 1
+    dt1 = sum(run(inp1, True, 1) for _ in range(reps1)) / reps1
     return {"value": n / dt, "unit": "elements/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"first {rows} of {w.rows} rows ({n} elements) of {w.name}, forward + backward "
-                      f"(Y, dX, dA, dB) in fp64, {dt:.1f} s wall",
+            "sample": f"first {rows} of {w.rows} rows ({n} elements) of {w.name}: forward + backward (Y, dX, dA, "
+                      f"dB) in fp64, {dt:.3g} s wall (mean of {reps}); the forward alone (Y) on the same rows "
+                      f"{dt_fwd:.3g} s",
+            "forward_value": n / dt_fwd,
             "value_1_thread": rows1 * w.d / dt1,
-            "sample_1_thread": f"first {rows1} rows ({rows1 * w.d} elements), {dt1:.1f} s wall"}
+            "sample_1_thread": f"first {rows1} rows ({rows1 * w.d} elements), forward + backward, {dt1:.1f} s wall",
+            "host": host_info()}
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
@@ -127,7 +162,7 @@ def cpu_baseline_layer(w, target_s: float = 10.0) -> dict:
     flops = 3 * 2.0 * rows * w.d * w.d_out
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"first {rows} of {w.rows} rows of {w.name}: forward and backward, F in fp64 with bf16 "
-                      f"rounding, fp64 matrix products, {dt:.1f} s wall"}
+                      f"rounding, fp64 matrix products, {dt:.1f} s wall", "host": host_info()}
 
 
 def bench_layer(args, w, gk, synth, dev, log) -> int:
@@ -262,7 +297,7 @@ def cpu_baseline_cheby(w, target_s: float = 10.0) -> dict:
     flops = 3 * 2.0 * rows * w.d * (w.cheby + 1) * w.d_out
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": f"first {rows} of {w.rows} rows of {w.name}: forward and backward in fp64 (basis rounded "
-                      f"to bf16), {dt:.1f} s wall"}
+                      f"to bf16), {dt:.1f} s wall", "host": host_info()}
 
 
 def bench_cheby(args, w, gk, synth, dev, log) -> int:
@@ -420,8 +455,17 @@ def main() -> int:
     A = torch.from_numpy(inp["A"]).to(dev)
     B = torch.from_numpy(inp["B"]).to(dev) if w.n > 0 else None
     del inp
-    y = torch.empty_like(x)
-    dx = torch.empty_like(x)
+    E = w.elements
+    es = w.io_bytes
+    # Input sets, rotated call by call so that no call finds its operands in the 256 MB Infinity
+    # Cache (MALL) from the call before: one set when a set (x, dy, y, dx) is already far larger
+    # than that cache (KAT-B: 2.5 GB), else copies of the same inputs in distinct buffers until
+    # the sets together hold MALL_DEFEAT_BYTES (KAT-T: 28 sets of 77 MB).
+    set_bytes = 4 * E * es
+    n_sets = int(min(MAX_SETS, max(1, -(-MALL_DEFEAT_BYTES // set_bytes))))
+    sets = [(x, dy, torch.empty_like(x), torch.empty_like(x))]
+    for _ in range(n_sets - 1):
+        sets.append((x.clone(), dy.clone(), torch.empty_like(x), torch.empty_like(x)))
     dA = torch.empty((w.n_groups, w.m + 1), dtype=torch.float32, device=dev)
     dB = torch.empty((w.n_groups, w.n), dtype=torch.float32, device=dev) if w.n > 0 else None
     # GR-KAN itself (degrees (5, 4)) goes through the grkan_* entry points, the other
@@ -434,48 +478,69 @@ def main() -> int:
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def fwd():
+    def fwd(i=0):
+        xs, _, ys, _ = sets[i % n_sets]
         if pau:
-            gk.grkan_pau_forward(x, A, B, w.n_groups, w.m, w.n, out=y, stream=stream)
+            gk.grkan_pau_forward(xs, A, B, w.n_groups, w.m, w.n, out=ys, stream=stream)
         else:
-            gk.grkan_forward(x, A, B, w.n_groups, out=y, stream=stream)
+            gk.grkan_forward(xs, A, B, w.n_groups, out=ys, stream=stream)
 
-    def bwd(mode=args.mode):
+    def bwd(i=0, mode=args.mode):
+        xs, dys, _, dxs = sets[i % n_sets]
         if pau:
-            gk.grkan_pau_backward(x, dy, A, B, w.n_groups, w.m, w.n, mode=mode,
-                                  dx=dx, dA=dA, dB=dB, workspace=ws, stream=stream)
+            gk.grkan_pau_backward(xs, dys, A, B, w.n_groups, w.m, w.n, mode=mode,
+                                  dx=dxs, dA=dA, dB=dB, workspace=ws, stream=stream)
         else:
-            gk.grkan_backward(x, dy, A, B, w.n_groups, mode=mode,
-                              dx=dx, dA=dA, dB=dB, workspace=ws, stream=stream)
+            gk.grkan_backward(xs, dys, A, B, w.n_groups, mode=mode,
+                              dx=dxs, dA=dA, dB=dB, workspace=ws, stream=stream)
+
+    def probe(i=0):
+        xs, dys, _, dxs = sets[i % n_sets]
+        gk.grkan_stream_probe(xs, dys, out=dxs, stream=stream)
 
     def launch(pass_):
         if pau:
             return gk.grkan_pau_query_launch(w.rows, w.d, w.n_groups, w.m, w.n, io, pass_)
         return gk.grkan_query_launch(w.rows, w.d, w.n_groups, io, pass_)
 
-    log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
+    def step(i=0):
+        fwd(i)
+        bwd(i)
+
+    log(f"warmup {args.warmup} steps ({n_sets} input set(s) of {set_bytes / 1e6:.1f} MB)")
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
     def timed(fn, reps):
-        """Average duration (ms) of fn over reps back-to-back calls, bracketed by two HIP
-        events on the stream the kernels run on."""
+        """Average duration (ms) of fn over reps back-to-back calls (rotating the input sets),
+        bracketed by two HIP events on the stream the kernels run on."""
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
-        fn()  # first call outside the timing (loads the code object if not yet loaded)
+        fn(0)  # first call outside the timing (loads the code object if not yet loaded)
         torch.cuda.synchronize()
         t0.record(stream)
-        for _ in range(reps):
-            fn()
+        for i in range(reps):
+            fn(i + 1)
         t1.record(stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / reps
 
-    def step():
-        fwd()
-        bwd()
+    flush = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_sum = torch.empty((), dtype=torch.float32, device=dev)
+
+    def timed_flushed(fn, reps):
+        """Average duration (ms) of fn with the Infinity Cache flushed before each call (a read of
+        FLUSH_BYTES outside the events; a read leaves clean lines, so the call pays no write-back
+        of the flush itself): a cross-check of the rotation."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (e0, e1) in enumerate(ev):
+            torch.sum(flush, out=flush_sum)
+            e0.record(stream)
+            fn(i)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
 
     log(f"timing {args.steps} steps")
     wall0 = time.perf_counter()
@@ -484,32 +549,41 @@ def main() -> int:
     # Per-kernel averages for the roofline: the same calls, timed in their own back-to-back loops.
     bwd_ms = timed(bwd, args.steps)
     fwd_ms = timed(fwd, args.steps)
-    # Ceiling of this traffic mix on this device: a library elementwise kernel that reads two
-    # tensors of the workload's size and writes a third (what the backward moves).
-    z = torch.empty_like(x)
-    ceil_ms = timed(lambda: torch.add(x, dy, out=z), args.steps) if w.io == "f32" else None
-    del z
-    E = w.elements
-    es = w.io_bytes
+    # The measured ceiling of the backward's traffic (two tensors read, one written) on this
+    # device: the library's streaming probe over the same buffers.
+    probe_ms = timed(probe, args.steps)
+    bwd_ms_flushed = timed_flushed(bwd, min(args.steps, 20))
+    fwd_ms_flushed = timed_flushed(fwd, min(args.steps, 20))
+    del flush, flush_sum
     value = E / (ms_per_step * 1e-3)
     bwd_bytes = 3 * es * E
     fwd_bytes = 2 * es * E
     bwd_gbps = bwd_bytes / (bwd_ms * 1e-3) / 1e9
     fwd_gbps = fwd_bytes / (fwd_ms * 1e-3) / 1e9
-    log(f"step {ms_per_step:.4f} ms; fwd {fwd_ms:.4f} ms, bwd {bwd_ms:.4f} ms; wall {wall:.3f} s")
+    probe_gbps = bwd_bytes / (probe_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step:.4f} ms; fwd {fwd_ms:.4f} ms, bwd {bwd_ms:.4f} ms ({bwd_gbps:.0f} GB/s); "
+        f"stream probe {probe_ms:.4f} ms ({probe_gbps:.0f} GB/s); flushed fwd {fwd_ms_flushed:.4f} / "
+        f"bwd {bwd_ms_flushed:.4f} ms; wall {wall:.3f} s")
 
     detail = {
         "elements": E,
+        "input_sets": n_sets, "input_set_bytes": set_bytes,
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
         "fwd_GBps": fwd_gbps, "fwd_frac_hbm_peak": fwd_gbps / HBM_PEAK_GBPS,
         "bwd_GBps": bwd_gbps, "bwd_frac_hbm_peak": bwd_gbps / HBM_PEAK_GBPS,
         "fwdbwd_GBps": (fwd_bytes + bwd_bytes) / (ms_per_step * 1e-3) / 1e9,
-        "two_reads_one_write_ceiling_GBps": (bwd_bytes / (ceil_ms * 1e-3) / 1e9) if ceil_ms else None,
-        "bwd_frac_of_that_ceiling": (ceil_ms / bwd_ms) if ceil_ms else None,
+        "fwd_ms_flushed": fwd_ms_flushed, "bwd_ms_flushed": bwd_ms_flushed,
+        "stream_probe_ms": probe_ms, "stream_probe_GBps": probe_gbps,
+        "bwd_frac_of_stream_probe": probe_ms / bwd_ms,
         "launch_fwd": launch(0),
         "launch_bwd": launch(1),
         "device": torch.cuda.get_device_name(dev),
     }
+    # the rest uses the first set only
+    x, dy, y, dx = sets[0]
+    sets = sets[:1]
+    n_sets = 1
+    torch.cuda.empty_cache()
 
     # other backward modes, outside the timed region
     def time_one(fn, reps):
@@ -538,15 +612,15 @@ def main() -> int:
         return e
 
     other = "block_atomic" if args.mode == "deterministic" else "deterministic"
-    detail[f"bwd_{other}_ms"] = time_one(lambda: bwd(other), 10)
+    detail[f"bwd_{other}_ms"] = time_one(lambda: bwd(0, other), 10)
     for mode in ("deterministic", "block_atomic"):
-        bwd(mode)
+        bwd(0, mode)
         torch.cuda.synchronize()
         if ref is not None:
             errors[mode] = grad_errors()
     if not args.no_naive and not pau:
         log("naive per-element-atomic backward (one run)")
-        detail["bwd_naive_ms"] = time_one(lambda: bwd("naive"), 1)
+        detail["bwd_naive_ms"] = time_one(lambda: bwd(0, "naive"), 1)
         if ref is not None:
             errors["naive_per_element_atomic"] = grad_errors()
     if errors:

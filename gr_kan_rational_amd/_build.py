@@ -44,6 +44,7 @@ def units() -> list[tuple[str, list[str], str]]:
     out = [("grkan_api.hip", [], "grkan_api.o"),
            ("grkan_merge.hip", [], "grkan_merge.o"),
            ("grkan_layer.hip", [], "grkan_layer.o"),
+           ("grkan_probe.hip", [], "grkan_probe.o"),
            ("grkan_naive.hip", ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"], "grkan_naive.o")]
     for m, n in degree_pairs():
         out.append(("grkan_kernels.hip", [f"-DGRKAN_M={m}", f"-DGRKAN_N={n}"], f"grkan_kernels_{m}_{n}.o"))

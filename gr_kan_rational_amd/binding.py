@@ -60,6 +60,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grkan_forward.restype = ctypes.c_int
     lib.grkan_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, ctypes.c_int, u32, vp, sz, vp]
     lib.grkan_backward.restype = ctypes.c_int
+    lib.grkan_stream_probe.argtypes = [vp, vp, vp, i64, vp]
+    lib.grkan_stream_probe.restype = ctypes.c_int
     lib.grkan_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, ctypes.c_int, vp]
     lib.grkan_backward_noalloc.restype = ctypes.c_int
     lib.grkan_backward_workspace_size.argtypes = [i64, i64, i32, ctypes.c_int, u32]
@@ -280,6 +282,22 @@ def grkan_backward_noalloc(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B
 
 
 GRKAN_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def grkan_stream_probe(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """out = a XOR b over the tensors' bytes (``grkan_stream_probe``, the streaming ceiling
+    probe: two reads and one write per 16 bytes, as the backward moves)."""
+    if a.numel() * a.element_size() != b.numel() * b.element_size() or not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous tensors of the same byte size")
+    out = torch.empty_like(a) if out is None else out
+    nbytes = a.numel() * a.element_size()
+    if out.numel() * out.element_size() != nbytes or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of a's byte size")
+    st = load_library().grkan_stream_probe(_ptr(a), _ptr(b), _ptr(out), nbytes, ctypes.c_void_p(_stream(stream)))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_stream_probe")
+    return out
 
 
 def grkan_pau_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B, n_groups: int,

@@ -414,6 +414,19 @@ extern "C" grkan_status_t grkan_backward(const void *x, const void *dy, const fl
                          workspace, workspace_bytes, stream);
 }
 
+// --------------------------------------------------- streaming ceiling
+
+extern "C" grkan_status_t grkan_stream_probe(const void *a, const void *b, void *c, int64_t bytes,
+                                             hipStream_t stream) {
+    if (bytes < 0) return GRKAN_ERR_INVALID_ARG;
+    if (bytes == 0) return GRKAN_OK;
+    if (!a || !b || !c) return GRKAN_ERR_INVALID_ARG;
+    if (bytes % 16 != 0 || !aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16)) return GRKAN_ERR_UNSUPPORTED;
+    if (bad_alias(c, a, (size_t)bytes) || bad_alias(c, b, (size_t)bytes)) return GRKAN_ERR_INVALID_ARG;
+    // ---- validation done; HIP calls from here on
+    return from_hip(launch_stream_probe(a, b, c, bytes, stream));
+}
+
 // ------------------------------------------- backward without allocation
 //
 // For callers that cannot allocate (code under HIP graph capture, tight

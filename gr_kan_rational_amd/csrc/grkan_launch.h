@@ -170,6 +170,10 @@ hipError_t launch_cheby_g_dx(const void *dy, const void *Ct, const void *x, void
 // out [C][R] = in [R][C]^T, bf16.
 hipError_t launch_transpose16(const void *in, void *out, int64_t R, int64_t C, hipStream_t s);
 
+// Streaming ceiling probe (grkan_probe.hip): c = a XOR b over `bytes` bytes
+// (a multiple of 16; 16-byte aligned pointers; checked by the caller).
+hipError_t launch_stream_probe(const void *a, const void *b, void *c, int64_t bytes, hipStream_t s);
+
 // Per-element-atomic baseline, GR-KAN degrees only (grkan_naive.hip).
 hipError_t launch_naive(grkan_dtype_t io, const void *x, const void *dy, void *dx, const float *A,
                         const float *B, float *dA, float *dB, int64_t rows, int64_t d,

@@ -146,6 +146,19 @@ GRKAN_API size_t grkan_backward_workspace_size(int64_t rows, int64_t d, int32_t 
                                      grkan_dtype_t io, uint32_t flags);
 
 /*
+ * Streaming ceiling probe (a measurement tool, like grkan_inflated_*): c = a
+ * XOR b, word by word, over `bytes` bytes -- the backward's memory traffic
+ * (two tensors read, one written, 16-byte non-temporal accesses, one-shot
+ * grid) with no arithmetic to speak of.  Its rate is the ceiling the
+ * benchmark rates the backward against, next to the published HBM peak.
+ *   a, b, c   device buffers of `bytes` bytes, 16-byte aligned; c may equal a
+ *             or b exactly, any other overlap is GRKAN_ERR_INVALID_ARG.
+ *   bytes     >= 0 (0 is a no-op), a multiple of 16 (else UNSUPPORTED).
+ */
+GRKAN_API grkan_status_t grkan_stream_probe(const void *a, const void *b, void *c, int64_t bytes,
+                                  hipStream_t stream);
+
+/*
  * grkan_backward without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation).  The deterministic two-stage scheme of grkan_backward

@@ -101,12 +101,17 @@ def _lib():
 
 
 def threads() -> int:
-    """Host threads the oracle uses: the CPUs this process may run on, at most 16."""
+    """Host threads the oracle uses: the CPU share the machine declares for this process through
+    OMP_NUM_THREADS when it sets one (a shared GPU host allots each GPU's jobs a share of its
+    cores), else every CPU this process may run on."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    if share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return max(1, n)
 
 
 def _ptr(a):

@@ -43,7 +43,7 @@ def test_header_declares_the_abi():
         "grkan_inflated_forward", "grkan_inflated_backward",
         "grkan_layer_forward", "grkan_linear_forward", "grkan_layer_backward",
         "grkan_layer_backward_workspace_size", "grkan_chebykan_forward", "grkan_chebykan_backward",
-        "grkan_chebykan_backward_workspace_size", "grkan_backward_noalloc"])
+        "grkan_chebykan_backward_workspace_size", "grkan_backward_noalloc", "grkan_stream_probe"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -422,3 +422,15 @@ def test_noalloc_covers_the_gr_kan_workloads(lib):
     for rows, d, io in ((16, 32, F32), (25216, 192, F32), (201728, 1536, F32), (201728, 768, F32),
                         (201728, 3072, BF16), (2 * 201728, 3072, BF16)):
         assert 0 < ws(lib, rows, d, 8, io) <= 16 << 20
+
+
+# ------------------------------------------------------- streaming ceiling probe
+
+@pytest.mark.parametrize("args,code", [
+    ((P, P + 0x1000, P + 0x2000, -16), INVALID), ((None, P, P + 0x2000, 64), INVALID),
+    ((P, P + 0x1000, P + 0x2000, 24), UNSUPPORTED), ((P + 8, P + 0x1000, P + 0x2000, 64), UNSUPPORTED),
+    ((P, P + 0x1000, P + 16, 64), INVALID),      # c partially overlaps a
+    ((None, None, None, 0), OK),                 # empty: no HIP call
+])
+def test_stream_probe_validates_before_any_device_call(lib, args, code):
+    assert lib.grkan_stream_probe(*args, None) == code

@@ -422,3 +422,16 @@ def test_flags_zero_and_deterministic_are_the_same_call(gk):
     torch.cuda.synchronize()
     for a, b in zip(*out):
         assert torch.equal(_bits(a), _bits(b))
+
+
+def test_stream_probe_is_the_xor_of_its_inputs(gk):
+    """The streaming-ceiling probe the benchmark rates the backward against: c = a XOR b over
+    the whole byte range, including a ragged last workgroup, and in place."""
+    g = torch.Generator(device="cpu").manual_seed(5)
+    for n in (16, 4096 * 4 + 48, 201728 * 768):
+        a = torch.randint(-2**31, 2**31 - 1, (n,), dtype=torch.int32, generator=g).to(DEV)
+        b = torch.randint(-2**31, 2**31 - 1, (n,), dtype=torch.int32, generator=g).to(DEV)
+        c = gk.grkan_stream_probe(a, b)
+        assert torch.equal(c, a ^ b)
+        gk.grkan_stream_probe(a, b, out=a)
+        assert torch.equal(a, c)
