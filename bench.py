@@ -535,7 +535,7 @@ def main() -> int:
         of the flush itself): a cross-check of the rotation."""
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for i, (e0, e1) in enumerate(ev):
-            torch.sum(flush, out=flush_sum)
+            torch.sum(flush, dim=0, out=flush_sum)
             e0.record(stream)
             fn(i)
             e1.record(stream)
