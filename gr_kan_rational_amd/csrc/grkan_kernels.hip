@@ -62,13 +62,17 @@ constexpr int kMaxBlock = 1024;
 // per workgroup (all of a lane's loads are issued together).  Forward: 2
 // passes, 384-lane blocks.  The fp32 backward at GR-KAN-sized degrees: 2
 // passes, 384-lane blocks (292 us; 4 passes of 192 lanes -- the same 32-row
-// tiles -- 302 us, 2 x 192 303, 2 x 768 293, 3 x 384 295, 1 x 384 327).  The
-// bf16 backward, which is bound by its arithmetic rather than by memory, and
-// high-degree fp32 backwards, which need more registers per element: 2 passes,
-// 192-lane blocks.
+// tiles -- 302 us, 2 x 192 303, 2 x 768 293, 3 x 384 295, 1 x 384 327; 4 x 384
+// with the passes kept apart 626 against 599 us at KAT-S hidden).  High-degree
+// fp32 backwards, which need more registers per element: 2 passes, 192-lane
+// blocks.  The bf16 backward, which is bound by its arithmetic rather than by
+// memory: 4 passes of 192 lanes (32 elements per lane, so the per-lane work of
+// the reduction and set-up is spread over twice as many elements: 749 against
+// 771 us at KAT-B hidden), its passes kept apart by a scheduling barrier (80
+// VGPRs; 62 at 2 passes, 88 without the barrier).
 template <class IO> constexpr bool is_f32() { return __is_same(IO, float); }
 template <class IO, int M, int N> constexpr int fwd_unroll() { return 2; }
-template <class IO, int M, int N> constexpr int bwd_unroll() { return 2; }
+template <class IO, int M, int N> constexpr int bwd_unroll() { return is_f32<IO>() ? 2 : 4; }
 template <class IO, int M, int N> constexpr bool bwd_wide_block() { return is_f32<IO>() && M + N <= 9; }
 constexpr int kFwdBlock = 384;
 constexpr int kBwdBlock = 192;

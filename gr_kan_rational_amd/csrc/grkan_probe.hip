@@ -18,41 +18,49 @@ constexpr int64_t kProbeChunk = (int64_t)kProbeBlock * kProbeUnroll * 16;  // by
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kProbeBlock) void grkan_stream_probe_kernel(const u32x4 *__restrict__ a,
-                                                                         const u32x4 *__restrict__ b,
-                                                                         u32x4 *__restrict__ c, int64_t nvec,
+__global__ __launch_bounds__(kProbeBlock) void grkan_stream_probe_kernel(const char *__restrict__ a,
+                                                                         const char *__restrict__ b,
+                                                                         char *__restrict__ c, int64_t bytes,
                                                                          int64_t block0) {
-    // workgroup w covers vectors [w * 1024, (w + 1) * 1024): lane l takes
-    // vectors l, l + 256, l + 512, l + 768 of it, so each wave reads whole
-    // 1 KB runs per access
-    const int64_t base = (block0 + (int64_t)blockIdx.x) * (kProbeBlock * kProbeUnroll) + threadIdx.x;
-    u32x4 va[kProbeUnroll], vb[kProbeUnroll];
+    // workgroup w covers bytes [w * kProbeChunk, (w + 1) * kProbeChunk): lane l
+    // takes the 16-byte vectors l, l + 256, l + 512, l + 768 of it, so each
+    // wave reads whole 1 KB runs per access; all loads are issued before the
+    // first store, and only the last, ragged workgroup checks bounds
+    const int64_t base = (block0 + (int64_t)blockIdx.x) * kProbeChunk;
+    const u32x4 *pa = reinterpret_cast<const u32x4 *>(a + base);
+    const u32x4 *pb = reinterpret_cast<const u32x4 *>(b + base);
+    u32x4 *pc = reinterpret_cast<u32x4 *>(c + base);
+    const int64_t avail = bytes - base;
+    const int t = (int)threadIdx.x;
+    if (avail >= kProbeChunk) {
+        u32x4 va[kProbeUnroll], vb[kProbeUnroll];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) {
-        const int64_t i = base + (int64_t)u * kProbeBlock;
-        if (i < nvec) {
-            va[u] = __builtin_nontemporal_load(a + i);
-            vb[u] = __builtin_nontemporal_load(b + i);
+        for (int u = 0; u < kProbeUnroll; ++u) {
+            va[u] = __builtin_nontemporal_load(pa + t + u * kProbeBlock);
+            vb[u] = __builtin_nontemporal_load(pb + t + u * kProbeBlock);
         }
-    }
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) {
-        const int64_t i = base + (int64_t)u * kProbeBlock;
-        if (i < nvec) __builtin_nontemporal_store(va[u] ^ vb[u], c + i);
+        for (int u = 0; u < kProbeUnroll; ++u) __builtin_nontemporal_store(va[u] ^ vb[u], pc + t + u * kProbeBlock);
+    } else {
+        const int nv = (int)(avail / 16);
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) {
+            const int i = t + u * kProbeBlock;
+            if (i < nv) __builtin_nontemporal_store(pa[i] ^ pb[i], pc + i);
+        }
     }
 }
 
 }  // namespace
 
 hipError_t launch_stream_probe(const void *a, const void *b, void *c, int64_t bytes, hipStream_t s) {
-    const int64_t nvec = bytes / 16;
     const int64_t blocks = (bytes + kProbeChunk - 1) / kProbeChunk;
     const int64_t per_launch = ((int64_t(1) << 32) - 1) / kProbeBlock;  // work-items below 2^32
     for (int64_t b0 = 0; b0 < blocks; b0 += per_launch) {
         const int64_t nb = blocks - b0 < per_launch ? blocks - b0 : per_launch;
         hipLaunchKernelGGL(grkan_stream_probe_kernel, dim3((unsigned)nb), dim3(kProbeBlock), 0, s,
-                           static_cast<const u32x4 *>(a), static_cast<const u32x4 *>(b),
-                           static_cast<u32x4 *>(c), nvec, b0);
+                           static_cast<const char *>(a), static_cast<const char *>(b), static_cast<char *>(c),
+                           bytes, b0);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -169,8 +169,9 @@ GRKAN_API grkan_status_t grkan_stream_probe(const void *a, const void *b, void *
  *   Arguments and errors as grkan_backward (no flags, no workspace); a shape
  *   whose partial sums need more than GRKAN_NOALLOC_SCRATCH_BYTES (what
  *   grkan_backward_workspace_size() reports for it) is GRKAN_ERR_UNSUPPORTED,
- *   before any HIP call.  16 MiB covers every GR-KAN shape up to twice the
- *   KAT-B hidden activations in bf16 (8.1 MB there).
+ *   before any HIP call.  16 MiB covers the partial sums of every GR-KAN
+ *   shape up to four times the KAT-B hidden activations in bf16 (4.0 MB
+ *   there, as at KAT-S hidden in fp32).
  *   Calls on one device share the array and must not overlap in time (e.g.
  *   run on different streams without ordering): they would race on it.
  *   Nothing in it needs to start at zero -- every partial sum is written
