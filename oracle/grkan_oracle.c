@@ -191,6 +191,12 @@ static int sign_q_exact(double x, int n, const double *b)
  * so the factor below leaves a wide margin. */
 static int sign_q(double x, int n, const double *b, double q, double qabs)
 {
+    /* Non-finite x, or terms that overflow fp64 (|x| beyond ~1e300 / |b|):
+     * no exact evaluation exists; the sign is IEEE's, that of q (0 for NaN),
+     * and the outputs propagate as IEEE arithmetic does (the pages are
+     * silent on such inputs). */
+    if (!isfinite(q) || !isfinite(qabs))
+        return sign_of(q);
     if (fabs(q) > (8.0 * n + 16.0) * DBL_EPSILON * qabs)
         return sign_of(q);
     return sign_q_exact(x, n, b);

@@ -414,3 +414,24 @@ def test_bf16_decode_is_exact():
     bits = np.array([0x3F80, 0xC000, 0x3EAB, 0x0000, 0x8000], dtype=np.uint16)
     v = orc.to_f64(bits, "bf16")
     assert list(v[:3]) == [1.0, -2.0, 0.333984375] and v[3] == 0.0 and math.copysign(1, v[4]) == -1
+
+
+def test_non_finite_inputs_propagate_as_ieee():
+    """NaN and +-inf inputs, and |x| so large that the terms overflow fp64: the oracle returns
+    (it does not attempt an exact sign it cannot form) and the outputs are IEEE's -- NaN in, NaN
+    out; a finite element next to them is unaffected (its own record only)."""
+    rng = np.random.default_rng(3)
+    a = rng.standard_normal(6) * 0.5
+    b = rng.standard_normal(4) * 0.5
+    rec = orc.point(float("nan"), 1.0, a, b)
+    assert math.isnan(rec[orc.F]) and math.isnan(rec[orc.DX])
+    assert all(math.isnan(v) for v in rec[orc.T:orc.T + 10])
+    rec = orc.point(1.0, float("nan"), a, b)
+    assert math.isnan(rec[orc.DX]) and not math.isnan(rec[orc.F])
+    for x in (float("inf"), float("-inf"), 1e300, -1e300):
+        rec = orc.point(x, 1.0, a, b)
+        assert not math.isfinite(rec[orc.F]) or not math.isfinite(rec[orc.DX])
+    ok = orc.point(0.5, 1.0, a, b)
+    P = sum(a[i] * 0.5 ** i for i in range(6))
+    Q = sum(b[j] * 0.5 ** (j + 1) for j in range(4))
+    assert ok[orc.F] == pytest.approx(P / (1 + abs(Q)), rel=1e-15)
