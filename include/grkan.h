@@ -66,7 +66,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations are ints (as every C enum is); under C++ they are given
+ * that underlying type explicitly, so that any int a C caller passes -- an
+ * unknown status or dtype included -- is a valid value to test and reject. */
+#ifdef __cplusplus
+#define GRKAN_ENUM_INT : int
+#else
+#define GRKAN_ENUM_INT
+#endif
+
+typedef enum GRKAN_ENUM_INT {
     GRKAN_OK = 0,
     GRKAN_ERR_INVALID_ARG = 1, /* null pointer, bad shape, overlap, small workspace, bad flags */
     GRKAN_ERR_UNSUPPORTED = 2, /* misaligned pointer, d/n_groups*bytes(io) not a multiple of 16,
@@ -74,7 +83,7 @@ typedef enum {
     GRKAN_ERR_HIP = 3          /* the HIP runtime reported an error on query or launch          */
 } grkan_status_t;
 
-typedef enum {
+typedef enum GRKAN_ENUM_INT {
     GRKAN_F32 = 0,  /* fp32 x, y, dy, dx                                   */
     GRKAN_BF16 = 1  /* bf16 x, y, dy, dx; outputs rounded to nearest even  */
 } grkan_dtype_t;
