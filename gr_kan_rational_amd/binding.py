@@ -89,6 +89,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.grkan_inflated_backward.restype = ctypes.c_int
     lib.grkan_layer_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp]
     lib.grkan_layer_forward.restype = ctypes.c_int
+    lib.grkan_layer_forward_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+    lib.grkan_layer_forward_ws.restype = ctypes.c_int
+    lib.grkan_layer_forward_workspace_size.argtypes = [i64, i64, i64, i32]
+    lib.grkan_layer_forward_workspace_size.restype = sz
     lib.grkan_linear_forward.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.grkan_linear_forward.restype = ctypes.c_int
     lib.grkan_layer_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
@@ -349,6 +353,30 @@ def grkan_layer_forward(x: torch.Tensor, A: torch.Tensor, B: torch.Tensor, W: to
                                             d_out, n_groups, ctypes.c_void_p(_stream(stream)))
     if st != GRKAN_OK:
         raise GRKANError(st, "grkan_layer_forward")
+    return z
+
+
+def grkan_layer_forward_workspace_size(rows: int, d_in: int, d_out: int, n_groups: int = 8) -> int:
+    return int(load_library().grkan_layer_forward_workspace_size(rows, d_in, d_out, n_groups))
+
+
+def grkan_layer_forward_ws(x: torch.Tensor, A: torch.Tensor, B: torch.Tensor, W: torch.Tensor,
+                           n_groups: int = 8, out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """z = F(x) W^T by ``grkan_layer_forward_ws``: the fused or the unfused form, whichever the
+    library takes for the shape (same bits); the workspace is allocated here when not given."""
+    _check_coefs(A, B, n_groups, x.device)
+    rows, d_in, d_out, z = _layer_out(x, W, out)
+    lib = load_library()
+    need = lib.grkan_layer_forward_workspace_size(rows, d_in, d_out, n_groups)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wsp = _ptr(workspace) if workspace is not None else None
+    wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.grkan_layer_forward_ws(_ptr(x), _ptr(A), _ptr(B), _ptr(W), _ptr(z), rows, d_in, d_out, n_groups,
+                                    wsp, wsn, ctypes.c_void_p(_stream(stream)))
+    if st != GRKAN_OK:
+        raise GRKANError(st, "grkan_layer_forward_ws")
     return z
 
 

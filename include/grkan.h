@@ -298,6 +298,27 @@ GRKAN_API grkan_status_t grkan_layer_forward(const void *x, const float *A, cons
                                    int64_t d_out, int32_t n_groups, hipStream_t stream);
 
 /*
+ * grkan_layer_forward with a workspace, which lets the library take the
+ * faster form for the shape: the fused form evaluates F again for every
+ * 256-column tile of z, so for d_out > 256 F is evaluated once into the
+ * workspace (bf16 [rows][d_in], as the fused form rounds it) and the plain
+ * matrix product follows -- the same bits either way.  Arguments and limits
+ * as grkan_layer_forward, plus
+ *   workspace  grkan_layer_forward_workspace_size() bytes (0 when the fused
+ *              form is taken; then it may be NULL), 16-byte aligned, not
+ *              overlapping any other argument; contents on entry do not matter.
+ */
+GRKAN_API grkan_status_t grkan_layer_forward_ws(const void *x, const float *A, const float *B,
+                                      const void *W, void *z, int64_t rows, int64_t d_in,
+                                      int64_t d_out, int32_t n_groups, void *workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace grkan_layer_forward_ws needs (0 when it takes the fused
+ * form, for rows == 0, or for arguments it would reject).  Host-only. */
+GRKAN_API size_t grkan_layer_forward_workspace_size(int64_t rows, int64_t d_in, int64_t d_out,
+                                          int32_t n_groups);
+
+/*
  * The same linear map without the activation: z = y W^T, bf16 y [rows][d_in]
  * (16-byte aligned), W and z as above, the same matrix-core kernel and
  * limits.  With y = grkan_forward(x) (bf16) it is the unfused form of

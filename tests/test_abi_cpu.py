@@ -43,7 +43,8 @@ def test_header_declares_the_abi():
         "grkan_inflated_forward", "grkan_inflated_backward",
         "grkan_layer_forward", "grkan_linear_forward", "grkan_layer_backward",
         "grkan_layer_backward_workspace_size", "grkan_chebykan_forward", "grkan_chebykan_backward",
-        "grkan_chebykan_backward_workspace_size", "grkan_backward_noalloc", "grkan_stream_probe"])
+        "grkan_chebykan_backward_workspace_size", "grkan_backward_noalloc", "grkan_stream_probe",
+        "grkan_layer_forward_ws", "grkan_layer_forward_workspace_size"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -434,3 +435,28 @@ def test_noalloc_covers_the_gr_kan_workloads(lib):
 ])
 def test_stream_probe_validates_before_any_device_call(lib, args, code):
     assert lib.grkan_stream_probe(*args, None) == code
+
+
+# ------------------------------------------------------ layer forward with a workspace
+
+def test_layer_forward_workspace_size(lib):
+    # the unfused form (one bf16 copy of F(x)) beyond one 256-column tile of z, else none
+    assert lib.grkan_layer_forward_workspace_size(201728, 768, 3072, 8) == 201728 * 768 * 2
+    assert lib.grkan_layer_forward_workspace_size(201728, 3072, 768, 8) == 201728 * 3072 * 2
+    assert lib.grkan_layer_forward_workspace_size(1000, 768, 256, 8) == 0
+    assert lib.grkan_layer_forward_workspace_size(0, 768, 3072, 8) == 0
+    assert lib.grkan_layer_forward_workspace_size(1000, 100, 3072, 8) == 0   # rejected shape
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws_bytes=100), INVALID), (dict(ws_ptr=None), INVALID), (dict(ws_ptr=P + 0x700008), UNSUPPORTED),
+    (dict(ws_ptr=P + 64), INVALID),                   # workspace overlaps x
+    (dict(A=None), INVALID), (dict(z=P + 0x600002 + 1), UNSUPPORTED), (dict(d_in=100), UNSUPPORTED),
+])
+def test_layer_forward_ws_rejects(lib, kw, code):
+    args = dict(x=P, A=P + 0x200000, B=P + 0x300000, W=P + 0x400000, z=P + 0x600000, rows=64, d_in=64,
+                d_out=512, n_g=8, ws_ptr=P + 0x700000, ws_bytes=1 << 20)
+    args.update(kw)
+    assert lib.grkan_layer_forward_ws(args["x"], args["A"], args["B"], args["W"], args["z"], args["rows"],
+                                      args["d_in"], args["d_out"], args["n_g"], args["ws_ptr"], args["ws_bytes"],
+                                      None) == code

@@ -69,6 +69,25 @@ def test_layer_parity(gk, shape):
     assert torch.equal(z.view(torch.int16), z2.view(torch.int16)), "fused and unfused differ"
 
 
+@pytest.mark.parametrize("shape", [(301, 256, 8, 320), (257, 512, 64, 640), (300, 768, 8, 256), (64, 64, 8, 48)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_layer_forward_ws_takes_either_form_with_the_same_bits(gk, shape):
+    """grkan_layer_forward_ws (the unfused form beyond 256 output columns, else the fused one)
+    gives grkan_layer_forward's bits, and the oracle's values."""
+    rows, d_in, n_g, d_out = shape
+    inp = inputs(rows, d_in, n_g, d_out, 6100 + rows)
+    x, W = bf(inp["x"]), bf(inp["W"])
+    A, B = torch.from_numpy(inp["A"]).to(DEV), torch.from_numpy(inp["B"]).to(DEV)
+    need = gk.grkan_layer_forward_workspace_size(rows, d_in, d_out, n_g)
+    assert (need > 0) == (d_out > 256)
+    z = gk.grkan_layer_forward(x, A, B, W, n_g)
+    z2 = gk.grkan_layer_forward_ws(x, A, B, W, n_g)
+    torch.cuda.synchronize()
+    assert torch.equal(z.view(torch.int16), z2.view(torch.int16))
+    parity.check_layer(f"layer_ws {shape}", host(z2), layer.forward(inp["x"], inp["A"], inp["B"], inp["W"], n_g),
+                       d_in)
+
+
 @pytest.mark.parametrize("shape", [(301, 256, 272), (300, 3072, 768), (64, 64, 33)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_linear_parity(gk, shape):
