@@ -29,7 +29,7 @@ namespace {
 
 struct DegreeOps {
     int m, n;
-    int (*unroll)(grkan_dtype_t, int);
+    int (*unroll)(grkan_dtype_t, int, bool);
     int (*target_block)(grkan_dtype_t, int, bool);
     hipError_t (*forward)(grkan_dtype_t, const FwdArgs &, int, dim3, hipStream_t);
     hipError_t (*backward)(grkan_dtype_t, const BwdArgs &, int, dim3, hipStream_t);
@@ -154,7 +154,13 @@ grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, const Degre
         }
         if (rpi == 0) rpi = target / (int)seg_vecs > 0 ? target / (int)seg_vecs : 1;
     }
-    const int u = deg.unroll(io, pass);
+    int u = deg.unroll(io, pass, false);
+    {
+        // fewer passes for small grids (see kSmallGrid)
+        const int64_t tiles0 = (rows + (int64_t)u * rpi - 1) / ((int64_t)u * rpi);
+        const int64_t grid0 = 8 * parts * n_groups * ((tiles0 + 7) / 8);
+        if (grid0 < kSmallGrid) u = deg.unroll(io, pass, true);
+    }
     if ((int64_t)u * rpi * row_bytes > kMaxLaneSpan) return GRKAN_ERR_UNSUPPORTED;
     *P = Plan{};
     P->kind = kSegment;

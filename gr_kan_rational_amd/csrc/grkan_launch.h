@@ -110,7 +110,8 @@ struct BwdArgs {
 // whose kernels exist for GR-KAN's degrees (5, 4) and segment plans only
 // (forward / backward return hipErrorInvalidValue for anything else).
 template <int M, int N> struct Kernels {
-    static int unroll(grkan_dtype_t io, int pass);
+    // passes per tile; `small`: the count for grids under kSmallGrid workgroups
+    static int unroll(grkan_dtype_t io, int pass, bool small);
     static int target_block(grkan_dtype_t io, int pass, bool atomic_mode);
     static hipError_t forward(grkan_dtype_t io, const FwdArgs &a, int repeat, dim3 grid, hipStream_t s);
     static hipError_t backward(grkan_dtype_t io, const BwdArgs &a, int repeat, dim3 grid, hipStream_t s);
@@ -119,6 +120,11 @@ template <int M, int N> struct Kernels {
     // batches per tile.
     static void narrow_shape(grkan_dtype_t io, int pass, int *row_lanes, int *unroll, int *iters);
 };
+
+// Segment plans whose grid at the usual pass count has fewer workgroups than
+// this take the kernels' small-grid pass count (a function of the shape only,
+// so the summation order is still the same on every device).
+constexpr int64_t kSmallGrid = 4096;
 
 // Degree pairs compiled into the library: (m, n) with a_0..a_m, b_1..b_n.
 // GR-KAN's (5, 4) first.

@@ -102,8 +102,10 @@ def test_workspace_size(lib):
     assert ws(lib, 201728, 768, 8) == 8 * 10 * 6304 * 4
     assert ws(lib, 16, 32, 8) == 8 * 10 * 8 * 4             # tiny: a single tile, 8 slots
     assert ws(lib, 201728, 3072, 8, io=BF16) == 8 * 10 * 12608 * 4 + 8 * 10 * 2 * 8  # 4 rows x 4 passes
-    assert ws(lib, 1000, 768, 8) == 8 * 10 * 32 * 4         # 32 tiles of 32 rows (the last ragged)
-    assert ws(lib, 1025, 768, 8) == 8 * 10 * 40 * 4         # 33 tiles -> 40 slots
+    # small grids (under 4096 workgroups at 2 passes) take 1 pass: 16-row tiles
+    assert ws(lib, 1000, 768, 8) == 8 * 10 * 64 * 4         # 63 tiles of 16 rows (the last ragged) -> 64 slots
+    assert ws(lib, 1025, 768, 8) == 8 * 10 * 72 * 4         # 65 tiles -> 72 slots
+    assert ws(lib, 25216, 192, 8) == 8 * 10 * 400 * 4       # KAT-T: 394 tiles of 64 rows -> 400 slots
     assert ws(lib, 201728, 768, 8, flags=BLOCK) == 0        # atomic modes need none
     assert ws(lib, 201728, 768, 8, flags=NAIVE) == 0
     assert ws(lib, 100, 770, 8) == 0                        # d % n_g != 0: rejected
