@@ -243,15 +243,23 @@ __device__ static inline double widen_exact(float f) {
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// Constants of the backward pass derived from one group's coefficients.
+// Constants of the backward pass derived from one group's coefficients:
+// the fp32 ones (BwdCoefs) and b_1..b_N in fp64 (QWide, exact copies, for Q).
+// Two objects rather than one: with the fp64 array inside, BwdCoefs outgrows
+// 128 bytes at degrees (6, 5) and (7, 6), and hipcc then keeps the gradient
+// sums as separate scalars instead of one register vector, which costs those
+// kernels 40-60 VGPRs (62 -> 110 and 66 -> 122 at fp32) and the bf16 (7, 6)
+// kernel scratch spills.
 template <int M, int N> struct BwdCoefs {
     float a[M + 1];              // a_0..a_M
     float da[M > 0 ? M : 1];     // i * a_i, i = 1..M   (P')
     float b[N > 0 ? N : 1];      // b_1..b_N
     float db[N > 0 ? N : 1];     // j * b_j, j = 1..N   (Q')
-    double bd[N > 0 ? N : 1];    // b_1..b_N in fp64 (exact), for Q
     float kguard;                // sign guard scale, see below
     bool q_zero;                 // b = 0 (or N = 0): Q vanishes identically, s = 0
+};
+template <int N> struct QWide {
+    double b[N > 0 ? N : 1];     // b_1..b_N
 };
 
 // The sign guard.  The backward's Q is x q(x) by Horner's rule in fp64,
@@ -266,10 +274,7 @@ template <int M, int N> struct BwdCoefs {
 // for NaN or huge x; those elements take the exact path.
 template <int N> constexpr float sign_guard_scale() { return (float)(N + 4) / 2097152.0f; }
 
-// UNIFORM: the coefficients are the same in every lane (scalar registers), so
-// their fp64 copies are formed on the scalar unit; otherwise (per-lane
-// coefficients) by the vector conversion.
-template <int M, int N, bool UNIFORM = true>
+template <int M, int N>
 __device__ static inline BwdCoefs<M, N> derive(const Coefs<M, N> &c) {
     BwdCoefs<M, N> k;
 #pragma unroll
@@ -285,7 +290,6 @@ __device__ static inline BwdCoefs<M, N> derive(const Coefs<M, N> &c) {
     for (int j = 0; j < N; ++j) {
         k.b[j] = c.b[j];
         k.db[j] = (float)(j + 1) * c.b[j];
-        k.bd[j] = UNIFORM ? widen_exact(c.b[j]) : (double)c.b[j];
         bsum += fabsf(c.b[j]);
         nonzero |= __float_as_uint(c.b[j]) << 1;
     }
@@ -293,11 +297,22 @@ __device__ static inline BwdCoefs<M, N> derive(const Coefs<M, N> &c) {
     if constexpr (N == 0) {
         k.b[0] = 0.0f;
         k.db[0] = 0.0f;
-        k.bd[0] = 0.0;
     }
     k.kguard = sign_guard_scale<N>() * bsum;
     k.q_zero = zero;
     return k;
+}
+
+// UNIFORM: the coefficients are the same in every lane (scalar registers), so
+// their fp64 copies are formed on the scalar unit; otherwise (per-lane
+// coefficients) by the vector conversion.
+template <int M, int N, bool UNIFORM = true>
+__device__ static inline QWide<N> widen(const Coefs<M, N> &c) {
+    QWide<N> q;
+#pragma unroll
+    for (int j = 0; j < N; ++j) q.b[j] = UNIFORM ? widen_exact(c.b[j]) : (double)c.b[j];
+    if constexpr (N == 0) q.b[0] = 0.0;
+    return q;
 }
 
 // sign of q(x) = b_1 + b_2 x + ... + b_N x^(N-1) by compensated Horner in
@@ -354,7 +369,8 @@ struct ElemBwd {
 };
 
 template <int M, int N, int K>
-__device__ static inline ElemBwd backward_element(const Pow<K> &X, float dy, const BwdCoefs<M, N> &k) {
+__device__ static inline ElemBwd backward_element(const Pow<K> &X, float dy, const BwdCoefs<M, N> &k,
+                                                  const QWide<N> &kw) {
     static_assert(K >= M && K >= N, "powers");
     const float x = X.p[K >= 1 ? 1 : 0];
     float P = k.a[0];
@@ -375,9 +391,9 @@ __device__ static inline ElemBwd backward_element(const Pow<K> &X, float dy, con
         e.sure = true;
     } else {
         const double xd = (double)x;
-        double qd = k.bd[N - 1];
+        double qd = kw.b[N - 1];
 #pragma unroll
-        for (int j = N - 2; j >= 0; --j) qd = fma(qd, xd, k.bd[j]);
+        for (int j = N - 2; j >= 0; --j) qd = fma(qd, xd, kw.b[j]);
         const float Q = (float)(xd * qd);
         float Qd = k.db[0];
 #pragma unroll
@@ -410,11 +426,11 @@ __device__ static inline void accumulate(float w, float sv, const Pow<K> &X,
 // s = sign(x) sign(q(x)) exactly (0 at x == 0), replaces the dB terms that
 // were accumulated with the fp32 sign and returns the exact dX.
 template <int M, int N>
-__device__ static inline float exact_fix(float x, float dy, const BwdCoefs<M, N> &k,
+__device__ static inline float exact_fix(float x, float dy, const BwdCoefs<M, N> &k, const QWide<N> &kw,
                                          float (&acc)[Deg<M, N>::kNumCoef]) {
     constexpr int K = Deg<M, N>::kTop;
     const Pow<K> X(x);
-    const ElemBwd e = backward_element<M, N, K>(X, dy, k);
+    const ElemBwd e = backward_element<M, N, K>(X, dy, k, kw);
     if constexpr (N == 0) {
         return e.dx;
     } else {
@@ -433,8 +449,9 @@ __device__ static inline float exact_fix(float x, float dy, const BwdCoefs<M, N>
 // dX are recomputed with it.  Bit for bit equal to backward_element wherever
 // the guard holds.
 template <int M, int N, int K>
-__device__ static inline ElemBwd exact_element(const Pow<K> &X, float dy, const BwdCoefs<M, N> &k) {
-    ElemBwd e = backward_element<M, N, K>(X, dy, k);
+__device__ static inline ElemBwd exact_element(const Pow<K> &X, float dy, const BwdCoefs<M, N> &k,
+                                               const QWide<N> &kw) {
+    ElemBwd e = backward_element<M, N, K>(X, dy, k, kw);
     if constexpr (N > 0) {
         if (!e.sure) {
             const float x = X.p[1];

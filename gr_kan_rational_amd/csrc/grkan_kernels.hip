@@ -172,7 +172,7 @@ __device__ static inline void burn_forward(float x, const Coefs<M, N> &c) {
 }
 
 template <int M, int N, int K, int R, bool QZERO>
-__device__ static inline void burn_backward(float x, float dy, const BwdCoefs<M, N> &k) {
+__device__ static inline void burn_backward(float x, float dy, const BwdCoefs<M, N> &k, const QWide<N> &kw) {
 #pragma unroll
     for (int r = 1; r < R; ++r) {
         const Pow<K> X(opaque(x));
@@ -182,7 +182,7 @@ __device__ static inline void burn_backward(float x, float dy, const BwdCoefs<M,
             for (int i = 2; i <= M; ++i) Pd = fmaf(k.da[i - 1], X.p[i - 1], Pd);
             asm volatile("" ::"v"(dy * Pd));
         } else {
-            const ElemBwd e = backward_element<M, N, K>(X, dy, k);
+            const ElemBwd e = backward_element<M, N, K>(X, dy, k, kw);
             asm volatile("" ::"v"(e.dx), "v"(e.w), "v"(e.sv), "v"(e.sure ? 1 : 0));
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -265,8 +265,8 @@ __device__ static inline void store_all(Span r, const Window &w, const u32x4 (&v
 
 template <class IO, int M, int N, int U, bool QZERO, int R = 1, bool WY = false>
 __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window &w,
-                                       const BwdCoefs<M, N> &k, float (&acc)[Deg<M, N>::kNumCoef],
-                                       Span ry = Span{}) {
+                                       const BwdCoefs<M, N> &k, const QWide<N> &kw,
+                                       float (&acc)[Deg<M, N>::kNumCoef], Span ry = Span{}) {
     using V = Io<IO>;
     constexpr int E = V::kElems;
     constexpr int K = Deg<M, N>::kTop;
@@ -289,7 +289,7 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
         V::unpack(din[u], dyf);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            if constexpr (R > 1) burn_backward<M, N, K, R, QZERO>(xf[e], dyf[e], k);
+            if constexpr (R > 1) burn_backward<M, N, K, R, QZERO>(xf[e], dyf[e], k, kw);
             const Pow<K> X(xf[e]);
             const float dy = dyf[e];
             if constexpr (QZERO) {
@@ -306,7 +306,7 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
                     yf[e] = P;
                 }
             } else {
-                const ElemBwd eb = backward_element<M, N, K>(X, dy, k);
+                const ElemBwd eb = backward_element<M, N, K>(X, dy, k, kw);
                 accumulate<M, N>(eb.w, eb.sv, X, acc);
                 dxf[u][e] = eb.dx;
                 if constexpr (WY) yf[e] = eb.F;
@@ -327,7 +327,7 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
                 V::unpack(win_reload16<true>(rx, w.lane + u * w.stride), xf);
                 V::unpack(win_reload16<true>(rdy, w.lane + u * w.stride), dyf);
 #pragma unroll
-                for (int e = 0; e < E; ++e) dxf[u][e] = exact_fix<M, N>(xf[e], dyf[e], k, acc);
+                for (int e = 0; e < E; ++e) dxf[u][e] = exact_fix<M, N>(xf[e], dyf[e], k, kw, acc);
             }
         }
     }
@@ -414,7 +414,9 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
     const Plan &P = a.plan;
     Pos p;
     if (!pos_of(P, a.bundle0, p)) return;
-    const BwdCoefs<M, N> k = derive<M, N>(load_coefs<M, N>(a.A, a.B, p.g));
+    const Coefs<M, N> c = load_coefs<M, N>(a.A, a.B, p.g);
+    const BwdCoefs<M, N> k = derive<M, N>(c);
+    const QWide<N> kw = widen<M, N>(c);
     const Window w = window_of<U>(P, p);
     const Span rx = make_span(at(a.x, w.base), w.avail);
     const Span rdy = make_span(at(a.dy, w.base), w.avail);
@@ -424,9 +426,9 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_bwd_kernel(BwdArgs a) {
     for (int i = 0; i < NC; ++i) acc[i] = 0.0f;
     const Span ry = WY ? make_span(at(a.y, w.base), w.avail) : Span{};
     if (k.q_zero) {
-        bwd_tile<IO, M, N, U, true, R, WY>(rx, rdy, rdx, w, k, acc, ry);
+        bwd_tile<IO, M, N, U, true, R, WY>(rx, rdy, rdx, w, k, kw, acc, ry);
     } else {
-        if constexpr (N > 0) bwd_tile<IO, M, N, U, false, R, WY>(rx, rdy, rdx, w, k, acc, ry);
+        if constexpr (N > 0) bwd_tile<IO, M, N, U, false, R, WY>(rx, rdy, rdx, w, k, kw, acc, ry);
     }
     reduce_and_emit<M, N>(a, P, p, acc);
 }
@@ -544,7 +546,8 @@ __global__ __launch_bounds__(kNarrowThreads) void grkan_fwd_narrow_kernel(FwdArg
 // arithmetic, decide this kernel's rate.
 template <class IO, int M, int N, int U, int K, bool CHECK>
 __device__ static inline void narrow_bwd_rows(Span sx, Span sdy, Span sdx, const Window &w,
-                                              const BwdCoefs<M, N> &k, float (&acc)[Deg<M, N>::kNumCoef]) {
+                                              const BwdCoefs<M, N> &k, const QWide<N> &kw,
+                                              float (&acc)[Deg<M, N>::kNumCoef]) {
     using V = Elem<IO>;
     constexpr int KP = Deg<M, N>::kTop;
     float xf[U], dyf[U];
@@ -573,7 +576,7 @@ __device__ static inline void narrow_bwd_rows(Span sx, Span sdy, Span sdx, const
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const Pow<KP> X(xf[u]);
-            const ElemBwd eb = backward_element<M, N, KP>(X, dyf[u], k);
+            const ElemBwd eb = backward_element<M, N, KP>(X, dyf[u], k, kw);
             accumulate<M, N>(eb.w, eb.sv, X, acc);
             dxf[u] = eb.dx;
             sure = sure && eb.sure;
@@ -583,7 +586,7 @@ __device__ static inline void narrow_bwd_rows(Span sx, Span sdy, Span sdx, const
             // (x == 0, a root of Q, or b = 0 in its group): fix this lane's rows.
             if (__builtin_expect(!sure, 0)) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) dxf[u] = exact_fix<M, N>(xf[u], dyf[u], k, acc);
+                for (int u = 0; u < U; ++u) dxf[u] = exact_fix<M, N>(xf[u], dyf[u], k, kw, acc);
             }
         }
 #pragma unroll
@@ -613,7 +616,9 @@ __global__ __launch_bounds__(kNarrowBwdThreads) void grkan_bwd_narrow_kernel(Bwd
     if (p.tile >= P.tiles) return;
     int64_t ch;
     const Window w = narrow_window<RW, U, K>(P, p, ch);
-    const BwdCoefs<M, N> k = derive<M, N, false>(load_coefs<M, N>(a.A, a.B, narrow_group(P, ch)));
+    const Coefs<M, N> c = load_coefs<M, N>(a.A, a.B, narrow_group(P, ch));
+    const BwdCoefs<M, N> k = derive<M, N>(c);
+    const QWide<N> kw = widen<M, N, false>(c);
     const Span sx = make_span(at(a.x, w.base), w.avail);
     const Span sdy = make_span(at(a.dy, w.base), w.avail);
     const Span sdx = make_span(at(a.dx, w.base), w.avail);
@@ -621,8 +626,8 @@ __global__ __launch_bounds__(kNarrowBwdThreads) void grkan_bwd_narrow_kernel(Bwd
     float acc[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) acc[i] = 0.0f;
-    if (w.full) narrow_bwd_rows<IO, M, N, U, K, false>(sx, sdy, sdx, w, k, acc);
-    else narrow_bwd_rows<IO, M, N, U, K, true>(sx, sdy, sdx, w, k, acc);
+    if (w.full) narrow_bwd_rows<IO, M, N, U, K, false>(sx, sdy, sdx, w, k, kw, acc);
+    else narrow_bwd_rows<IO, M, N, U, K, true>(sx, sdy, sdx, w, k, kw, acc);
 
     // Workgroup sums in a fixed order: per channel over the row lanes, then
     // per group over its channels in this column block, in fp64.

@@ -44,13 +44,15 @@ __global__ __launch_bounds__(256) void grkan_bwd_naive_kernel(const void *x, con
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
         const int g = (int)((i % d) / d_g);
-        const BwdCoefs<kM, kN> k = derive<kM, kN, false>(load_coefs<kM, kN>(A, B, g));
+        const Coefs<kM, kN> c = load_coefs<kM, kN>(A, B, g);
+        const BwdCoefs<kM, kN> k = derive<kM, kN>(c);
+        const QWide<kN> kw = widen<kM, kN, false>(c);
         float acc[kNumCoef];
 #pragma unroll
         for (int c = 0; c < kNumCoef; ++c) acc[c] = 0.0f;
         const float xv = Scalar<IO>::load(x, i), dyv = Scalar<IO>::load(dy, i);
         const Pow<kM> X(xv);
-        const ElemBwd e = exact_element<kM, kN, kM>(X, dyv, k);
+        const ElemBwd e = exact_element<kM, kN, kM>(X, dyv, k, kw);
         accumulate<kM, kN>(e.w, e.sv, X, acc);
         Scalar<IO>::store(dx, i, e.dx);
 #pragma unroll
