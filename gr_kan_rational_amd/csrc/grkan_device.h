@@ -262,17 +262,25 @@ template <int N> struct QWide {
     double b[N > 0 ? N : 1];     // b_1..b_N
 };
 
-// The sign guard.  The backward's Q is x q(x) by Horner's rule in fp64,
-// rounded once to fp32 (backward_element); it differs from the exact Q(x) by
-// at most 2^-24 |Q| plus an fp64 error far below 2^-24 sum_j |b_j| |x|^j,
-// and sum_j |b_j| |x|^j is at most (sum_j |b_j|) (|x| + |x|^N).  So
-// |Q| > (N + 4) 2^-21 (sum_j |b_j|) (|x| + |x|^N) -- a bound derived for an
-// fp32 evaluation, (2N + 1) 2^-24 sum_j |b_j| |x|^j, times four, and thus a
-// conservative one here -- proves Q != 0 and sign(fl(Q)) = sign(Q).  (For
-// GR-KAN's N = 4 the scale is 2^-18.)  It fails at x = 0 (Q = 0), next to a
-// root of Q (rare: about 1e-5 of the elements at the workloads' inputs) and
-// for NaN or huge x; those elements take the exact path.
-template <int N> constexpr float sign_guard_scale() { return (float)(N + 4) / 2097152.0f; }
+// The sign guard.  The backward's Q is x q(x), q(x) = b_1 + b_2 x + ... +
+// b_N x^(N-1) by Horner's rule with FMAs in fp64 from exact fp64 copies of x
+// and b, then x q and its rounding to fp32 (backward_element).  Rounding
+// keeps signs, so sign(Q) = sign(x) sign(q_computed) whenever Q != 0, and
+// q_computed has q(x)'s sign when |q_computed| exceeds Horner's error bound,
+// gamma_{N-1} S with S = sum_j |b_j| |x|^(j-1) and gamma_n ~ n 2^-53
+// (Higham, "Accuracy and Stability of Numerical Algorithms", Horner's rule).
+// Since |x| S <= (sum_j |b_j|) (1 + |x|^N), the test
+//   |Q| > kguard (1 + |x|^N),  kguard = 2^-46 sum_j |b_j|
+// -- one FMA and one compare -- proves the sign with a margin of 8x over
+// gamma_{2N} for N <= 8, which also covers the fp32 roundings of Q, of |x|^N
+// and of the bound itself.  kguard is kept at least 2^-126, so that a passing
+// |Q| is a normal number (relative rounding) even for tiny coefficients.  The
+// test fails at x = 0 (Q = 0), for NaN, infinite or huge x (|x|^N
+// overflows), for |x| below ~2^-46 (relative to the coefficients), and within
+// ~2^-46 (relative) of a root of q -- in practice only x = 0 at the
+// workloads' inputs; those elements take the exact path.
+template <int N> constexpr float sign_guard_scale() { return 1.0f / 70368744177664.0f; }  // 2^-46
+constexpr float kGuardFloor = 1.17549435e-38f;  // 2^-126
 
 template <int M, int N>
 __device__ static inline BwdCoefs<M, N> derive(const Coefs<M, N> &c) {
@@ -298,7 +306,7 @@ __device__ static inline BwdCoefs<M, N> derive(const Coefs<M, N> &c) {
         k.b[0] = 0.0f;
         k.db[0] = 0.0f;
     }
-    k.kguard = sign_guard_scale<N>() * bsum;
+    k.kguard = fmaxf(sign_guard_scale<N>() * bsum, kGuardFloor);
     k.q_zero = zero;
     return k;
 }
@@ -403,7 +411,7 @@ __device__ static inline ElemBwd backward_element(const Pow<K> &X, float dy, con
         e.F = P * r;
         e.v = e.w * e.F;
         e.sv = __uint_as_float(__float_as_uint(e.v) ^ (__float_as_uint(Q) & 0x80000000u));
-        e.sure = fabsf(Q) > k.kguard * (fabsf(x) + fabsf(X.p[N]));
+        e.sure = fabsf(Q) > fmaf(fabsf(X.p[N]), k.kguard, k.kguard);
         e.Qd = Qd;
         e.wPd = e.w * Pd;
         e.dx = fmaf(-e.sv, Qd, e.wPd);
