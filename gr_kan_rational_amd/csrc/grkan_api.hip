@@ -122,8 +122,13 @@ grkan_status_t plan_narrow(int64_t rows, int64_t d, int32_t n_groups, const Degr
 }
 
 // Shape checks and the launch plan (a function of the shape, dtype and degrees).
+// with_f: the backward that also stores F(x) (the layer backward).  Its
+// kernel holds every pass's F until the tile's end (F may overwrite dy,
+// which the rare exact-sign path re-reads), so it takes the small-grid pass
+// count at every size: 96 VGPRs with 2 bf16 passes, against 128 and spills
+// with 4 (KAT-B layer 2: 840 against 896 us).
 grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, const DegreeOps &deg,
-                          grkan_dtype_t io, int pass, bool atomic_mode, Plan *P) {
+                          grkan_dtype_t io, int pass, bool atomic_mode, Plan *P, bool with_f = false) {
     if (io != GRKAN_F32 && io != GRKAN_BF16) return GRKAN_ERR_INVALID_ARG;
     if (rows < 0 || d <= 0 || n_groups <= 0 || d % n_groups != 0) return GRKAN_ERR_INVALID_ARG;
     const int es = io_bytes(io);
@@ -159,7 +164,7 @@ grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, const Degre
         // fewer passes for small grids (see kSmallGrid)
         const int64_t tiles0 = (rows + (int64_t)u * rpi - 1) / ((int64_t)u * rpi);
         const int64_t grid0 = 8 * parts * n_groups * ((tiles0 + 7) / 8);
-        if (grid0 < kSmallGrid) u = deg.unroll(io, pass, true);
+        if (grid0 < kSmallGrid || with_f) u = deg.unroll(io, pass, true);
     }
     if ((int64_t)u * rpi * row_bytes > kMaxLaneSpan) return GRKAN_ERR_UNSUPPORTED;
     *P = Plan{};
@@ -294,7 +299,7 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
     if (!valid_repeat(repeat)) return GRKAN_ERR_INVALID_ARG;
     if (naive && (m != kGrkanM || n != kGrkanN)) return GRKAN_ERR_UNSUPPORTED;
     Plan P;
-    grkan_status_t st = plan_shape(rows, d, n_groups, *deg, io, 1, !det, &P);
+    grkan_status_t st = plan_shape(rows, d, n_groups, *deg, io, 1, !det, &P, y != nullptr);
     if (st != GRKAN_OK) return st;
     if (repeat != 1 && (P.kind == kNarrow || m != kGrkanM || n != kGrkanN || naive))
         return GRKAN_ERR_UNSUPPORTED;
@@ -648,7 +653,7 @@ grkan_status_t layer_bwd_plan(int64_t rows, int64_t d_in, int64_t d_out, int32_t
     if (n_groups > layer_max_groups() || (d_in / n_groups) % 8 != 0) return GRKAN_ERR_UNSUPPORTED;
     if (d_out % layer_k_step() != 0) return GRKAN_ERR_UNSUPPORTED;
     const DegreeOps *deg = find_degree(kGrkanM, kGrkanN);
-    st = plan_shape(rows > 0 ? rows : 1, d_in, n_groups, *deg, GRKAN_BF16, 1, false, &lp->act);
+    st = plan_shape(rows > 0 ? rows : 1, d_in, n_groups, *deg, GRKAN_BF16, 1, false, &lp->act, true);
     if (st != GRKAN_OK) return st;
     lp->off_wt = 0;
     lp->off_buf = align256((size_t)d_in * d_out * 2);

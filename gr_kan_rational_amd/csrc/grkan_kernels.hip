@@ -768,14 +768,9 @@ hipError_t bwd_impl(const BwdArgs &a, int repeat, dim3 grid, hipStream_t s) {
         }
         return hipErrorInvalidValue;
     }
-    if (a.y) {
-        // F(x) as a second output: the GR-KAN bf16 layer backward only
-        if constexpr (std::is_same<IO, bf16io>::value && M == 5 && N == 4) {
-            hipLaunchKernelGGL((grkan_bwd_kernel<IO, M, N, U, 1, true>), grid, block, lds, s, a);
-            return hipGetLastError();
-        }
-        return hipErrorInvalidValue;
-    }
+    // F(x) as a second output (the GR-KAN bf16 layer backward) takes the
+    // small pass count at every size (plan_shape's with_f)
+    if (a.y) return hipErrorInvalidValue;
     hipLaunchKernelGGL((grkan_bwd_kernel<IO, M, N, U, 1>), grid, block, lds, s, a);
     return hipGetLastError();
 }

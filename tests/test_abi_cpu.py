@@ -325,11 +325,15 @@ def lbwd(lib, x=P, dz=P + 0x100000, A=P + 0x200000, B=P + 0x300000, W=P + 0x4000
 def test_layer_backward_workspace_size(lib):
     f = lib.grkan_layer_backward_workspace_size
     # KAT-B layer 2: W^T (768 x 3072 bf16), one [rows][3072] bf16 buffer, the bf16 activation
-    # backward's partials (as grkan_backward_workspace_size), 14 row splits of fp32 dW partials
-    # (at most 16384 rows each: 13 at least; 36 output tiles x 14 = 504 workgroups fill two
-    # rounds of 256 to 98%, 13 would fill 91%), each piece 256-byte aligned
+    # backward's partials, 14 row splits of fp32 dW partials (at most 16384 rows each: 13 at
+    # least; 36 output tiles x 14 = 504 workgroups fill two rounds of 256 to 98%, 13 would fill
+    # 91%), each piece 256-byte aligned.  The activation backward that also stores F runs 2
+    # passes per workgroup (8-row tiles: 25,216 slots), not the 4 of grkan_backward: fp32
+    # partials [8 groups][10 coefficients][25,216], then 4 fp64 chunk sums (8,192 slots each)
+    # per coefficient.
     a256 = lambda v: (v + 255) // 256 * 256
-    act = lib.grkan_backward_workspace_size(201728, 3072, 8, BF16, 0)
+    act = 8 * 10 * 25216 * 4 + 8 * 10 * 4 * 8
+    assert act == 2 * lib.grkan_backward_workspace_size(201728, 3072, 8, BF16, 0)
     assert f(201728, 3072, 768, 8) == (a256(768 * 3072 * 2) + a256(201728 * 3072 * 2) + a256(act)
                                       + a256(14 * 768 * 3072 * 4))
     assert f(0, 256, 64, 8) == 0
