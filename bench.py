@@ -20,7 +20,11 @@ inputs in distinct buffers, call by call, so that every call streams from
 HBM; a second timing with the cache flushed before each call (a 512 MB write
 outside the events) cross-checks it.  `detail.stream_probe_GBps` is the
 measured ceiling of the backward's traffic: grkan_stream_probe (two reads,
-one write, no arithmetic) over the same buffers.
+one write, no arithmetic) over the same buffers.  A bf16-I/O backward does the
+same arithmetic per element on half the bytes and is bound by its vector-ALU
+work: its `roofline` rates it against the vector-ALU peak instead (lane
+operations the method needs per element over the call's duration), with the
+HBM figures under `roofline.hbm`.
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
 workload.  `detail` adds the forward's figures, the atomic-mode and naive
 per-element-atomic backward times, the rounding error of each backward
@@ -43,6 +47,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+# Vector-ALU peak in lane operations per second (an FMA counts once): the published fp32
+# vector rate, 157.3 TFLOP/s = 256 CUs x 128 FMA lanes per clock x 2 x 2.4 GHz, halved.
+VALU_PEAK_TOPS = 256 * 128 * 2.4e9 / 1e12
 MALL_BYTES = 256 << 20  # MI355X Infinity Cache
 MALL_DEFEAT_BYTES = 8 * MALL_BYTES  # rotated input sets hold at least this much
 MAX_SETS = 64
@@ -57,6 +64,15 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, "gr_kan_rational_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def backward_valu_ops_per_element(m: int, n: int, io: str) -> int:
+    """Vector-ALU operations one backward element needs in these kernels (degrees m, n >= 1):
+    bf16 unpack of x and dy, powers x^2..x^max(m,n), P, P', Q in fp64 (n - 1 FMAs, x q, two
+    conversions), Q', D and 1/D, w, F, v, s v, w P', dX, the sign guard (one FMA, one compare)
+    and the m + 1 + n gradient terms -- 44 for GR-KAN's (5, 4) with bf16 I/O."""
+    return ((2 if io == "bf16" else 0) + (max(m, n) - 1) + m + (m - 1) + (n + 2) + (n - 1) + 2 + 6 + 2
+            + (m + 1 + n))
 
 
 def traffic_from_profiles(workload: str, io_bytes_per_launch: float):
@@ -681,6 +697,18 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": bwd_bytes},
         "detail": detail,
     }
+    if w.io == "bf16" and w.n > 0 and w.m > 0:
+        # bf16 I/O halves the bytes per element but not the arithmetic: this backward is bound
+        # by its vector-ALU work, and is rated against the vector-ALU issue peak instead (its
+        # HBM figures stay under detail)
+        ops = backward_valu_ops_per_element(w.m, w.n, w.io)
+        tops = ops * E / (bwd_ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "alu", "achieved": tops, "peak": VALU_PEAK_TOPS, "unit": "TOP/s",
+                           "frac": tops / VALU_PEAK_TOPS, "traffic": traffic,
+                           "kernel": out["roofline"]["kernel"], "valu_ops_per_element": ops,
+                           "elements_per_launch": E,
+                           "hbm": {"achieved": bwd_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                   "frac": bwd_gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": bwd_bytes}}
     if not args.no_cpu_baseline:
         log("cpu baseline: fp64 oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w)
