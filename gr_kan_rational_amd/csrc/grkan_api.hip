@@ -160,11 +160,28 @@ grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, const Degre
         if (rpi == 0) rpi = target / (int)seg_vecs > 0 ? target / (int)seg_vecs : 1;
     }
     int u = deg.unroll(io, pass, false);
+    bool small = false;
     {
         // fewer passes for small grids (see kSmallGrid)
         const int64_t tiles0 = (rows + (int64_t)u * rpi - 1) / ((int64_t)u * rpi);
         const int64_t grid0 = 8 * parts * n_groups * ((tiles0 + 7) / 8);
-        if (grid0 < kSmallGrid || with_f) u = deg.unroll(io, pass, true);
+        small = grid0 < kSmallGrid;
+        if (small || with_f) u = deg.unroll(io, pass, true);
+    }
+    if (pass == 0 && !small) {
+        // Large forward grids: one-wave workgroups, as many whole segments as
+        // fit in a wave (partial waves allowed) -- the shape that streams best
+        // (see kFwdWaveBlock).
+        if (seg_vecs > kFwdWaveBlock) {
+            parts = (seg_vecs + kFwdWaveBlock - 1) / kFwdWaveBlock;
+            part_vecs = (seg_vecs + parts - 1) / parts;
+            parts = (seg_vecs + part_vecs - 1) / part_vecs;
+            rpi = 1;
+        } else {
+            parts = 1;
+            part_vecs = seg_vecs;
+            rpi = kFwdWaveBlock / (int)seg_vecs;
+        }
     }
     if ((int64_t)u * rpi * row_bytes > kMaxLaneSpan) return GRKAN_ERR_UNSUPPORTED;
     *P = Plan{};

@@ -126,6 +126,15 @@ template <int M, int N> struct Kernels {
 // so the summation order is still the same on every device).
 constexpr int64_t kSmallGrid = 4096;
 
+// Forward workgroups on grids that are not small: one wave (a segment's
+// vectors per row, times as many rows as fit), 2 passes.  Measured on MI355X
+// (forward call): KAT-B 195.5 against 197.5 us for 384-lane workgroups,
+// KAT-S hidden 401 against 409, KAT-B hidden bf16 397.5 against 412-415; on
+// the small KAT-T grid it was 16 against 12.7 us, which keeps 384 lanes and 1
+// pass.  The 2-read / 1-write streaming probe peaks with one-wave
+// workgroups too.
+constexpr int kFwdWaveBlock = 64;
+
 // Degree pairs compiled into the library: (m, n) with a_0..a_m, b_1..b_n.
 // GR-KAN's (5, 4) first.
 #define GRKAN_FOR_EACH_DEGREE(X) X(5, 4) X(3, 2) X(4, 3) X(6, 5) X(7, 6) X(2, 1) X(4, 4) X(5, 0)
