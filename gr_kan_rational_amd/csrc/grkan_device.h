@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "grkan_qsign.h"
+
 namespace grkan {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -321,32 +323,73 @@ __device__ static inline QWide<N> widen(const Coefs<M, N> &c) {
     return q;
 }
 
+// Denominator degrees from which the backward decides an unproven sign of Q
+// exactly (qsign_lanes, exact_signs, exact_apply below) instead of by
+// compensated Horner (sign_q_exact, exact_fix, exact_element): compensated
+// Horner was measured wrong next to 5-fold roots of a degree-5 q, and
+// matched the exact sign on every clustered and exact root tried below that.
+// The split also keeps the GR-KAN (5, 4) kernels' code as it was: the scalar
+// sign loop, present in a kernel, changes how its main loop is scheduled
+// (2-3% slower at KAT-B), while it did not slow the (7, 6) ones.
+constexpr int kExactSignMinN = 5;
+
 // sign of q(x) = b_1 + b_2 x + ... + b_N x^(N-1) by compensated Horner in
-// fp64 (error-free products by FMA and error-free sums; Graillat, Langlois &
-// Louvet, "Compensated Horner scheme", 2005).  The result carries about twice
-// fp64's precision, enough to fix the sign of every fp32 x that is not within
-// ~2^-100 (relative) of a root.
+// fp64 (grkan_qsign.h), for denominators of degree N < kExactSignMinN.
 template <int M, int N>
 __device__ static inline int sign_q_exact(float xf, const BwdCoefs<M, N> &k) {
-    // The error-free transformations need every product and sum rounded on its
-    // own: no contraction of s*x + b into one FMA.
-#pragma clang fp contract(off)
     static_assert(N >= 1, "no denominator");
-    const double x = (double)xf;
-    double s = (double)k.b[N - 1];
-    double c = 0.0;
+    return qsign_compensated<N>(xf, k.b);
+}
+
+// sign(q(x)), q(x) = b_1 + b_2 x + ... + b_N x^(N-1), exactly by the integer
+// evaluation of grkan_qsign.h, for the elements x[i] of each lane whose bit i
+// of `need` is set: bit i of `pos` / `neg` for a positive / negative q(x[i]),
+// of `keep` for an element beyond the integer window (it keeps the sign of
+// its fp64-evaluated Q).  One (lane, element) at a time, its x and b are read
+// into scalar registers and the evaluation runs on the scalar unit, so this
+// rare decision takes almost no vector registers from the loop around it, and
+// its code appears once per call.  A wave-wide loop: every active lane must
+// call it.
+template <int N, int E>
+__device__ static inline void qsign_lanes(uint32_t need, const float (&x)[E], const float (&b)[N],
+                                          uint32_t &pos, uint32_t &neg, uint32_t &keep) {
+    static_assert(N >= 1 && E >= 1 && E <= 32, "sizes");
+    const uint32_t me = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    pos = 0u;
+    neg = 0u;
+    keep = 0u;
+    for (;;) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(need != 0u);
+        if (m == 0) break;
+        const int l = __builtin_ctzll(m);
+        const int i = need ? __builtin_ctz(need) : 0;  // this lane's next element
+        // Chosen by selects; the asm keeps the compiler from turning them
+        // into an indexed load from a stack copy of x.
+        float xi = 0.0f;
 #pragma unroll
-    for (int j = N - 2; j >= 0; --j) {
-        double p = s * x;
-        double pe = fma(s, x, -p);         // s*x = p + pe exactly
-        double t = p + (double)k.b[j];
-        double bb = t - p;
-        double te = (p - (t - bb)) + ((double)k.b[j] - bb);  // p + b = t + te exactly
-        s = t;
-        c = fma(c, x, pe + te);
+        for (int e = 0; e < E; ++e) {
+            float xe = x[e];
+            asm volatile("" : "+v"(xe));
+            xi = (i == e) ? xe : xi;
+        }
+        // The asm keeps the coefficients' decomposition inside the loop
+        // rather than hoisted out of it and held in registers throughout.
+        float bl[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            int bj = __builtin_amdgcn_readlane(__float_as_int(b[j]), l);
+            asm volatile("" : "+s"(bj));
+            bl[j] = __int_as_float(bj);
+        }
+        int sl = 0;
+        const bool ok = qsign_integer<N>(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(xi), l)), bl, sl);
+        if (me == (uint32_t)l) {
+            pos |= (uint32_t)(ok && sl > 0) << i;
+            neg |= (uint32_t)(ok && sl < 0) << i;
+            keep |= (uint32_t)!ok << i;
+            need &= need - 1u;
+        }
     }
-    double q = s + c;
-    return (q > 0.0) - (q < 0.0);
 }
 
 // Everything the backward needs about one element.  fp32 arithmetic except Q:
@@ -450,15 +493,101 @@ __device__ static inline float exact_fix(float x, float dy, const BwdCoefs<M, N>
     }
 }
 
+// Where the exact-sign steps below take the coefficients from: the caller's
+// registers.
+template <int M, int N> struct CoefHeld {
+    const BwdCoefs<M, N> &k;
+    const QWide<N> &kw;
+    __device__ void get(BwdCoefs<M, N> &k2, QWide<N> &kw2) const {
+        k2 = k;
+        kw2 = kw;
+    }
+};
+
+// The exact sign for a lane's E elements of a tile in which some sign was
+// not proven, in two steps.  exact_signs: which elements the guard did not
+// prove and that are to be redone (unsure: all of them but those beyond the
+// integer window, which keep their sign) and, for those with x != 0, the sign
+// of q(x) (pos / neg bits).  A wave-wide call.  Only the guard's verdicts of
+// its evaluation are used; the rest is dead code.
+template <int M, int N, int E, class Src>
+__device__ static inline void exact_signs(const float (&x)[E], const Src &src, uint32_t &unsure,
+                                          uint32_t &pos, uint32_t &neg) {
+    constexpr int K = Deg<M, N>::kTop;
+    BwdCoefs<M, N> k;
+    QWide<N> kw;
+    src.get(k, kw);
+    uint32_t need = 0u;
+    unsure = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        // one element after another (the asm ties x[e] to the bits so far):
+        // interleaved, the E evaluations would need E times the registers
+        float xe = x[e];
+        asm volatile("" : "+v"(xe) : "v"(unsure));
+        const bool sure = backward_element<M, N, K>(Pow<K>(xe), 0.0f, k, kw).sure;
+        unsure |= (uint32_t)!sure << e;
+        need |= (uint32_t)(!sure && xe != 0.0f && !k.q_zero) << e;
+    }
+    pos = 0u;
+    neg = 0u;
+    uint32_t keep = 0u;
+    if constexpr (N > 0) qsign_lanes<N, E>(need, x, k.b, pos, neg, keep);
+    unsure &= ~keep;
+}
+
+// exact_apply: evaluates the E elements, replaces the dB terms of the unsure
+// ones (accumulated with the fp64-Q sign) by those of the exact sign and
+// returns every element's dX in dx.  x and dy must be the same values that
+// went through the main loop and exact_signs.
+template <int M, int N, int E, class Src>
+__device__ static inline void exact_apply(const float (&x)[E], const float (&dy)[E], const Src &src,
+                                          uint32_t unsure, uint32_t pos, uint32_t neg,
+                                          float (&acc)[Deg<M, N>::kNumCoef], float (&dx)[E]) {
+    constexpr int K = Deg<M, N>::kTop;
+    BwdCoefs<M, N> k;
+    QWide<N> kw;
+    src.get(k, kw);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        float xe = x[e];
+        if (e > 0) asm volatile("" : "+v"(xe) : "v"(dx[e - 1]));  // one after another, as above
+        const Pow<K> X(xe);
+        const ElemBwd el = backward_element<M, N, K>(X, dy[e], k, kw);
+        dx[e] = el.dx;
+        if constexpr (N > 0) {
+            if ((unsure >> e) & 1u) {
+                const int sq = ((pos >> e) & 1u) ? 1 : (((neg >> e) & 1u) ? -1 : 0);
+                const int s = sq * ((xe > 0.0f) ? 1 : -1);
+                const float sv = (s == 0) ? 0.0f : ((s > 0) ? el.v : -el.v);
+                const float diff = el.sv - sv;  // undo -el.sv x^j, add -sv x^j
+#pragma unroll
+                for (int j = 1; j <= N; ++j) acc[M + j] = fmaf(diff, X.p[j], acc[M + j]);
+                dx[e] = fmaf(-sv, el.Qd, el.wPd);
+            }
+        }
+    }
+}
+
 // backward_element with the exact sign: when the fp32 guard does not prove
-// sign(Q), s = sign(x) sign(q(x)) is decided exactly (0 at x == 0) and sv and
-// dX are recomputed with it.  Bit for bit equal to backward_element wherever
-// the guard holds.
+// sign(Q), s = sign(x) sign(q(x)) is decided (0 at x == 0; exactly from
+// kExactSignMinN on, a wave-wide call there) and sv and dX are recomputed
+// with it.  Bit for bit equal to backward_element wherever the guard holds.
 template <int M, int N, int K>
 __device__ static inline ElemBwd exact_element(const Pow<K> &X, float dy, const BwdCoefs<M, N> &k,
                                                const QWide<N> &kw) {
     ElemBwd e = backward_element<M, N, K>(X, dy, k, kw);
-    if constexpr (N > 0) {
+    if constexpr (N >= kExactSignMinN) {
+        const float x[1] = {X.p[1]};
+        uint32_t pos, neg, keep;
+        qsign_lanes<N, 1>((uint32_t)(!e.sure && x[0] != 0.0f && !k.q_zero), x, k.b, pos, neg, keep);
+        if (!e.sure && !keep) {
+            const int s = (pos ? 1 : (neg ? -1 : 0)) * ((x[0] > 0.0f) ? 1 : -1);
+            e.sv = (s == 0) ? 0.0f : ((s > 0) ? e.v : -e.v);
+            e.dx = fmaf(-e.sv, e.Qd, e.wPd);
+        }
+        e.sure = true;
+    } else if constexpr (N > 0) {
         if (!e.sure) {
             const float x = X.p[1];
             const int s = (x == 0.0f || k.q_zero) ? 0 : sign_q_exact<M, N>(x, k) * ((x > 0.0f) ? 1 : -1);

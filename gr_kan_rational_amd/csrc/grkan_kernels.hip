@@ -321,13 +321,32 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
         // Re-read the tile (dx has not been written yet, so this is safe when
         // dx aliases x or dy) and fix those elements before storing.
         if (__builtin_expect(!sure, 0)) {
+            if constexpr (N >= kExactSignMinN) {
+                // exact integer sign: one vector at a time, x and dy read
+                // again after the sign loop rather than held across it
+                const CoefHeld<M, N> src{k, kw};
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float xf[E], dyf[E];
-                V::unpack(win_reload16<true>(rx, w.lane + u * w.stride), xf);
-                V::unpack(win_reload16<true>(rdy, w.lane + u * w.stride), dyf);
+                for (int u = 0; u < U; ++u) {
+                    uint32_t unsure, pos, neg;
+                    {
+                        float xf[E];
+                        V::unpack(win_reload16<true>(rx, w.lane + u * w.stride), xf);
+                        exact_signs<M, N, E>(xf, src, unsure, pos, neg);
+                    }
+                    float xf[E], dyf[E];
+                    V::unpack(win_reload16<true>(rx, w.lane + u * w.stride), xf);
+                    V::unpack(win_reload16<true>(rdy, w.lane + u * w.stride), dyf);
+                    exact_apply<M, N, E>(xf, dyf, src, unsure, pos, neg, acc, dxf[u]);
+                }
+            } else {
 #pragma unroll
-                for (int e = 0; e < E; ++e) dxf[u][e] = exact_fix<M, N>(xf[e], dyf[e], k, kw, acc);
+                for (int u = 0; u < U; ++u) {
+                    float xf[E], dyf[E];
+                    V::unpack(win_reload16<true>(rx, w.lane + u * w.stride), xf);
+                    V::unpack(win_reload16<true>(rdy, w.lane + u * w.stride), dyf);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) dxf[u][e] = exact_fix<M, N>(xf[e], dyf[e], k, kw, acc);
+                }
             }
         }
     }
@@ -585,8 +604,15 @@ __device__ static inline void narrow_bwd_rows(Span sx, Span sdy, Span sdx, const
             // Rare: an element whose sign of Q the fp32 guard did not prove
             // (x == 0, a root of Q, or b = 0 in its group): fix this lane's rows.
             if (__builtin_expect(!sure, 0)) {
+                if constexpr (N >= kExactSignMinN) {
+                    uint32_t unsure, pos, neg;
+                    const CoefHeld<M, N> src{k, kw};
+                    exact_signs<M, N, U>(xf, src, unsure, pos, neg);
+                    exact_apply<M, N, U>(xf, dyf, src, unsure, pos, neg, acc, dxf);
+                } else {
 #pragma unroll
-                for (int u = 0; u < U; ++u) dxf[u] = exact_fix<M, N>(xf[u], dyf[u], k, kw, acc);
+                    for (int u = 0; u < U; ++u) dxf[u] = exact_fix<M, N>(xf[u], dyf[u], k, kw, acc);
+                }
             }
         }
 #pragma unroll

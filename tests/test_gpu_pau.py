@@ -18,6 +18,7 @@ import torch
 
 from gr_kan_rational_amd import synth
 from oracle import oracle as orc
+import nearroot
 import parity
 
 pytestmark = pytest.mark.gpu
@@ -132,6 +133,28 @@ def test_narrow_special_values(gk):
     inp["B"][7] = np.array([-0.75, 1.0], np.float32)   # Q = x (x - 0.75): root at 0.75
     inp["x"][1::3, 7] = np.float32(0.75)
     run_and_check(gk, w, inp, "deterministic", "narrow special values")
+
+
+# (rows, d, n_groups): 8-channel groups (the segment kernels, a small grid), one function
+# per channel (the narrow kernels), and 96-channel groups on a grid large enough for the
+# kernels the full-size workloads run
+NEAR_ROOT_GEOMS = [(96, 64, 8), (96, 64, 64), (65536, 768, 8)]
+
+
+@pytest.mark.parametrize("m,n", [(7, 6), (6, 5), (5, 4)])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("geom", NEAR_ROOT_GEOMS, ids=lambda g: f"{g[0]}x{g[1]}g{g[2]}")
+def test_exact_sign_at_clustered_roots(gk, m, n, io, geom):
+    """x next to 3- to 5-fold roots of q (tests/nearroot.py), where the sign of Q lies below
+    fp64's resolution and compensated Horner's: every unproven element's sign must be the
+    oracle's exact one.  A wrong sign moves that element's dB terms by 2 |v x^j|, far beyond
+    the sums' tolerance; dX moves little there (Q' vanishes at a multiple root)."""
+    rows, d, n_g = geom
+    inp = nearroot.make(m, n, n_g, d, rows, seed=100 * m + n, io=io)
+    w = synth.custom(f"nearroot{m}{n}", rows, d, n_g, m=m, n=n, io=io, seed=0)
+    for mode in ("deterministic", "block_atomic"):
+        log(f"[exact_sign] (m,n)=({m},{n}) io={io} rows={rows} d={d} n_g={n_g} {mode}")
+        run_and_check(gk, w, inp, mode, f"clustered roots ({m},{n}) {io} {geom} {mode}")
 
 
 @pytest.mark.parametrize("m,n", [(5, 4), (3, 2), (7, 6), (5, 0)])
