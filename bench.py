@@ -60,7 +60,7 @@ GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("grkan_kernels.hip", "grkan_device.h", "grkan_api.hip", "grkan_merge.hip"):
+    for f in ("grkan_kernels.hip", "grkan_device.h", "grkan_qsign.h", "grkan_api.hip", "grkan_merge.hip"):
         with open(os.path.join(ROOT, "gr_kan_rational_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
