@@ -31,6 +31,10 @@
  *     dx have the I/O dtype `io`; A is fp32 [n_groups][6] (a_0..a_5), B is
  *     fp32 [n_groups][4] (b_1..b_4), dA and dB are fp32 with the same shapes.
  *     Arithmetic is fp32; group sums are carried in fp64 inside the library.
+ *     Q is evaluated in fp64; where a bound does not prove its sign, the
+ *     sign of Q = x q(x) is decided again: exactly, in integers over the
+ *     fp32 mantissas, for denominator degrees n >= 5 (unless the terms span
+ *     more than ~250 bits), and by compensated Horner in fp64 for n <= 4.
  *   - All pointers are device pointers on the current HIP device, owned by
  *     the caller.  The library allocates no device memory and keeps no state
  *     beyond a per-device cache of launch limits.
