@@ -57,8 +57,8 @@ def neighbours(r, k, dtype=np.float32):
 
 def make(m, n, n_g, d, rows, seed, io="f32", k=40):
     """x (rows, d), dy, A (n_g, m + 1), B (n_g, n): group g takes cluster g mod 8 of CLUSTERS[n];
-    in every group's channels, even rows hold neighbours of the cluster's roots and odd rows
-    standard normal values.  bf16 x and dy come as uint16 bit patterns (dy rounded toward
+    in every group's channels, even rows hold neighbours of the cluster's roots, row 1 exact
+    zeros and tiny values, the other odd rows standard normal values.  bf16 x and dy come as uint16 bit patterns (dy rounded toward
     zero: any bf16 values will do)."""
     rng = np.random.default_rng(seed)
     sets = CLUSTERS[n]
@@ -74,6 +74,11 @@ def make(m, n, n_g, d, rows, seed, io="f32", k=40):
         block = x[::2, cols]
         block[...] = pool[rng.integers(0, pool.size, block.shape)]
         x[::2, cols] = block
+    # row 1: exact zeros (s = 0) and tiny x, whose terms span more bits than the kernels'
+    # integer window holds (the sign then comes from the fp64 Q, here clear of rounding)
+    specials = np.array([0.0, -0.0, 1e-30, -1e-30, 1e-20, -1e-20, 3e-12, -2e-9], np.float32)
+    if rows > 1:
+        x[1, :] = specials[np.arange(d) % specials.size]
     if io == "bf16":
         x = (x.view(np.uint32) >> 16).astype(np.uint16)
         dy = (dy.view(np.uint32) >> 16).astype(np.uint16)
