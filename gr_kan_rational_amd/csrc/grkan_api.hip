@@ -124,7 +124,7 @@ grkan_status_t plan_narrow(int64_t rows, int64_t d, int32_t n_groups, const Degr
 // Shape checks and the launch plan (a function of the shape, dtype and degrees).
 // with_f: the backward that also stores F(x) (the layer backward).  Its
 // kernel holds every pass's F until the tile's end (F may overwrite dy,
-// which the rare exact-sign path re-reads), so it takes the small-grid pass
+// which the rare sign-fix path re-reads), so it takes the small-grid pass
 // count at every size: 96 VGPRs with 2 bf16 passes, against 128 and spills
 // with 4 (KAT-B layer 2: 840 against 896 us).
 grkan_status_t plan_shape(int64_t rows, int64_t d, int32_t n_groups, const DegreeOps &deg,

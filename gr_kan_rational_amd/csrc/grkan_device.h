@@ -14,8 +14,9 @@
 // 工作"), i.e. to other (M, N), which the templates below cover.  N = 0 is a
 // plain polynomial.  Everything here is fp32 register arithmetic except two
 // fp64 uses in the backward: Q is evaluated in fp64 (see backward_element),
-// and the sign of Q is decided exactly for the rare element whose Q is
-// within rounding of 0.
+// and the sign of Q is decided again for the rare element whose Q is within
+// rounding of 0 (exactly for N >= kExactSignMinN, by compensated Horner in
+// fp64 below that).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -403,9 +404,9 @@ __device__ static inline void qsign_lanes(uint32_t need, const float (&x)[E], co
 // issues fp64 FMAs at the fp32 rate; this costs two conversions per element.)
 // s = sign(Q) is taken from that Q; `sure` says whether the guard proves
 // that sign right.  When it does not (x == 0, x within rounding of a root of
-// Q, NaN), the element still gets the fp32 sign here and exact_fix() later
-// swaps in the exact one.  One function so that the hot loop and the fix
-// agree bit for bit.
+// Q, NaN), the element still gets that sign here and exact_fix() or
+// exact_apply() later swap in the one decided again.  One function so that
+// the hot loop and the fix agree bit for bit.
 struct ElemBwd {
     float dx;   // dY (P'/D - s P Q'/D^2)
     float w;    // dY / D          (dA terms: w x^i)
@@ -471,9 +472,10 @@ __device__ static inline void accumulate(float w, float sv, const Pow<K> &X,
     for (int j = 1; j <= N; ++j) acc[M + j] = fmaf(-sv, X.p[j], acc[M + j]);
 }
 
-// For an element whose sign was not proven: recomputes it, decides
-// s = sign(x) sign(q(x)) exactly (0 at x == 0), replaces the dB terms that
-// were accumulated with the fp32 sign and returns the exact dX.
+// For an element whose sign was not proven (N < kExactSignMinN): recomputes
+// it, decides s = sign(x) sign(q(x)) by compensated Horner (0 at x == 0),
+// replaces the dB terms that were accumulated with the fp64-Q sign and
+// returns dX with the new sign.
 template <int M, int N>
 __device__ static inline float exact_fix(float x, float dy, const BwdCoefs<M, N> &k, const QWide<N> &kw,
                                          float (&acc)[Deg<M, N>::kNumCoef]) {

@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kMaxBlock) void grkan_fwd_kernel(FwdArgs a) {
 // ---------------------------------------------------------------- backward
 
 // One tile's elements: dX stored, this lane's gradient sums in acc.  The rare
-// exact-sign fix runs once per tile, before any dX is stored; it re-reads x
+// sign fix runs once per tile, before any dX is stored; it re-reads x
 // and dy, which is safe even when dx aliases x or dy.
 // With WY, F(x) is stored too, through ry (which may be rdy: every load
 // precedes every store).

@@ -5,7 +5,7 @@ run time.  The probe must change only the arithmetic: its outputs are those of
 grkan_forward / grkan_backward bit for bit (same kernels' memory traffic, same
 reduction order), for every repeat count, both I/O types, ragged tiles and
 column parts, b = 0 groups (the Q = 0 variant), exact zeros and x at a root of
-Q (the exact-sign path), and at full workload size; and they match the fp64
+Q (the sign-fix path), and at full workload size; and they match the fp64
 oracle within the tolerances of tests/parity.py.
 """
 import sys

@@ -125,7 +125,7 @@ def test_pau_parity_narrow_block_atomic(gk, geom):
 
 def test_narrow_special_values(gk):
     """One PAU per channel with exact zeros, b = 0 channels and x at a root of Q: the narrow
-    kernel's exact-sign path, element by element against the oracle."""
+    kernel's sign-fix path, element by element against the oracle."""
     w = synth.custom("narrowspecial", 96, 64, 64, m=3, n=2, io="f32", seed=77)
     inp = synth.make_inputs(w)
     inp["x"][::3, :] = 0.0                    # exact zeros: s = 0
