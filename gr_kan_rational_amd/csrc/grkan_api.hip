@@ -362,13 +362,16 @@ grkan_status_t backward_impl(const void *x, const void *dy, const float *A, cons
         if (st != GRKAN_OK) return st;
     }
     float *partials = static_cast<float *>(workspace);
+    // One tile and one part: each workgroup holds its group's whole sum (no merge).
+    const bool direct = det && P.tiles == 1 && P.parts == 1;
+    const int32_t mode = direct ? kModeDirect : (det ? kModePartials : kModeAtomic);
     for (int64_t b0 = 0; b0 < launch_units(P); b0 += units_per_launch(P)) {
         const int64_t nz = (launch_units(P) - b0 < units_per_launch(P)) ? launch_units(P) - b0 : units_per_launch(P);
-        BwdArgs a{x, dy, dx, A, B, dA, dB, partials, det ? kModePartials : kModeAtomic, P, b0, y};
+        BwdArgs a{x, dy, dx, A, B, dA, dB, partials, mode, P, b0, y};
         st = from_hip(deg->backward(io, a, repeat, grid_of(P, nz), stream));
         if (st != GRKAN_OK) return st;
     }
-    if (!det) return GRKAN_OK;
+    if (!det || direct) return GRKAN_OK;
     double *chunk_sums = reinterpret_cast<double *>(static_cast<char *>(workspace) + chunk_sums_offset(P));
     const bool narrow = P.kind == kNarrow;
     return from_hip(launch_merge(partials, chunk_sums, n_groups, m, n, P.tiles, P.bundles, P.parts,

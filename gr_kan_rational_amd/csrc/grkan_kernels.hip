@@ -415,11 +415,12 @@ __device__ static inline void reduce_and_emit(const BwdArgs &a, const Plan &P, c
         double total = 0.0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) total += (double)slices[t * 16 + j];
-        if (a.mode == kModePartials) {
+        float *dst = (t <= M) ? (a.dA + p.g * (M + 1) + t) : (a.dB + p.g * N + (t - M - 1));
+        if (a.mode != kModeAtomic) {
             const int64_t slot = (int64_t)p.part * 8 * P.bundles + slot_in_part(P, p.tile);
-            a.partials[((int64_t)p.g * NC + t) * plan_slots(P) + slot] = (float)total;
+            float *part = a.partials + ((int64_t)p.g * NC + t) * plan_slots(P) + slot;
+            *(a.mode == kModeDirect ? dst : part) = (float)total;
         } else {
-            float *dst = (t <= M) ? (a.dA + p.g * (M + 1) + t) : (a.dB + p.g * N + (t - M - 1));
             unsafeAtomicAdd(dst, (float)total);
         }
     }
@@ -683,12 +684,13 @@ __global__ __launch_bounds__(kNarrowBwdThreads) void grkan_bwd_narrow_kernel(Bwd
         const int64_t hi = ((gg + 1) * P.d_g < c1 ? (gg + 1) * P.d_g : c1) - c0;
         double s = 0.0;
         for (int64_t c = lo; c < hi; ++c) s += ct[i * kNarrowCols + c];
-        if (a.mode == kModePartials) {
+        float *dst = (i <= M) ? (a.dA + gg * (M + 1) + i) : (a.dB + gg * N + (i - M - 1));
+        if (a.mode != kModeAtomic) {
             const int64_t part = (int64_t)p.cb - gg * P.d_g / P.cpb;
             const int64_t slot = part * 8 * P.bundles + slot_in_part(P, p.tile);
-            a.partials[(gg * NC + i) * plan_slots(P) + slot] = (float)s;
+            float *pp = a.partials + (gg * NC + i) * plan_slots(P) + slot;
+            *(a.mode == kModeDirect ? dst : pp) = (float)s;
         } else {
-            float *dst = (i <= M) ? (a.dA + gg * (M + 1) + i) : (a.dB + gg * N + (i - M - 1));
             unsafeAtomicAdd(dst, (float)s);
         }
     }

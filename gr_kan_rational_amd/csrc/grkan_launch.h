@@ -84,7 +84,10 @@ struct FwdArgs {
     int64_t bundle0;  // first bundle (segment plans) or first tile (narrow plans) of this launch
 };
 
-enum BwdMode : int32_t { kModeAtomic = 0, kModePartials = 1 };
+// kModeDirect: the plan has one tile and one part, so each workgroup's sum is
+// its group's whole sum and is stored to dA / dB (no merge; the bits are the
+// merge's, which would add that one value to nothing).
+enum BwdMode : int32_t { kModeAtomic = 0, kModePartials = 1, kModeDirect = 2 };
 
 struct BwdArgs {
     const void *x;
