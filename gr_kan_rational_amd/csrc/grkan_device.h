@@ -326,7 +326,7 @@ __device__ static inline QWide<N> widen(const Coefs<M, N> &c) {
 
 // Denominator degrees from which the backward decides an unproven sign of Q
 // exactly (qsign_lanes, exact_signs, exact_apply below) instead of by
-// compensated Horner (sign_q_exact, exact_fix, exact_element): compensated
+// compensated Horner (sign_q_compensated, compensated_fix): compensated
 // Horner was measured wrong next to 5-fold roots of a degree-5 q, and
 // matched the exact sign on every clustered and exact root tried below that.
 // The split also keeps the GR-KAN (5, 4) kernels' code as it was: the scalar
@@ -337,7 +337,7 @@ constexpr int kExactSignMinN = 5;
 // sign of q(x) = b_1 + b_2 x + ... + b_N x^(N-1) by compensated Horner in
 // fp64 (grkan_qsign.h), for denominators of degree N < kExactSignMinN.
 template <int M, int N>
-__device__ static inline int sign_q_exact(float xf, const BwdCoefs<M, N> &k) {
+__device__ static inline int sign_q_compensated(float xf, const BwdCoefs<M, N> &k) {
     static_assert(N >= 1, "no denominator");
     return qsign_compensated<N>(xf, k.b);
 }
@@ -404,7 +404,7 @@ __device__ static inline void qsign_lanes(uint32_t need, const float (&x)[E], co
 // issues fp64 FMAs at the fp32 rate; this costs two conversions per element.)
 // s = sign(Q) is taken from that Q; `sure` says whether the guard proves
 // that sign right.  When it does not (x == 0, x within rounding of a root of
-// Q, NaN), the element still gets that sign here and exact_fix() or
+// Q, NaN), the element still gets that sign here and compensated_fix() or
 // exact_apply() later swap in the one decided again.  One function so that
 // the hot loop and the fix agree bit for bit.
 struct ElemBwd {
@@ -477,8 +477,8 @@ __device__ static inline void accumulate(float w, float sv, const Pow<K> &X,
 // replaces the dB terms that were accumulated with the fp64-Q sign and
 // returns dX with the new sign.
 template <int M, int N>
-__device__ static inline float exact_fix(float x, float dy, const BwdCoefs<M, N> &k, const QWide<N> &kw,
-                                         float (&acc)[Deg<M, N>::kNumCoef]) {
+__device__ static inline float compensated_fix(float x, float dy, const BwdCoefs<M, N> &k,
+                                               const QWide<N> &kw, float (&acc)[Deg<M, N>::kNumCoef]) {
     constexpr int K = Deg<M, N>::kTop;
     const Pow<K> X(x);
     const ElemBwd e = backward_element<M, N, K>(X, dy, k, kw);
@@ -486,7 +486,7 @@ __device__ static inline float exact_fix(float x, float dy, const BwdCoefs<M, N>
         return e.dx;
     } else {
         if (e.sure) return e.dx;
-        const int s = (x == 0.0f || k.q_zero) ? 0 : sign_q_exact<M, N>(x, k) * ((x > 0.0f) ? 1 : -1);
+        const int s = (x == 0.0f || k.q_zero) ? 0 : sign_q_compensated<M, N>(x, k) * ((x > 0.0f) ? 1 : -1);
         const float sv = (s == 0) ? 0.0f : ((s > 0) ? e.v : -e.v);
         const float diff = e.sv - sv;  // undo -e.sv x^j, add -sv x^j
 #pragma unroll
@@ -571,13 +571,14 @@ __device__ static inline void exact_apply(const float (&x)[E], const float (&dy)
     }
 }
 
-// backward_element with the exact sign: when the fp32 guard does not prove
-// sign(Q), s = sign(x) sign(q(x)) is decided (0 at x == 0; exactly from
-// kExactSignMinN on, a wave-wide call there) and sv and dX are recomputed
-// with it.  Bit for bit equal to backward_element wherever the guard holds.
+// backward_element with the sign fixed: when the guard does not prove
+// sign(Q), s = sign(x) sign(q(x)) is decided again (0 at x == 0; exactly from
+// kExactSignMinN on, a wave-wide call there; by compensated Horner below) and
+// sv and dX are recomputed with it.  Bit for bit equal to backward_element
+// wherever the guard holds.
 template <int M, int N, int K>
-__device__ static inline ElemBwd exact_element(const Pow<K> &X, float dy, const BwdCoefs<M, N> &k,
-                                               const QWide<N> &kw) {
+__device__ static inline ElemBwd sign_fixed_element(const Pow<K> &X, float dy, const BwdCoefs<M, N> &k,
+                                                    const QWide<N> &kw) {
     ElemBwd e = backward_element<M, N, K>(X, dy, k, kw);
     if constexpr (N >= kExactSignMinN) {
         const float x[1] = {X.p[1]};
@@ -592,7 +593,7 @@ __device__ static inline ElemBwd exact_element(const Pow<K> &X, float dy, const 
     } else if constexpr (N > 0) {
         if (!e.sure) {
             const float x = X.p[1];
-            const int s = (x == 0.0f || k.q_zero) ? 0 : sign_q_exact<M, N>(x, k) * ((x > 0.0f) ? 1 : -1);
+            const int s = (x == 0.0f || k.q_zero) ? 0 : sign_q_compensated<M, N>(x, k) * ((x > 0.0f) ? 1 : -1);
             e.sv = (s == 0) ? 0.0f : ((s > 0) ? e.v : -e.v);
             e.dx = fmaf(-e.sv, e.Qd, e.wPd);
             e.sure = true;

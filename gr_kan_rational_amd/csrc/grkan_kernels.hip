@@ -345,7 +345,7 @@ __device__ static inline void bwd_tile(Span rx, Span rdy, Span rdx, const Window
                     V::unpack(win_reload16<true>(rx, w.lane + u * w.stride), xf);
                     V::unpack(win_reload16<true>(rdy, w.lane + u * w.stride), dyf);
 #pragma unroll
-                    for (int e = 0; e < E; ++e) dxf[u][e] = exact_fix<M, N>(xf[e], dyf[e], k, kw, acc);
+                    for (int e = 0; e < E; ++e) dxf[u][e] = compensated_fix<M, N>(xf[e], dyf[e], k, kw, acc);
                 }
             }
         }
@@ -612,7 +612,7 @@ __device__ static inline void narrow_bwd_rows(Span sx, Span sdy, Span sdx, const
                     exact_apply<M, N, U>(xf, dyf, src, unsure, pos, neg, acc, dxf);
                 } else {
 #pragma unroll
-                    for (int u = 0; u < U; ++u) dxf[u] = exact_fix<M, N>(xf[u], dyf[u], k, kw, acc);
+                    for (int u = 0; u < U; ++u) dxf[u] = compensated_fix<M, N>(xf[u], dyf[u], k, kw, acc);
                 }
             }
         }

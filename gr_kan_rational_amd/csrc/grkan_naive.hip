@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void grkan_bwd_naive_kernel(const void *x, con
         for (int c = 0; c < kNumCoef; ++c) acc[c] = 0.0f;
         const float xv = Scalar<IO>::load(x, i), dyv = Scalar<IO>::load(dy, i);
         const Pow<kM> X(xv);
-        const ElemBwd e = exact_element<kM, kN, kM>(X, dyv, k, kw);
+        const ElemBwd e = sign_fixed_element<kM, kN, kM>(X, dyv, k, kw);
         accumulate<kM, kN>(e.w, e.sv, X, acc);
         Scalar<IO>::store(dx, i, e.dx);
 #pragma unroll
