@@ -131,6 +131,27 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on_gpu(x: torch.Tensor) -> None:
+    # the library computes on the device only: a host tensor's pointer must never reach a kernel
+    if x.device.type != "cuda":
+        raise ValueError(f"GR-KAN tensors must be on a GPU device, got {x.device}")
+
+
+def _check_out(t: torch.Tensor, name: str, dtype, numel: int, dev) -> None:
+    """A caller-supplied output: the library writes numel elements of dtype through its pointer."""
+    if t.dtype != dtype or t.numel() != numel or not t.is_contiguous() or t.device != dev:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of {numel} elements on {dev}")
+
+
+def _workspace(ws, dev):
+    """(pointer, size in bytes) of an optional caller-supplied workspace on dev."""
+    if ws is None:
+        return None, 0
+    if not ws.is_contiguous() or ws.device != dev:
+        raise ValueError(f"workspace must be a contiguous tensor on {dev}")
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
 GRKAN_M, GRKAN_N = 5, 4  # GR-KAN's numerator / denominator degrees
 
 
@@ -152,10 +173,11 @@ def _rows_d(x: torch.Tensor):
 def _forward(x, A, B, n_groups, m, n, out, stream, pau, repeat=None):
     lib = load_library()
     io = _io(x)
+    _on_gpu(x)
     _check_coefs(A, B, n_groups, x.device, m, n)
     rows, d = _rows_d(x)
     y = torch.empty_like(x) if out is None else out
-    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous():
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous() or y.device != x.device:
         raise ValueError("out must match x")
     s = ctypes.c_void_p(_stream(stream))
     if repeat is not None:
@@ -208,9 +230,27 @@ def grkan_pau_supported(m: int, n: int) -> bool:
     return bool(load_library().grkan_pau_supported(m, n))
 
 
+def _grad_outputs(x, n_groups, m, n, dx, dA, dB):
+    """dx, dA [n_groups, m+1], dB [n_groups, n] (None when n == 0): allocated when not given,
+    checked when given."""
+    if dx is None:
+        dx = torch.empty_like(x)
+    elif dx.shape != x.shape or dx.dtype != x.dtype or not dx.is_contiguous() or dx.device != x.device:
+        raise ValueError("dx must match x")
+    if dA is None:
+        dA = torch.empty((n_groups, m + 1), dtype=torch.float32, device=x.device)
+    _check_out(dA, "dA", torch.float32, n_groups * (m + 1), x.device)
+    if n > 0:
+        if dB is None:
+            dB = torch.empty((n_groups, n), dtype=torch.float32, device=x.device)
+        _check_out(dB, "dB", torch.float32, n_groups * n, x.device)
+    return dx, dA, dB
+
+
 def _backward(x, dy, A, B, n_groups, m, n, mode, dx, dA, dB, workspace, stream, pau, repeat=None):
     lib = load_library()
     io = _io(x)
+    _on_gpu(x)
     if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device or not dy.is_contiguous():
         raise ValueError("dy must match x")
     _check_coefs(A, B, n_groups, x.device, m, n)
@@ -218,18 +258,14 @@ def _backward(x, dy, A, B, n_groups, m, n, mode, dx, dA, dB, workspace, stream, 
     if mode not in _MODES:
         raise ValueError(f"mode must be one of {sorted(_MODES)}")
     flags = _MODES[mode]
-    dx = torch.empty_like(x) if dx is None else dx
-    dA = torch.empty((n_groups, m + 1), dtype=torch.float32, device=x.device) if dA is None else dA
-    if dB is None and n > 0:
-        dB = torch.empty((n_groups, n), dtype=torch.float32, device=x.device)
+    dx, dA, dB = _grad_outputs(x, n_groups, m, n, dx, dA, dB)
     if pau:
         ws_bytes = lib.grkan_pau_backward_workspace_size(rows, d, n_groups, m, n, io, flags)
     else:
         ws_bytes = lib.grkan_backward_workspace_size(rows, d, n_groups, io, flags)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
-    wsp = _ptr(workspace) if workspace is not None else None
-    wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wsp, wsn = _workspace(workspace, x.device)
     s = ctypes.c_void_p(_stream(stream))
     if repeat is not None:
         name = "grkan_inflated_backward"
@@ -271,13 +307,12 @@ def grkan_backward_noalloc(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, B
     tensors are allocated here only when not given)."""
     lib = load_library()
     io = _io(x)
+    _on_gpu(x)
     if dy.shape != x.shape or dy.dtype != x.dtype or dy.device != x.device or not dy.is_contiguous():
         raise ValueError("dy must match x")
     _check_coefs(A, B, n_groups, x.device)
     rows, d = _rows_d(x)
-    dx = torch.empty_like(x) if dx is None else dx
-    dA = torch.empty((n_groups, GRKAN_M + 1), dtype=torch.float32, device=x.device) if dA is None else dA
-    dB = torch.empty((n_groups, GRKAN_N), dtype=torch.float32, device=x.device) if dB is None else dB
+    dx, dA, dB = _grad_outputs(x, n_groups, GRKAN_M, GRKAN_N, dx, dA, dB)
     st = lib.grkan_backward_noalloc(_ptr(x), _ptr(dy), _ptr(A), _ptr(B), _ptr(dx), _ptr(dA), _ptr(dB),
                                     rows, d, n_groups, io, ctypes.c_void_p(_stream(stream)))
     if st != GRKAN_OK:
@@ -292,12 +327,14 @@ def grkan_stream_probe(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | Non
                        stream=None) -> torch.Tensor:
     """out = a XOR b over the tensors' bytes (``grkan_stream_probe``, the streaming ceiling
     probe: two reads and one write per 16 bytes, as the backward moves)."""
-    if a.numel() * a.element_size() != b.numel() * b.element_size() or not (a.is_contiguous() and b.is_contiguous()):
-        raise ValueError("a and b must be contiguous tensors of the same byte size")
+    _on_gpu(a)
+    if a.numel() * a.element_size() != b.numel() * b.element_size() or not (a.is_contiguous() and b.is_contiguous()) \
+            or b.device != a.device:
+        raise ValueError("a and b must be contiguous tensors of the same byte size on one device")
     out = torch.empty_like(a) if out is None else out
     nbytes = a.numel() * a.element_size()
-    if out.numel() * out.element_size() != nbytes or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor of a's byte size")
+    if out.numel() * out.element_size() != nbytes or not out.is_contiguous() or out.device != a.device:
+        raise ValueError("out must be a contiguous tensor of a's byte size on a's device")
     st = load_library().grkan_stream_probe(_ptr(a), _ptr(b), _ptr(out), nbytes, ctypes.c_void_p(_stream(stream)))
     if st != GRKAN_OK:
         raise GRKANError(st, "grkan_stream_probe")
@@ -327,6 +364,7 @@ def grkan_inflated_backward(x: torch.Tensor, dy: torch.Tensor, A: torch.Tensor, 
 def _layer_dims(x, W):
     if x.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
         raise TypeError("the layer takes bfloat16 x and W")
+    _on_gpu(x)
     if W.dim() != 2 or not W.is_contiguous() or W.device != x.device:
         raise ValueError("W must be a contiguous [d_out, d_in] tensor on x's device")
     rows, d_in = _rows_d(x)
@@ -338,8 +376,7 @@ def _layer_dims(x, W):
 def _layer_out(x, W, out):
     rows, d_in, d_out = _layer_dims(x, W)
     z = torch.empty((*x.shape[:-1], d_out), dtype=torch.bfloat16, device=x.device) if out is None else out
-    if z.dtype != torch.bfloat16 or z.numel() != rows * d_out or not z.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor of rows x d_out elements")
+    _check_out(z, "out", torch.bfloat16, rows * d_out, x.device)
     return rows, d_in, d_out, z
 
 
@@ -371,8 +408,7 @@ def grkan_layer_forward_ws(x: torch.Tensor, A: torch.Tensor, B: torch.Tensor, W:
     need = lib.grkan_layer_forward_workspace_size(rows, d_in, d_out, n_groups)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    wsp = _ptr(workspace) if workspace is not None else None
-    wsn = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    wsp, wsn = _workspace(workspace, x.device)
     st = lib.grkan_layer_forward_ws(_ptr(x), _ptr(A), _ptr(B), _ptr(W), _ptr(z), rows, d_in, d_out, n_groups,
                                     wsp, wsn, ctypes.c_void_p(_stream(stream)))
     if st != GRKAN_OK:
@@ -404,18 +440,15 @@ def grkan_layer_backward(x: torch.Tensor, dz: torch.Tensor, A: torch.Tensor, B: 
     dz [..., d_out], W [d_out, d_in]; dx bf16, dA / dB / dW fp32."""
     _check_coefs(A, B, n_groups, x.device)
     rows, d_in, d_out = _layer_dims(x, W)
-    if dz.dtype != torch.bfloat16 or dz.numel() != rows * d_out or not dz.is_contiguous():
-        raise ValueError("dz must be a contiguous bfloat16 tensor of rows x d_out elements")
-    dx = torch.empty_like(x) if dx is None else dx
-    dA = torch.empty((n_groups, 6), dtype=torch.float32, device=x.device) if dA is None else dA
-    dB = torch.empty((n_groups, 4), dtype=torch.float32, device=x.device) if dB is None else dB
+    _check_out(dz, "dz", torch.bfloat16, rows * d_out, x.device)
+    dx, dA, dB = _grad_outputs(x, n_groups, GRKAN_M, GRKAN_N, dx, dA, dB)
     dW = torch.empty((d_out, d_in), dtype=torch.float32, device=x.device) if dW is None else dW
+    _check_out(dW, "dW", torch.float32, d_out * d_in, x.device)
     lib = load_library()
     need = lib.grkan_layer_backward_workspace_size(rows, d_in, d_out, n_groups)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    wsp = _ptr(workspace) if workspace is not None else None
-    wsn = workspace.numel() if workspace is not None else 0
+    wsp, wsn = _workspace(workspace, x.device)
     st = lib.grkan_layer_backward(_ptr(x), _ptr(dz), _ptr(A), _ptr(B), _ptr(W), _ptr(dx), _ptr(dA), _ptr(dB),
                                   _ptr(dW), rows, d_in, d_out, n_groups, wsp, wsn,
                                   ctypes.c_void_p(_stream(stream)))
@@ -430,6 +463,7 @@ CHEBY_DEGREE = 7
 def _cheby_dims(x, C, degree):
     if x.dtype != torch.bfloat16 or C.dtype != torch.bfloat16:
         raise TypeError("the Chebyshev-KAN layer takes bfloat16 x and C")
+    _on_gpu(x)
     rows, d_in = _rows_d(x)
     if C.dim() != 3 or C.shape[1] != d_in or C.shape[2] != degree + 1 or not C.is_contiguous() \
             or C.device != x.device:
@@ -442,8 +476,7 @@ def grkan_chebykan_forward(x: torch.Tensor, C: torch.Tensor, degree: int = CHEBY
     """y = sum_i sum_k C[o, i, k] T_k(tanh x_i) (``grkan_chebykan_forward``), bf16."""
     rows, d_in, d_out = _cheby_dims(x, C, degree)
     y = torch.empty((*x.shape[:-1], d_out), dtype=torch.bfloat16, device=x.device) if out is None else out
-    if y.dtype != torch.bfloat16 or y.numel() != rows * d_out or not y.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor of rows x d_out elements")
+    _check_out(y, "out", torch.bfloat16, rows * d_out, x.device)
     st = load_library().grkan_chebykan_forward(_ptr(x), _ptr(C), _ptr(y), rows, d_in, d_out, degree,
                                                ctypes.c_void_p(_stream(stream)))
     if st != GRKAN_OK:
@@ -460,16 +493,17 @@ def grkan_chebykan_backward(x: torch.Tensor, dy: torch.Tensor, C: torch.Tensor, 
                             workspace: torch.Tensor | None = None, stream=None):
     """(dx, dC) of the Chebyshev-KAN layer (``grkan_chebykan_backward``): dx bf16, dC fp32."""
     rows, d_in, d_out = _cheby_dims(x, C, degree)
-    if dy.dtype != torch.bfloat16 or dy.numel() != rows * d_out or not dy.is_contiguous():
-        raise ValueError("dy must be a contiguous bfloat16 tensor of rows x d_out elements")
-    dx = torch.empty_like(x) if dx is None else dx
+    _check_out(dy, "dy", torch.bfloat16, rows * d_out, x.device)
+    if dx is None:
+        dx = torch.empty_like(x)
+    _check_out(dx, "dx", torch.bfloat16, x.numel(), x.device)
     dC = torch.empty(C.shape, dtype=torch.float32, device=x.device) if dC is None else dC
+    _check_out(dC, "dC", torch.float32, C.numel(), x.device)
     lib = load_library()
     need = lib.grkan_chebykan_backward_workspace_size(rows, d_in, d_out, degree)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    wsp = _ptr(workspace) if workspace is not None else None
-    wsn = workspace.numel() if workspace is not None else 0
+    wsp, wsn = _workspace(workspace, x.device)
     st = lib.grkan_chebykan_backward(_ptr(x), _ptr(dy), _ptr(C), _ptr(dx), _ptr(dC), rows, d_in, d_out, degree,
                                      wsp, wsn, ctypes.c_void_p(_stream(stream)))
     if st != GRKAN_OK:

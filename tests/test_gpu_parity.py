@@ -307,6 +307,27 @@ def test_errors_surface_as_exceptions(gk):
     assert e.value.status == gk.GRKAN_ERR_INVALID_ARG
 
 
+def test_binding_refuses_what_the_library_cannot_check(gk):
+    """Outputs and workspaces of the wrong size, dtype or device, and host tensors, are refused
+    by the binding before any launch (the library sees only their pointers)."""
+    x, dy = torch.randn(4, 768, device=DEV), torch.randn(4, 768, device=DEV)
+    A, B = torch.randn(8, 6, device=DEV), torch.randn(8, 4, device=DEV)
+    for kw in (dict(dA=torch.empty(8, 5, device=DEV)), dict(dB=torch.empty(8, 4, device=DEV).double()),
+               dict(dx=torch.empty(4, 767, device=DEV)), dict(workspace=torch.empty(1 << 20, dtype=torch.uint8))):
+        with pytest.raises(ValueError):
+            gk.grkan_backward(x, dy, A, B, 8, **kw)
+    with pytest.raises(ValueError):
+        gk.grkan_forward(x, A, B, 8, out=torch.empty(4, 768))
+    with pytest.raises(ValueError, match="GPU device"):
+        gk.grkan_forward(x.cpu(), A.cpu(), B.cpu(), 8)
+    xb = torch.randn(256, 256, device=DEV).bfloat16()
+    W = torch.randn(64, 256, device=DEV).bfloat16()
+    with pytest.raises(ValueError, match="dW"):
+        gk.grkan_layer_backward(xb, torch.randn(256, 64, device=DEV).bfloat16(), A, B, W, 8,
+                                dW=torch.empty(64, 256, device=DEV).bfloat16())
+    torch.cuda.synchronize()
+
+
 def test_launch_geometry(gk):
     g = gk.grkan_query_launch(201728, 768, 8, gk.GRKAN_F32, 1)
     log(f"[geometry] KAT-B backward: {g}")
