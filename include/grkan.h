@@ -82,8 +82,9 @@ extern "C" {
 typedef enum GRKAN_ENUM_INT {
     GRKAN_OK = 0,
     GRKAN_ERR_INVALID_ARG = 1, /* null pointer, bad shape, overlap, small workspace, bad flags */
-    GRKAN_ERR_UNSUPPORTED = 2, /* misaligned pointer, d/n_groups*bytes(io) not a multiple of 16,
-                                  more than 65535 groups, a degree pair not compiled in        */
+    GRKAN_ERR_UNSUPPORTED = 2, /* misaligned pointer, a degree pair not compiled in, more than
+                                  65535 groups whose row segments are whole 16-byte vectors,
+                                  a shape past the launch limits                               */
     GRKAN_ERR_HIP = 3          /* the HIP runtime reported an error on query or launch          */
 } grkan_status_t;
 
@@ -120,6 +121,10 @@ enum {
  *             NULL when rows == 0.
  *   A, B      fp32 coefficients [n_groups][6] and [n_groups][4], 4-byte aligned.
  *   rows >= 0 (0 is a no-op), d >= 1, n_groups >= 1, d % n_groups == 0.
+ *   Any such n_groups is served: groups whose row segment (d / n_groups
+ *   elements) is a whole number of 16-byte vectors take kernels with one
+ *   16-byte vector per lane, narrower ones -- down to one function per
+ *   channel, n_groups = d -- kernels with one channel column per lane.
  */
 GRKAN_API grkan_status_t grkan_forward(const void *x, void *y, const float *A, const float *B,
                              int64_t rows, int64_t d, int32_t n_groups,
