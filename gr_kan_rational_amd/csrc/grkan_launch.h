@@ -143,9 +143,10 @@ constexpr int kFwdWaveBlock = 64;
 #define GRKAN_FOR_EACH_DEGREE(X) X(5, 4) X(3, 2) X(4, 3) X(6, 5) X(7, 6) X(2, 1) X(4, 4) X(5, 0)
 
 // Degree-independent kernels (grkan_merge.hip).  The merge adds each
-// (group, coefficient)'s partials in chunks of 8192 slots; with more than one
-// chunk it needs merge_chunks(slots) fp64 chunk sums per (group,
-// coefficient) of scratch, after the partials in the workspace.
+// (group, coefficient)'s partials in one workgroup up to 16384 slots, else in
+// chunks of 8192 slots; with more than one chunk it needs merge_chunks(slots)
+// fp64 chunk sums per (group, coefficient) of scratch, after the partials in
+// the workspace.
 // For narrow plans the merge skips the parts a group does not span (d_g,
 // cpb > 0); segment plans pass 0, 0.
 uint32_t merge_chunks(int64_t slots);

@@ -15,17 +15,20 @@ namespace {
 
 // Second stage of the deterministic backward: the partials of group g,
 // coefficient k -- one per (column part, row tile) -- are added in a fixed
-// order in fp64.  Workgroup (g, k, c) takes the c-th chunk of 8 slots per
-// thread; each thread issues all of its loads before adding, so a chunk
-// costs about one memory round trip.  With one chunk per (g, k) (up to 8192
-// slots: GR-KAN's 8 groups at KAT-B) the workgroup writes dA / dB directly;
-// otherwise (few groups, many tiles) it writes an fp64 chunk sum and
-// grkan_merge_chunks_kernel adds the chunk sums in order.  Slots are
-// [parts][8 * bundles]; within a part, slot r = (t mod 8) * bundles + t / 8
-// holds tile t, and the slots of tiles past the end hold nothing.
+// order in fp64.  Up to 16384 slots per (g, k) one workgroup takes them all,
+// 8 or 16 per thread, and writes dA / dB directly (GR-KAN's 8 groups at KAT-B
+// and at the hidden-layer shapes); beyond that (few groups, many tiles)
+// workgroup (g, k, c) takes the c-th chunk of 8 slots per thread and writes
+// an fp64 chunk sum, and grkan_merge_chunks_kernel adds the chunk sums in
+// order.  Each thread issues all of its loads before adding, so a chunk
+// costs about one memory round trip.  Slots are [parts][8 * bundles];
+// within a part, slot r = (t mod 8) * bundles + t / 8 holds tile t, and the
+// slots of tiles past the end hold nothing.
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeLoads = 8;
+constexpr int kMergeLoadsOne = 16;  // per thread when one workgroup takes all the slots
 constexpr uint32_t kMergeChunk = (uint32_t)kMergeThreads * kMergeLoads;
+constexpr uint32_t kMergeOneChunk = (uint32_t)kMergeThreads * kMergeLoadsOne;
 // Coefficients with at most this many slots (many groups, few tiles: one
 // function per channel) are merged one wave each: lane l adds slots l,
 // l + 64, ... in order, then the wave adds its lanes in a fixed tree.
@@ -79,25 +82,25 @@ __device__ static inline bool slot_holds_tile(uint32_t q, const SlotMap &sm) {
     return (r - a * sm.bundles) * 8u + a < sm.tiles;
 }
 
-template <int T>
+template <int T, int L>
 __global__ __launch_bounds__(T) void grkan_merge_kernel(
     const float *__restrict__ partials, SlotMap sm, uint32_t slots,
     int32_t na, int32_t nb, int32_t dg, int32_t cpb, uint32_t chunks, double *__restrict__ chunk_sums,
     float *__restrict__ dA, float *__restrict__ dB) {
-    constexpr uint32_t chunk = (uint32_t)T * kMergeLoads;
+    constexpr uint32_t chunk = (uint32_t)T * L;
     const int gk = (int)blockIdx.x;
     const uint32_t c = blockIdx.y;
     const uint32_t valid = parts_of(gk / (na + nb), slots / sm.per_part, dg, cpb) * sm.per_part;
     const float *p = partials + (int64_t)gk * slots;
-    float v[kMergeLoads];
+    float v[L];
 #pragma unroll
-    for (int i = 0; i < kMergeLoads; ++i) {
+    for (int i = 0; i < L; ++i) {
         const uint32_t q = c * chunk + (uint32_t)i * T + threadIdx.x;
         v[i] = (q < valid && slot_holds_tile(q, sm)) ? p[q] : 0.0f;
     }
     double s = 0.0;
 #pragma unroll
-    for (int i = 0; i < kMergeLoads; ++i) s += (double)v[i];
+    for (int i = 0; i < L; ++i) s += (double)v[i];
     const double total = block_sum<T>(s);
     if (threadIdx.x == 0) {
         if (chunks == 1) write_sum(gk, na, nb, total, dA, dB);
@@ -151,6 +154,7 @@ __global__ __launch_bounds__(256) void grkan_zero_kernel(float *__restrict__ dA,
 }  // namespace
 
 uint32_t merge_chunks(int64_t slots) {
+    if (slots <= (int64_t)kMergeOneChunk) return 1;
     return (uint32_t)((slots + kMergeChunk - 1) / kMergeChunk);
 }
 
@@ -182,9 +186,17 @@ hipError_t launch_merge(const float *partials, double *chunk_sums, int32_t n_gro
         return hipGetLastError();
     }
     const uint32_t chunks = merge_chunks(slots);
-    hipLaunchKernelGGL(grkan_merge_kernel<kMergeThreads>, dim3(grid_gk.x, chunks), dim3(kMergeThreads), 0, s,
-                       partials, sm, (uint32_t)slots, na, n, narrow_dg, narrow_cpb, chunks, chunk_sums, dA, dB);
-    if (chunks == 1) return hipGetLastError();
+    if (chunks == 1) {
+        if (slots <= (int64_t)kMergeChunk)
+            hipLaunchKernelGGL((grkan_merge_kernel<kMergeThreads, kMergeLoads>), grid_gk, dim3(kMergeThreads), 0, s,
+                               partials, sm, (uint32_t)slots, na, n, narrow_dg, narrow_cpb, 1u, chunk_sums, dA, dB);
+        else
+            hipLaunchKernelGGL((grkan_merge_kernel<kMergeThreads, kMergeLoadsOne>), grid_gk, dim3(kMergeThreads), 0,
+                               s, partials, sm, (uint32_t)slots, na, n, narrow_dg, narrow_cpb, 1u, chunk_sums, dA, dB);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((grkan_merge_kernel<kMergeThreads, kMergeLoads>), dim3(grid_gk.x, chunks), dim3(kMergeThreads),
+                       0, s, partials, sm, (uint32_t)slots, na, n, narrow_dg, narrow_cpb, chunks, chunk_sums, dA, dB);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(grkan_merge_chunks_kernel, grid_gk, dim3(kChunkThreads), 0, s, chunk_sums, chunks, na,

@@ -97,11 +97,13 @@ def ws(lib, rows, d, n_g, io=F32, flags=DEFAULT):
 def test_workspace_size(lib):
     # KAT-B backward: 96 channels x 4 B = 24 vectors per group row; 16 rows x 24 = 384 lanes per
     # pass, 2 passes -> 32-row tiles; ceil(201728 / 32) = 6304 tiles; one fp32 partial per
-    # (group, coefficient, tile), slots rounded up to a multiple of 8 tiles.  Above 8192 slots
-    # the merge adds them in chunks and needs one fp64 chunk sum per (group, coefficient, chunk).
+    # (group, coefficient, tile), slots rounded up to a multiple of 8 tiles.  Above 16384 slots
+    # the merge adds them in chunks of 8192 and needs one fp64 chunk sum per (group, coefficient,
+    # chunk).
     assert ws(lib, 201728, 768, 8) == 8 * 10 * 6304 * 4
     assert ws(lib, 16, 32, 8) == 8 * 10 * 8 * 4             # tiny: a single tile, 8 slots
-    assert ws(lib, 201728, 3072, 8, io=BF16) == 8 * 10 * 12608 * 4 + 8 * 10 * 2 * 8  # 4 rows x 4 passes
+    assert ws(lib, 201728, 3072, 8, io=BF16) == 8 * 10 * 12608 * 4  # 4 rows x 4 passes: one merge launch
+    assert ws(lib, 300000, 3072, 8, io=BF16) == 8 * 10 * 18752 * 4 + 8 * 10 * 3 * 8  # 18752 slots: 3 chunks
     # small grids (under 4096 workgroups at 2 passes) take 1 pass: 16-row tiles
     assert ws(lib, 1000, 768, 8) == 8 * 10 * 64 * 4         # 63 tiles of 16 rows (the last ragged) -> 64 slots
     assert ws(lib, 1025, 768, 8) == 8 * 10 * 72 * 4         # 65 tiles -> 72 slots
@@ -194,7 +196,7 @@ def test_pau_workspace_size(lib):
     # One fp32 partial per (group, coefficient, part, tile); m + 1 + n coefficients.
     assert pws(lib, 201728, 768, 8, 5, 4) == ws(lib, 201728, 768, 8)
     assert pws(lib, 201728, 768, 8, 3, 2) == 8 * 6 * 6304 * 4     # 2 passes of 16 rows: 32-row tiles
-    assert pws(lib, 201728, 768, 8, 7, 6) == 8 * 14 * 12608 * 4 + 8 * 14 * 2 * 8  # 16-row tiles
+    assert pws(lib, 201728, 768, 8, 7, 6) == 8 * 14 * 12608 * 4     # 16-row tiles: one merge launch
     assert pws(lib, 201728, 768, 8, 5, 0) == 8 * 6 * 6304 * 4     # polynomial: no dB sums
     # n_groups = 1 (one PAU for all channels): a 192-vector segment, two rows per pass, 4-row tiles
     assert pws(lib, 201728, 768, 1, 5, 4) == 1 * 10 * 50432 * 4 + 1 * 10 * 7 * 8
@@ -333,7 +335,8 @@ def test_layer_backward_workspace_size(lib):
     # per coefficient.
     a256 = lambda v: (v + 255) // 256 * 256
     act = 8 * 10 * 25216 * 4 + 8 * 10 * 4 * 8
-    assert act == 2 * lib.grkan_backward_workspace_size(201728, 3072, 8, BF16, 0)
+    # twice the partials of grkan_backward's 16-row tiles, which one merge launch adds (12,608 slots)
+    assert 8 * 10 * 25216 * 4 == 2 * lib.grkan_backward_workspace_size(201728, 3072, 8, BF16, 0)
     assert f(201728, 3072, 768, 8) == (a256(768 * 3072 * 2) + a256(201728 * 3072 * 2) + a256(act)
                                       + a256(14 * 768 * 3072 * 4))
     assert f(0, 256, 64, 8) == 0

@@ -43,22 +43,32 @@ def bits(t):
     return t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32)
 
 
-# (workload, rows): first a large call, then a smaller one of another shape and dtype
+# (workload, rows): first a large call, then a smaller one of another shape and dtype.  The first
+# sequence's bf16 shape has 16-row tiles like KAT-B hidden and more rows, so that its merge runs in
+# chunks (18,752 slots per coefficient, three chunks of 8,192).
+CHUNKED = synth.custom("noalloc-chunked-bf16", 300000, 768, 2, io="bf16", seed=960)
 SEQUENCES = [
-    [("kat-b-hid-bf16", 201728), ("kat-b", 1001)],     # 4.0 MB of partial sums (two merge chunks), then 20 KB
-    [("kat-s-hid", 201728), ("kat-t", 4097)],          # 4.0 MB (two merge chunks), then one chunk
-    [("kat-b", 201728), ("tiny", 16)],                 # 2.0 MB, then a single tile
+    [(CHUNKED, None), ("kat-b", 1001)],                # 1.5 MB of partial sums and chunk sums, then 20 KB
+    [("kat-b-hid-bf16", 201728), ("kat-t", 4097)],     # 4.0 MB (one merge launch of 16 slots per thread),
+                                                       # then one of 8
+    [("kat-s-hid", 201728), ("tiny", 16)],             # 4.0 MB, then a single tile
+    [("kat-b", 201728), ("kat-b-hid-bf16", 1000)],     # 2.0 MB, then a few bf16 tiles
 ]
 
 
-@pytest.mark.parametrize("seq", SEQUENCES, ids=lambda s: "-".join(f"{n}x{r}" for n, r in s))
+def _name(n):
+    return n if isinstance(n, str) else n.name
+
+
+@pytest.mark.parametrize("seq", SEQUENCES, ids=lambda s: "-".join(f"{_name(n)}x{r}" for n, r in s))
 def test_noalloc_matches_backward_bitwise_on_two_calls(gk, seq):
-    for name, rows in seq:
-        inp = synth.make_inputs(name, rows=rows)
+    for spec, rows in seq:
+        inp = synth.make_inputs(spec, rows=rows)
         w = inp["workload"]
+        name = w.name
         io = gk.GRKAN_BF16 if w.io == "bf16" else gk.GRKAN_F32
         need = gk.grkan_backward_workspace_size(w.rows, w.d, w.n_groups, io)
-        log(f"[noalloc] {name} rows={rows} io={w.io}: partial sums {need} B")
+        log(f"[noalloc] {name} rows={w.rows} io={w.io}: partial sums {need} B")
         assert 0 < need <= gk.GRKAN_NOALLOC_SCRATCH_BYTES
         x, dy, A, B = dev_inputs(inp)
         dx0, dA0, dB0 = gk.grkan_backward(x, dy, A, B, w.n_groups)
@@ -66,7 +76,7 @@ def test_noalloc_matches_backward_bitwise_on_two_calls(gk, seq):
         torch.cuda.synchronize()
         for a, b in ((dx0, dx1), (dA0, dA1), (dB0, dB1)):
             assert torch.equal(bits(a), bits(b)), name
-        if rows <= 5000:
+        if w.rows <= 5000:
             ref = orc.run(inp["x"], inp["A"], inp["B"], w.n_groups, dy=inp["dy"], io=w.io)
             host = dx1.float().cpu().numpy() if w.io == "bf16" else dx1.cpu().numpy()
             parity.check_elem(f"noalloc {name} dX", host, ref["dx"], ref["dxmag"], w.io)
